@@ -1,0 +1,401 @@
+"""Seeded synthetic inputs for the CSA/HCA attention path.
+
+This module only draws random numbers and packs them into storage formats
+(bf16, OCP FP8 E4M3 with a per-row scale, OCP MXFP4).  It holds none of the
+method's arithmetic, and both the oracle side and the HIP side of every test
+and benchmark take their inputs from it.
+
+Distributions follow the workloads the pages describe (DeepSeek-V4-Flash
+``config.json`` shapes on the llm-atlas card; ``initializer_range`` 0.02):
+
+* projected activations are drawn i.i.d. N(0, (0.02*sqrt(4096))^2) = N(0, 1.28^2),
+  the marginal of x @ W for x ~ N(0,1) of width 4096 and W ~ N(0, 0.02);
+* the learned position bias of the compressor is N(0, 0.1), sinks N(0, 1);
+* decode caches are N(0, 1), then quantised to their storage format.
+
+Large tensors are drawn in fixed row chunks, each from its own child of
+``numpy.random.SeedSequence``, so any chunk can be regenerated on its own.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+ACT_STD = 0.02 * np.sqrt(4096.0)     # 1.28
+CHUNK_ELEMS = 1 << 22                # elements per independently seeded chunk
+
+
+# --------------------------------------------------------------------------- packing
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 (fn) codes, via torch's float8_e4m3fn cast."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+
+
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_pack(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """OCP MXFP4 quantiser for synthetic inputs.
+
+    Blocks of 32 along the last axis share an E8M0 scale X = 2^(floor(log2 amax) - 2)
+    (the OCP MX recipe, emax(E2M1) = 2); each element is rounded to the nearest
+    E2M1 value of x / X (ties to the even code) and saturated at 6.
+    Returns (packed nibbles [..., dim/2] uint8, low nibble = even element;
+    scales [..., dim/32] uint8)."""
+    x = np.asarray(x, dtype=np.float32)
+    dim = x.shape[-1]
+    assert dim % 32 == 0
+    blk = x.reshape(-1, dim // 32, 32).astype(np.float64)
+    amax = np.max(np.abs(blk), axis=-1)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    v = blk / np.ldexp(1.0, e)[..., None]
+    a = np.minimum(np.abs(v), 6.0)
+    # nearest grid point; ties go to the even code (mantissa bit 0)
+    d = np.abs(a[..., None] - _E2M1_GRID)
+    best = np.argmin(d, axis=-1)
+    dmin = np.take_along_axis(d, best[..., None], -1)[..., 0]
+    nxt = np.minimum(best + 1, 7)
+    dn = np.take_along_axis(d, nxt[..., None], -1)[..., 0]
+    tie = (dn == dmin) & (nxt != best) & (best % 2 == 1)
+    code = np.where(tie, nxt, best).astype(np.uint8)
+    code = code | (np.signbit(v) & (code != 0)).astype(np.uint8) << 3
+    code = code.reshape(*x.shape[:-1], dim)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    scales = (e + 127).astype(np.uint8).reshape(*x.shape[:-1], dim // 32)
+    return packed, scales
+
+
+def fp8r_pack(x: np.ndarray, tail: int) -> Tuple[np.ndarray, np.ndarray]:
+    """KV row storage: channels [0, dim-tail) as E4M3 codes of x / s with one
+    fp32 scale s = amax/448 per row; the trailing `tail` (rope) channels as bf16.
+    Returns (rows [..., (dim-tail) + 2*tail] uint8, scales [...] float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    dim = x.shape[-1]
+    head = x[..., : dim - tail]
+    amax = np.max(np.abs(head), axis=-1)
+    s = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    codes = e4m3_bytes(head / s[..., None])
+    rope = bf16_bits(x[..., dim - tail:]).view(np.uint8).reshape(*x.shape[:-1], 2 * tail)
+    return np.concatenate([codes, rope], axis=-1), s
+
+
+# --------------------------------------------------------------------------- row sets
+@dataclass
+class RowSet:
+    """Per-sequence stored rows: a compressed pool or a sliding window.
+
+    data      : [B, rows_per_seq, row_bytes] uint8 (any numpy dtype viewed as bytes)
+    kind      : 'f32' | 'bf16' | 'fp8r' | 'mxfp4'
+    count     : [B] valid rows per sequence
+    first_tok : [B] token index of row 0 (windows) or None (pools)
+    """
+    kind: str
+    data: np.ndarray
+    dim: int
+    count: np.ndarray
+    tail: int = 0
+    row_scale: Optional[np.ndarray] = None
+    blk_scale: Optional[np.ndarray] = None
+    first_tok: Optional[np.ndarray] = None
+
+    @property
+    def n_seq(self) -> int:
+        return self.data.shape[0]
+
+    @property
+    def rows_per_seq(self) -> int:
+        return self.data.shape[1]
+
+
+def rowset_from_values(x: np.ndarray, kind: str, tail: int = 0, count=None,
+                       first_tok=None) -> RowSet:
+    """Pack values [B, n, dim] into a RowSet of the given storage kind."""
+    x = np.asarray(x, dtype=np.float32)
+    B, n, dim = x.shape
+    cnt = np.full(B, n, np.int32) if count is None else np.asarray(count, np.int32)
+    ft = None if first_tok is None else np.asarray(first_tok, np.int32)
+    if kind == "f32":
+        return RowSet(kind, x.copy().view(np.uint8).reshape(B, n, 4 * dim), dim, cnt, first_tok=ft)
+    if kind == "bf16":
+        return RowSet(kind, bf16_bits(x).view(np.uint8).reshape(B, n, 2 * dim), dim, cnt, first_tok=ft)
+    if kind == "fp8r":
+        rows, sc = fp8r_pack(x, tail)
+        return RowSet(kind, rows, dim, cnt, tail=tail, row_scale=sc, first_tok=ft)
+    if kind == "mxfp4":
+        pk, sc = mxfp4_pack(x)
+        return RowSet(kind, pk, dim, cnt, blk_scale=sc, first_tok=ft)
+    raise ValueError(kind)
+
+
+# --------------------------------------------------------------------------- drawing
+def _chunking(shape):
+    """Row chunking of a tensor drawn by ``_draw``: rows are the flattened leading
+    axes, each of shape[-1] elements."""
+    shape = tuple(int(s) for s in shape)
+    last = shape[-1] if shape else 1
+    n_rows = int(np.prod(shape[:-1])) if len(shape) > 1 else (1 if shape else 1)
+    rows_per_chunk = max(1, CHUNK_ELEMS // max(last, 1))
+    n_chunks = (n_rows + rows_per_chunk - 1) // rows_per_chunk
+    return shape, last, n_rows, rows_per_chunk, n_chunks
+
+
+def _draw(ss: np.random.SeedSequence, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) float32 of `shape`, drawn in independently seeded row chunks."""
+    shape, last, n_rows, rpc, n_chunks = _chunking(shape)
+    out = np.empty((n_rows, last), dtype=np.float32)
+    for i, child in enumerate(ss.spawn(n_chunks)):
+        lo, hi = i * rpc, min(n_rows, (i + 1) * rpc)
+        rng = np.random.default_rng(child)
+        out[lo:hi] = (rng.standard_normal((hi - lo) * last, dtype=np.float32)
+                      * np.float32(std)).reshape(hi - lo, last)
+    return out.reshape(shape)
+
+
+def draw_rows(seed: int, name_index: int, shape, std: float, row_lo: int, row_hi: int) -> np.ndarray:
+    """Regenerate flattened rows [row_lo, row_hi) (rows = leading axes flattened,
+    each of shape[-1] elements) of the tensor ``_Tree(seed, ...).draw`` gives for
+    the name at position name_index, without drawing the rest."""
+    ss = np.random.SeedSequence(seed).spawn(name_index + 1)[name_index]
+    shape, last, n_rows, rpc, n_chunks = _chunking(shape)
+    children = ss.spawn(n_chunks)
+    out = np.empty((row_hi - row_lo, last), dtype=np.float32)
+    for ci in range(row_lo // rpc, (row_hi - 1) // rpc + 1):
+        lo, hi = ci * rpc, min(n_rows, (ci + 1) * rpc)
+        rng = np.random.default_rng(children[ci])
+        blk = (rng.standard_normal((hi - lo) * last, dtype=np.float32) * np.float32(std)).reshape(hi - lo, last)
+        a, b = max(lo, row_lo), min(hi, row_hi)
+        out[a - row_lo:b - row_lo] = blk[a - lo:b - lo]
+    return out
+
+
+class _Tree:
+    """Names -> independent seed-sequence children, in a fixed order."""
+
+    def __init__(self, seed: int, names):
+        self.seed = seed
+        self.names = list(names)
+        kids = np.random.SeedSequence(seed).spawn(len(self.names))
+        self.ss: Dict[str, np.random.SeedSequence] = dict(zip(self.names, kids))
+
+    def draw(self, name: str, shape, std: float = 1.0) -> np.ndarray:
+        return _draw(self.ss[name], shape, std)
+
+    def index(self, name: str) -> int:
+        return self.names.index(name)
+
+
+# --------------------------------------------------------------------------- prefill
+@dataclass
+class PrefillCase:
+    """Inputs of one prefill layer (CSA when topk > 0 and overlap, HCA otherwise).
+
+    Values are float32 arrays of what is stored (bf16 cases are already rounded
+    to bf16); ``store`` says which storage type the GPU side receives."""
+    name: str
+    store: str                       # 'f32' or 'bf16'
+    B: int
+    S: int
+    H: int
+    D: int
+    R: int
+    theta: float
+    m: int
+    overlap: bool
+    W: int
+    Hi: int = 0
+    Di: int = 0
+    topk: int = 0
+    score_scale: float = 1.0
+    sm_scale: float = 1.0
+    q: np.ndarray = None             # [B, S, H, D]
+    kv: np.ndarray = None            # [B, S, D]  window K=V before rotation
+    c: np.ndarray = None             # [B, S, D]  compressor candidates
+    z: np.ndarray = None             # [B, S, D]  compressor gate logits
+    bias: np.ndarray = None          # [window, D] learned position bias (fp32)
+    q_idx: np.ndarray = None         # [B, S, Hi, Di]
+    w_idx: np.ndarray = None         # [B, S, Hi]  fp32
+    c_idx: np.ndarray = None         # [B, S, Di]
+    z_idx: np.ndarray = None         # [B, S, Di]
+    bias_idx: np.ndarray = None      # [window, Di]
+    sinks: np.ndarray = None         # [H] fp32
+    pos0: np.ndarray = None          # [B] int64
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def N(self) -> int:
+        return self.S // self.m
+
+    @property
+    def window_len(self) -> int:
+        return 2 * self.m if self.overlap else self.m
+
+
+def _round_store(x: np.ndarray, store: str) -> np.ndarray:
+    return bf16_to_f32(bf16_bits(x)) if store == "bf16" else np.asarray(x, np.float32)
+
+
+def tiny_csa_layer(seed: int = 1001, S: int = 256, pos0: int = 0) -> PrefillCase:
+    """Tiny CSA layer, fp32: batch 1, seq 256, hidden 256, 8 q heads, one K=V head
+    of dim 64 (last 16 channels rotated, theta 10000), m=4, window 16, indexer
+    4 x 32, top-k 8, per-head sink; x ~ N(0,1), weights ~ N(0, 0.02), position
+    bias N(0, 0.1).  The projections are plain fp64 matmuls (they sit outside
+    the attention path) rounded to fp32 for both sides."""
+    hidden, H, D, R, Hi, Di = 256, 8, 64, 16, 4, 32
+    t = _Tree(seed, ["x", "Wq", "Wkv", "Wc", "Wz", "WqI", "Ww", "WcI", "WzI", "bias", "bias_idx", "sinks"])
+    x = t.draw("x", (S, hidden)).astype(np.float64)
+
+    def proj(name, cols):
+        return (x @ t.draw(name, (hidden, cols), 0.02).astype(np.float64)).astype(np.float32)
+
+    case = PrefillCase("tiny_csa_fp32", "f32", 1, S, H, D, R, 10000.0, 4, True, 16, Hi, Di, 8,
+                       score_scale=1.0 / np.sqrt(Hi * Di), sm_scale=1.0 / np.sqrt(D))
+    case.q = proj("Wq", H * D).reshape(1, S, H, D)
+    case.kv = proj("Wkv", D).reshape(1, S, D)
+    case.c = proj("Wc", D).reshape(1, S, D)
+    case.z = proj("Wz", D).reshape(1, S, D)
+    case.q_idx = proj("WqI", Hi * Di).reshape(1, S, Hi, Di)
+    case.w_idx = proj("Ww", Hi).reshape(1, S, Hi)
+    case.c_idx = proj("WcI", Di).reshape(1, S, Di)
+    case.z_idx = proj("WzI", Di).reshape(1, S, Di)
+    case.bias = t.draw("bias", (8, D), 0.1)
+    case.bias_idx = t.draw("bias_idx", (8, Di), 0.1)
+    case.sinks = t.draw("sinks", (H,), 1.0)
+    case.pos0 = np.array([pos0], np.int64)
+    return case
+
+
+def flash_prefill(seed: int, kind: str, B: int = 1, S: int = 8192, H: int = 64, D: int = 512,
+                  R: int = 64, W: int = 128, Hi: int = 64, Di: int = 128, topk: int = 512,
+                  m: Optional[int] = None, store: str = "bf16", pos0=None,
+                  theta: float = 160000.0, with_q: bool = True) -> PrefillCase:
+    """Flash-shaped prefill layer inputs (DeepSeek-V4-Flash attention fields).
+
+    kind 'csa': overlapping m=4 pooling, indexer Hi x Di, top-k.
+    kind 'hca': non-overlapping m'=128 pooling, no indexer.
+    Every projected tensor is i.i.d. N(0, 1.28^2), rounded to the storage type."""
+    if m is None:
+        m = 4 if kind == "csa" else 128
+    overlap = kind == "csa"
+    width = 2 * m if overlap else m
+    names = ["q", "kv", "c", "z", "bias", "q_idx", "w_idx", "c_idx", "z_idx", "bias_idx", "sinks"]
+    t = _Tree(seed, names)
+    case = PrefillCase(f"{kind}_prefill_{store}_S{S}", store, B, S, H, D, R, theta, m, overlap, W,
+                       Hi if kind == "csa" else 0, Di if kind == "csa" else 0,
+                       topk if kind == "csa" else 0,
+                       score_scale=(1.0 / np.sqrt(Hi * Di)) if kind == "csa" else 1.0,
+                       sm_scale=1.0 / np.sqrt(D))
+    if with_q:
+        case.q = _round_store(t.draw("q", (B, S, H, D), ACT_STD), store)
+    case.kv = _round_store(t.draw("kv", (B, S, D), ACT_STD), store)
+    case.c = _round_store(t.draw("c", (B, S, D), ACT_STD), store)
+    case.z = _round_store(t.draw("z", (B, S, D), ACT_STD), store)
+    case.bias = t.draw("bias", (width, D), 0.1)
+    if kind == "csa":
+        case.q_idx = _round_store(t.draw("q_idx", (B, S, Hi, Di), ACT_STD), store)
+        case.w_idx = t.draw("w_idx", (B, S, Hi), ACT_STD)
+        case.c_idx = _round_store(t.draw("c_idx", (B, S, Di), ACT_STD), store)
+        case.z_idx = _round_store(t.draw("z_idx", (B, S, Di), ACT_STD), store)
+        case.bias_idx = t.draw("bias_idx", (width, Di), 0.1)
+    case.sinks = t.draw("sinks", (H,), 1.0)
+    case.pos0 = np.zeros(B, np.int64) if pos0 is None else np.asarray(pos0, np.int64)
+    case.meta = {"seed": seed, "tree": names}
+    return case
+
+
+def prefill_q_rows(case: PrefillCase, b: int, t_lo: int, t_hi: int) -> np.ndarray:
+    """Regenerate q[b, t_lo:t_hi] ([t_hi-t_lo, H, D], storage-rounded) of a Flash
+    prefill case drawn with with_q=False: the values a full draw would give."""
+    seed, idx = case.meta["seed"], case.meta["tree"].index("q")
+    H = case.H
+    lo, hi = (b * case.S + t_lo) * H, (b * case.S + t_hi) * H
+    x = draw_rows(seed, idx, (case.B, case.S, case.H, case.D), ACT_STD, lo, hi)
+    return _round_store(x.reshape(t_hi - t_lo, H, case.D), case.store)
+
+
+# --------------------------------------------------------------------------- decode
+@dataclass
+class DecodeLayer:
+    """Cached state and the new query of one decode layer (B sequences)."""
+    kind: str                  # 'csa' | 'hca'
+    B: int
+    L: np.ndarray              # [B] tokens so far, the new token included
+    H: int
+    D: int
+    R: int
+    theta: float
+    m: int
+    W: int
+    q: np.ndarray              # [B, H, D] bf16-rounded values (unrotated)
+    sinks: np.ndarray          # [H]
+    pool: RowSet               # compressed K=V entries, already rotated
+    win: RowSet                # last W tokens' K=V rows, already rotated
+    topk: int = 0
+    Hi: int = 0
+    Di: int = 0
+    q_idx: Optional[np.ndarray] = None         # [B, Hi, Di] bf16-rounded values, or None (mxfp4)
+    q_idx_packed: Optional[np.ndarray] = None  # mxfp4 [B, Hi, Di/2]
+    q_idx_scale: Optional[np.ndarray] = None   # mxfp4 [B, Hi, Di/32]
+    q_idx_kind: str = "bf16"
+    w_idx: Optional[np.ndarray] = None         # [B, Hi] fp32
+    kpool: Optional[RowSet] = None             # indexer keys
+    score_scale: float = 1.0
+    sm_scale: float = 1.0
+    pos0: Optional[np.ndarray] = None
+
+    @property
+    def tok(self) -> np.ndarray:
+        return (self.L - 1).astype(np.int32)
+
+
+def decode_layer(seed: int, kind: str, B: int, L, H: int = 64, D: int = 512, R: int = 64,
+                 W: int = 128, m: Optional[int] = None, topk: int = 512, Hi: int = 64, Di: int = 128,
+                 idx_kind: str = "bf16", theta: float = 160000.0, pool_rows: Optional[int] = None) -> DecodeLayer:
+    """Synthetic decode state: pools/windows N(0,1) then stored as FP8 E4M3 (+bf16
+    rope channels, per-row scale); indexer keys N(0,1) as bf16 or MXFP4.
+
+    L: tokens per sequence (scalar or [B]); the new token is token L-1 (its K=V
+    row is the last window row), the pool holds L//m entries."""
+    if m is None:
+        m = 4 if kind == "csa" else 128
+    L = np.broadcast_to(np.asarray(L, np.int64), (B,)).copy()
+    N = (L // m).astype(np.int32)
+    Nmax = int(pool_rows if pool_rows is not None else N.max())
+    t = _Tree(seed, ["q", "pool", "win", "sinks", "q_idx", "w_idx", "kpool"])
+    q = bf16_to_f32(bf16_bits(t.draw("q", (B, H, D), 1.0)))
+    pool = rowset_from_values(t.draw("pool", (B, Nmax, D), 1.0), "fp8r", tail=R, count=N)
+    wcount = np.minimum(L, W).astype(np.int32)
+    win = rowset_from_values(t.draw("win", (B, W, D), 1.0), "fp8r", tail=R, count=wcount,
+                             first_tok=(L - wcount).astype(np.int32))
+    layer = DecodeLayer(kind, B, L, H, D, R, theta, m, W, q, t.draw("sinks", (H,), 1.0), pool, win,
+                        sm_scale=1.0 / np.sqrt(D), pos0=np.zeros(B, np.int64))
+    if kind == "csa":
+        layer.topk, layer.Hi, layer.Di = topk, Hi, Di
+        layer.score_scale = 1.0 / np.sqrt(Hi * Di)
+        layer.w_idx = t.draw("w_idx", (B, Hi), 1.0)
+        qi = t.draw("q_idx", (B, Hi, Di), 1.0)
+        keys = t.draw("kpool", (B, Nmax, Di), 1.0)
+        layer.q_idx_kind = idx_kind
+        if idx_kind == "mxfp4":
+            layer.q_idx_packed, layer.q_idx_scale = mxfp4_pack(qi)
+        else:
+            layer.q_idx = bf16_to_f32(bf16_bits(qi))
+        layer.kpool = rowset_from_values(keys, idx_kind, count=N)
+    return layer
