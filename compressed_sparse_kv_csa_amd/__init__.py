@@ -1,0 +1,254 @@
+"""Python binding of libdsv4 (the gfx950 CSA/HCA attention hot path).
+
+Argument marshalling only: every function takes torch tensors that live in
+device memory, checks shapes and dtypes, and calls the C entry point of the
+same name in ``libdsv4.so`` on ``torch.cuda.current_stream()``.  No step of the
+path is computed here, and nothing falls back to the CPU: if the library is
+missing the import of a function raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsv4.so")
+
+DSV4_F32, DSV4_BF16, DSV4_FP8R, DSV4_MXFP4 = 0, 1, 2, 3
+DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, -4
+
+EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
+           "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_last_error",
+           "dsv4_version"]
+
+
+class Dsv4Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dsv4 error {code}: {msg}")
+        self.code = code
+
+
+class Queries(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int32), ("n_seq", ctypes.c_int32), ("seq", ctypes.c_void_p),
+                ("tok", ctypes.c_void_p), ("pos0", ctypes.c_void_p)]
+
+
+class Rows(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("row_scale", ctypes.c_void_p), ("blk_scale", ctypes.c_void_p),
+                ("dtype", ctypes.c_int32), ("dim", ctypes.c_int32), ("tail", ctypes.c_int32),
+                ("seq_stride", ctypes.c_int64), ("count", ctypes.c_void_p), ("first_tok", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libdsv4.so (torch is imported first so that one HIP runtime serves both)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m compressed_sparse_kv_csa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, F, D, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                 ctypes.c_double, ctypes.c_size_t)
+        L.dsv4_compress.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, D, P, P, I32, P]
+        L.dsv4_rope.argtypes = [P, P, I32, I64, I32, I32, P, D, I32, P]
+        L.dsv4_index_topk_workspace.argtypes = [I32, I64, I32]
+        L.dsv4_index_topk_workspace.restype = SZ
+        L.dsv4_index_topk.argtypes = [P, P, P, I32, P, I32, I32, P, I32, I32, F, P, P, P, SZ, P]
+        L.dsv4_attn_workspace.argtypes = [I32, I32, I32, I64]
+        L.dsv4_attn_workspace.restype = SZ
+        L.dsv4_sparse_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, P, I32, P, F, I32, D, P, I32, P, SZ, P]
+        L.dsv4_hca_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, I32, P, F, I32, D, P, I32, P, SZ, P]
+        L.dsv4_last_error.restype = ctypes.c_char_p
+        L.dsv4_version.restype = ctypes.c_char_p
+        for name in EXPORTS:
+            getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != DSV4_OK:
+        raise Dsv4Error(rc, lib().dsv4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("dsv4 tensors must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("dsv4 tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _code(t: torch.Tensor, allow=(torch.float32, torch.bfloat16)) -> int:
+    if t.dtype not in allow:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return DSV4_F32 if t.dtype == torch.float32 else DSV4_BF16
+
+
+# ------------------------------------------------------------------ descriptors
+@dataclass
+class QueryRows:
+    """Device arrays describing query rows (sequence, token) and per-sequence pos0."""
+    seq: torch.Tensor      # [T] int32
+    tok: torch.Tensor      # [T] int32
+    pos0: Optional[torch.Tensor]   # [B] int64
+    n_seq: int
+
+    def c(self) -> Queries:
+        return Queries(self.seq.numel(), self.n_seq, _ptr(self.seq), _ptr(self.tok), _ptr(self.pos0))
+
+    @staticmethod
+    def prefill(n_seq: int, seq_len: int, pos0: Optional[torch.Tensor] = None, device="cuda") -> "QueryRows":
+        seq = torch.arange(n_seq, dtype=torch.int32, device=device).repeat_interleave(seq_len)
+        tok = torch.arange(seq_len, dtype=torch.int32, device=device).repeat(n_seq)
+        return QueryRows(seq, tok, pos0, n_seq)
+
+    @staticmethod
+    def decode(lengths: torch.Tensor, pos0: Optional[torch.Tensor] = None) -> "QueryRows":
+        B = lengths.numel()
+        seq = torch.arange(B, dtype=torch.int32, device=lengths.device)
+        return QueryRows(seq, (lengths - 1).to(torch.int32), pos0, B)
+
+
+@dataclass
+class RowStore:
+    """Per-sequence rows in device memory (see dsv4_rows in include/dsv4.h).
+
+    data: [B, stride, row_bytes] uint8, or a typed tensor [B, stride, dim]."""
+    data: torch.Tensor
+    dtype: int
+    dim: int
+    count: torch.Tensor                      # [B] int32
+    tail: int = 0
+    row_scale: Optional[torch.Tensor] = None  # [B, stride] f32
+    blk_scale: Optional[torch.Tensor] = None  # [B, stride, dim/32] u8
+    first_tok: Optional[torch.Tensor] = None  # [B] int32
+
+    @property
+    def stride(self) -> int:
+        return self.data.shape[1]
+
+    def c(self) -> Rows:
+        return Rows(_ptr(self.data), _ptr(self.row_scale), _ptr(self.blk_scale), self.dtype, self.dim,
+                    self.tail, self.stride, _ptr(self.count), _ptr(self.first_tok))
+
+
+# ------------------------------------------------------------------ entry points
+def dsv4_compress(c: torch.Tensor, z: torch.Tensor, pos_bias: torch.Tensor, m: int, overlap: bool,
+                  rope_dim: int = 0, rope_theta: float = 10000.0, pos0: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """KV compressor: c, z [B, S, dim] -> pool [B, S//m, dim]."""
+    B, S, dim = c.shape
+    assert z.shape == c.shape and z.dtype == c.dtype
+    assert pos_bias.dtype == torch.float32 and pos_bias.shape == ((2 * m if overlap else m), dim)
+    odt = out_dtype or c.dtype
+    if out is None:
+        out = torch.empty(B, S // m, dim, dtype=odt, device=c.device)
+    _check(lib().dsv4_compress(_ptr(c), _ptr(z), _code(c), _ptr(pos_bias), B, S, dim, m, int(bool(overlap)),
+                               rope_dim, float(rope_theta), _ptr(pos0), _ptr(out), _code(out), _stream()))
+    return out
+
+
+def dsv4_rope(x: torch.Tensor, pos: torch.Tensor, rope_dim: int, rope_theta: float, inverse: bool = False,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Partial interleaved RoPE of the last rope_dim channels; x [..., dim], pos [rows] int64."""
+    dim = x.shape[-1]
+    n = x.numel() // dim
+    if out is None:
+        out = torch.empty_like(x)
+    assert pos.dtype == torch.int64 and pos.numel() == n
+    _check(lib().dsv4_rope(_ptr(x), _ptr(out), _code(x), n, dim, rope_dim, _ptr(pos), float(rope_theta),
+                           int(bool(inverse)), _stream()))
+    return out
+
+
+def dsv4_index_topk(q: QueryRows, q_idx: torch.Tensor, w: torch.Tensor, k_pool: RowStore, m: int, topk: int,
+                    score_scale: float, q_idx_scale: Optional[torch.Tensor] = None, q_dtype: Optional[int] = None,
+                    want_scores: bool = False, ws: Optional[torch.Tensor] = None):
+    """Lightning Indexer + top-k.  Returns idx [T, topk] int32 (and scores)."""
+    T = q.seq.numel()
+    H = w.shape[-1]
+    if q_dtype is None:
+        q_dtype = DSV4_MXFP4 if q_idx.dtype == torch.uint8 else _code(q_idx)
+    Di = k_pool.dim
+    idx = torch.empty(T, topk, dtype=torch.int32, device=w.device)
+    sc = torch.empty(T, topk, dtype=torch.float32, device=w.device) if want_scores else None
+    need = lib().dsv4_index_topk_workspace(T, k_pool.stride, topk)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.device)
+    qc, kc = q.c(), k_pool.c()
+    _check(lib().dsv4_index_topk(ctypes.byref(qc), _ptr(q_idx), _ptr(q_idx_scale), q_dtype, _ptr(w), H, Di,
+                                 ctypes.byref(kc), m, topk, float(score_scale), _ptr(idx), _ptr(sc), _ptr(ws),
+                                 ws.numel(), _stream()))
+    return (idx, sc) if want_scores else idx
+
+
+def _attn_ws(T, H, D, max_rows, device, ws):
+    need = lib().dsv4_attn_workspace(T, H, D, max_rows)
+    if need == 0:
+        return ws, 0
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel()
+
+
+def dsv4_sparse_attn(q: QueryRows, qv: torch.Tensor, window: Optional[RowStore], W: int, pool: Optional[RowStore],
+                     idx: Optional[torch.Tensor], sinks: Optional[torch.Tensor], sm_scale: float, rope_dim: int,
+                     rope_theta: float, out_dtype: Optional[torch.dtype] = None,
+                     ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """CSA core attention.  qv [T, H, D]; idx [T, topk] int32 (or None: no pool branch)."""
+    T, H, D = qv.shape
+    topk = 0 if idx is None else idx.shape[1]
+    if out is None:
+        out = torch.empty(T, H, D, dtype=out_dtype or qv.dtype, device=qv.device)
+    ws, nbytes = _attn_ws(T, H, D, W + topk, qv.device, ws)
+    qc = q.c()
+    wc = window.c() if window is not None else None
+    pc = pool.c() if pool is not None else None
+    _check(lib().dsv4_sparse_attn(ctypes.byref(qc), _ptr(qv), _code(qv), H, D,
+                                  ctypes.byref(wc) if wc is not None else None, W,
+                                  ctypes.byref(pc) if pc is not None else None, _ptr(idx), topk, _ptr(sinks),
+                                  float(sm_scale), rope_dim, float(rope_theta), _ptr(out), _code(out),
+                                  _ptr(ws), nbytes, _stream()))
+    return out
+
+
+def dsv4_hca_attn(q: QueryRows, qv: torch.Tensor, window: Optional[RowStore], W: int, pool: Optional[RowStore],
+                  m: int, sinks: Optional[torch.Tensor], sm_scale: float, rope_dim: int, rope_theta: float,
+                  out_dtype: Optional[torch.dtype] = None, ws: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """HCA core attention: dense over visible pool entries plus the window."""
+    T, H, D = qv.shape
+    if out is None:
+        out = torch.empty(T, H, D, dtype=out_dtype or qv.dtype, device=qv.device)
+    ws, nbytes = _attn_ws(T, H, D, W + (pool.stride if pool is not None else 0), qv.device, ws)
+    qc = q.c()
+    wc = window.c() if window is not None else None
+    pc = pool.c() if pool is not None else None
+    _check(lib().dsv4_hca_attn(ctypes.byref(qc), _ptr(qv), _code(qv), H, D,
+                               ctypes.byref(wc) if wc is not None else None, W,
+                               ctypes.byref(pc) if pc is not None else None, m, _ptr(sinks), float(sm_scale),
+                               rope_dim, float(rope_theta), _ptr(out), _code(out), _ptr(ws), nbytes, _stream()))
+    return out
+
+
+def dsv4_last_error() -> str:
+    return lib().dsv4_last_error().decode()
+
+
+def dsv4_version() -> str:
+    return lib().dsv4_version().decode()

@@ -1,0 +1,68 @@
+"""Build libdsv4.so (the gfx950 HIP kernels + the C ABI) in-tree with hipcc.
+
+    python -m compressed_sparse_kv_csa_amd.build      # or build() from Python
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libdsv4.so")
+SOURCES = ["dsv4_api.cpp", "dsv4_compress.hip", "dsv4_indexer.hip", "dsv4_attn.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    # no packed fp32 (v_pk_*_f32) instructions anywhere in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    f"-I{INCLUDE}", f"-I{CSRC}",
+]
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile every source to an object (in parallel) and link the shared library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        objs.append(obj)
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+        if len(procs) >= jobs:
+            _wait(procs.pop(0), verbose)
+    for p in procs:
+        _wait(p, verbose)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _wait(item, verbose):
+    src, p = item
+    out, _ = p.communicate()
+    text = out.decode(errors="replace")
+    # hipcc's host pass does not know the packed-fp32 feature name: harmless
+    lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln]
+    if p.returncode != 0:
+        sys.stderr.write("\n".join(lines) + "\n")
+        raise RuntimeError(f"hipcc failed on {src}")
+    if verbose and lines:
+        print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

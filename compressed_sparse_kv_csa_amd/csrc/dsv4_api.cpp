@@ -1,0 +1,235 @@
+// dsv4_api.cpp -- the C ABI of libdsv4: host-side argument validation, kernel
+// selection and error reporting.  Every check runs before anything is queued,
+// so a failing call launches nothing.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "dsv4.h"
+
+namespace dsv4host {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char *what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSV4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return DSV4_OK;
+}
+
+// launchers (defined next to their kernels)
+int launch_compress(const void *c, const void *z, int in_dtype, const float *bias, int B, int S, int dim, int m,
+                    int overlap, int rope_dim, double theta, const int64_t *pos0, void *pool, int out_dtype,
+                    hipStream_t st);
+int launch_rope(const void *x, void *y, int dtype, int64_t n_rows, int dim, int rope_dim, const int64_t *pos,
+                double theta, int inverse, hipStream_t st);
+size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk);
+int index_topk_supported(int64_t stride, int topk);
+int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qscale, int q_dtype, const float *w,
+                      int H, int Di, const dsv4_rows *kp, int m, int topk, float scale, int32_t *idx_out,
+                      float *score_out, void *ws, hipStream_t st);
+int attn_nsplit(int T, int64_t max_rows);
+size_t attn_ws(int T, int H, int D, int64_t max_rows);
+int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
+                const dsv4_rows *pool, const int32_t *idx, int topk, int m, int csa, const float *sinks,
+                float sm_scale, int rope_dim, double theta, void *out, int out_dtype, void *ws, int64_t max_rows,
+                hipStream_t st);
+
+static int ok() {
+  g_err[0] = 0;
+  return DSV4_OK;
+}
+
+static int check_queries(const dsv4_queries *q) {
+  if (!q) return fail(DSV4_EINVAL, "queries: NULL descriptor");
+  if (q->n_rows < 0 || q->n_seq < 1) return fail(DSV4_EINVAL, "queries: n_rows %d, n_seq %d", q->n_rows, q->n_seq);
+  if (q->n_rows > 0 && (!q->seq || !q->tok)) return fail(DSV4_EINVAL, "queries: seq/tok arrays are NULL");
+  return DSV4_OK;
+}
+
+static int check_rows(const dsv4_rows *r, const char *what, int dim) {
+  if (!r) return fail(DSV4_EINVAL, "%s: NULL descriptor", what);
+  if ((!r->data && r->seq_stride > 0) || !r->count) return fail(DSV4_EINVAL, "%s: data/count is NULL", what);
+  if (r->dim != dim) return fail(DSV4_EINVAL, "%s: dim %d, expected %d", what, r->dim, dim);
+  if (r->seq_stride < 0) return fail(DSV4_EINVAL, "%s: negative seq_stride", what);
+  if (r->dtype == DSV4_FP8R) {
+    if (!r->row_scale && r->seq_stride > 0) return fail(DSV4_EINVAL, "%s: FP8R rows need row_scale", what);
+    if (r->tail < 0 || r->tail > dim || (r->tail % 8) != 0 || ((dim - r->tail) % 8) != 0)
+      return fail(DSV4_ENOTSUP, "%s: FP8R tail %d (multiple of 8 within dim required)", what, r->tail);
+  } else if (r->dtype == DSV4_MXFP4) {
+    if (!r->blk_scale && r->seq_stride > 0) return fail(DSV4_EINVAL, "%s: MXFP4 rows need blk_scale", what);
+  } else if (r->dtype != DSV4_F32 && r->dtype != DSV4_BF16) {
+    return fail(DSV4_EINVAL, "%s: unknown dtype %d", what, r->dtype);
+  }
+  return DSV4_OK;
+}
+
+}  // namespace dsv4host
+
+using namespace dsv4host;
+
+extern "C" {
+
+const char *dsv4_last_error(void) { return g_err; }
+
+const char *dsv4_version(void) { return "dsv4-gfx950 0.1"; }
+
+int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *pos_bias, int32_t n_seq,
+                  int32_t seq_len, int32_t dim, int32_t m, int32_t overlap, int32_t rope_dim, double rope_theta,
+                  const int64_t *pos0, void *pool, int32_t out_dtype, hipStream_t stream) {
+  if (n_seq < 0 || seq_len < 0 || m < 1) return fail(DSV4_EINVAL, "compress: n_seq %d seq_len %d m %d", n_seq, seq_len, m);
+  const bool empty = n_seq == 0 || seq_len / m == 0;   // nothing to pool: pointers may be NULL
+  if (!empty && (!c || !z || !pos_bias || !pool)) return fail(DSV4_EINVAL, "compress: NULL tensor pointer");
+  if (dim < 2 || (dim & 1) || dim > 4096) return fail(DSV4_ENOTSUP, "compress: dim %d (even, 2..4096)", dim);
+  if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
+    return fail(DSV4_EINVAL, "compress: rope_dim %d (even, <= min(dim, 64))", rope_dim);
+  if ((in_dtype != DSV4_F32 && in_dtype != DSV4_BF16) || (out_dtype != DSV4_F32 && out_dtype != DSV4_BF16))
+    return fail(DSV4_ENOTSUP, "compress: dtypes in %d out %d (F32/BF16 only)", in_dtype, out_dtype);
+  if (rope_dim > 0 && !(rope_theta > 0)) return fail(DSV4_EINVAL, "compress: rope_theta must be > 0");
+  const int rc = launch_compress(c, z, in_dtype, pos_bias, n_seq, seq_len, dim, m, overlap ? 1 : 0, rope_dim,
+                                 rope_theta, pos0, pool, out_dtype, stream);
+  return rc ? rc : ok();
+}
+
+int dsv4_rope(const void *x, void *y, int32_t dtype, int64_t n_rows, int32_t dim, int32_t rope_dim,
+              const int64_t *pos, double rope_theta, int32_t inverse, hipStream_t stream) {
+  if (!x || !y || (!pos && n_rows > 0)) return fail(DSV4_EINVAL, "rope: NULL pointer");
+  if (n_rows < 0) return fail(DSV4_EINVAL, "rope: n_rows %lld", (long long)n_rows);
+  if (dim < 2 || (dim & 1) || dim > 4096) return fail(DSV4_ENOTSUP, "rope: dim %d (even, 2..4096)", dim);
+  if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
+    return fail(DSV4_EINVAL, "rope: rope_dim %d (even, <= min(dim, 64))", rope_dim);
+  if (dtype != DSV4_F32 && dtype != DSV4_BF16) return fail(DSV4_ENOTSUP, "rope: dtype %d (F32/BF16 only)", dtype);
+  if (rope_dim > 0 && !(rope_theta > 0)) return fail(DSV4_EINVAL, "rope: rope_theta must be > 0");
+  const int rc = launch_rope(x, y, dtype, n_rows, dim, rope_dim, pos, rope_theta, inverse, stream);
+  return rc ? rc : ok();
+}
+
+size_t dsv4_index_topk_workspace(int32_t n_rows, int64_t pool_seq_stride, int32_t topk) {
+  if (n_rows < 0 || pool_seq_stride < 0 || topk < 1) return 0;
+  return index_topk_ws(n_rows, pool_seq_stride, topk);
+}
+
+int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale, int32_t q_dtype,
+                    const float *w, int32_t n_heads, int32_t head_dim, const dsv4_rows *k_pool, int32_t m,
+                    int32_t topk, float score_scale, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  int rc = check_queries(q);
+  if (rc) return rc;
+  if (!q_idx || !w || !idx_out) return fail(DSV4_EINVAL, "index_topk: NULL tensor pointer");
+  if (m < 1 || topk < 1 || topk > 2048) return fail(DSV4_EINVAL, "index_topk: m %d topk %d (1..2048)", m, topk);
+  if ((rc = check_rows(k_pool, "index_topk: k_pool", head_dim))) return rc;
+  if (k_pool->dtype != q_dtype) return fail(DSV4_ENOTSUP, "index_topk: key dtype %d != query dtype %d", k_pool->dtype, q_dtype);
+  if (!(score_scale > 0)) return fail(DSV4_EINVAL, "index_topk: score_scale must be > 0");
+  if (q_dtype == DSV4_F32) {
+    if (n_heads < 1 || head_dim < 1 || (size_t)(n_heads * head_dim + n_heads) * 4 > 65536)
+      return fail(DSV4_ENOTSUP, "index_topk: fp32 path needs n_heads*head_dim <= 16000 (%d x %d)", n_heads, head_dim);
+  } else if (q_dtype == DSV4_BF16) {
+    if (n_heads < 16 || n_heads > 64 || n_heads % 16 || head_dim < 32 || head_dim > 128 || head_dim % 32)
+      return fail(DSV4_ENOTSUP, "index_topk: bf16 path needs n_heads in {16,32,48,64}, head_dim in {32,64,96,128} (%d, %d)",
+                  n_heads, head_dim);
+  } else if (q_dtype == DSV4_MXFP4) {
+    if (n_heads < 16 || n_heads > 64 || n_heads % 16 || head_dim != 128)
+      return fail(DSV4_ENOTSUP, "index_topk: MXFP4 path needs n_heads in {16,32,48,64} and head_dim 128 (%d, %d)",
+                  n_heads, head_dim);
+    if (!q_idx_scale) return fail(DSV4_EINVAL, "index_topk: MXFP4 queries need q_idx_scale");
+  } else {
+    return fail(DSV4_ENOTSUP, "index_topk: query dtype %d", q_dtype);
+  }
+  if (!index_topk_supported(k_pool->seq_stride, topk))
+    return fail(DSV4_ENOTSUP, "index_topk: pool stride %lld with topk %d exceeds the two-stage select",
+                (long long)k_pool->seq_stride, topk);
+  const size_t need = index_topk_ws(q->n_rows, k_pool->seq_stride, topk);
+  if (q->n_rows > 0 && (!ws || ws_bytes < need))
+    return fail(DSV4_EWORKSPACE, "index_topk: workspace %zu bytes, need %zu", ws_bytes, need);
+  rc = launch_index_topk(q, q_idx, q_idx_scale, q_dtype, w, n_heads, head_dim, k_pool, m, topk, score_scale, idx_out,
+                         score_out, ws, stream);
+  return rc ? rc : ok();
+}
+
+size_t dsv4_attn_workspace(int32_t n_rows, int32_t n_heads, int32_t dim, int64_t max_rows_per_query) {
+  if (n_rows < 0 || n_heads < 1 || dim < 1 || max_rows_per_query < 0) return 0;
+  return attn_ws(n_rows, n_heads, dim, max_rows_per_query);
+}
+
+static int attn_common(const char *who, const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_t n_heads,
+                       int32_t dim, const dsv4_rows *window, int32_t W, const dsv4_rows *pool, int pool_needed,
+                       int32_t rope_dim, double rope_theta, void *out, int32_t out_dtype) {
+  int rc = check_queries(q);
+  if (rc) return rc;
+  if (!qv || !out) return fail(DSV4_EINVAL, "%s: NULL q/out", who);
+  if (W < 0) return fail(DSV4_EINVAL, "%s: W %d", who, W);
+  if (W > 0 && (rc = check_rows(window, "window", dim))) return rc;
+  if (W > 0 && !window->first_tok) return fail(DSV4_EINVAL, "%s: window rows need first_tok", who);
+  if (pool_needed && (rc = check_rows(pool, "pool", dim))) return rc;
+  if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
+    return fail(DSV4_EINVAL, "%s: rope_dim %d (even, <= min(dim, 64))", who, rope_dim);
+  if (rope_dim > 0 && !(rope_theta > 0)) return fail(DSV4_EINVAL, "%s: rope_theta must be > 0", who);
+  if (out_dtype != DSV4_F32 && out_dtype != DSV4_BF16) return fail(DSV4_ENOTSUP, "%s: out dtype %d", who, out_dtype);
+  const int wdt = W > 0 ? window->dtype : -1, pdt = pool_needed ? pool->dtype : -1;
+  if (q_dtype == DSV4_F32) {
+    if ((W > 0 && wdt != DSV4_F32) || (pool_needed && pdt != DSV4_F32))
+      return fail(DSV4_ENOTSUP, "%s: fp32 queries need fp32 rows", who);
+    if (n_heads < 1 || n_heads > 64 || dim < 2 || dim > 512 || (dim & 1) || n_heads * dim > 16384 ||
+        ((size_t)n_heads * dim + 32 * (size_t)dim + 35 * (size_t)n_heads) * 4 > 65536)
+      return fail(DSV4_ENOTSUP, "%s: fp32 path limits (n_heads %d, dim %d)", who, n_heads, dim);
+  } else if (q_dtype == DSV4_BF16) {
+    if (dim != 512) return fail(DSV4_ENOTSUP, "%s: bf16 path needs dim 512 (got %d)", who, dim);
+    if (n_heads < 16 || n_heads > 64 || n_heads % 16)
+      return fail(DSV4_ENOTSUP, "%s: bf16 path needs n_heads in {16,32,48,64} (got %d)", who, n_heads);
+    const bool ok_w = W == 0 || wdt == DSV4_BF16 || wdt == DSV4_FP8R;
+    const bool ok_p = !pool_needed || pdt == DSV4_BF16 || pdt == DSV4_FP8R;
+    if (!ok_w || !ok_p) return fail(DSV4_ENOTSUP, "%s: bf16 queries need BF16 or FP8R rows", who);
+    if (W > 0 && pool_needed && wdt != pdt) return fail(DSV4_ENOTSUP, "%s: window and pool dtypes differ", who);
+  } else {
+    return fail(DSV4_ENOTSUP, "%s: query dtype %d", who, q_dtype);
+  }
+  return DSV4_OK;
+}
+
+int dsv4_sparse_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_t n_heads, int32_t dim,
+                     const dsv4_rows *window, int32_t W, const dsv4_rows *pool, const int32_t *idx, int32_t topk,
+                     const float *sinks, float sm_scale, int32_t rope_dim, double rope_theta, void *out,
+                     int32_t out_dtype, void *ws, size_t ws_bytes, hipStream_t stream) {
+  if (topk < 0 || topk > 2048) return fail(DSV4_EINVAL, "sparse_attn: topk %d (0..2048)", topk);
+  if (topk > 0 && !idx) return fail(DSV4_EINVAL, "sparse_attn: idx is NULL");
+  int rc = attn_common("sparse_attn", q, qv, q_dtype, n_heads, dim, window, W, pool, topk > 0, rope_dim, rope_theta,
+                       out, out_dtype);
+  if (rc) return rc;
+  const int64_t max_rows = (int64_t)W + topk;
+  const size_t need = attn_ws(q->n_rows, n_heads, dim, max_rows);
+  if (q_dtype != DSV4_F32 && need > 0 && (!ws || ws_bytes < need))
+    return fail(DSV4_EWORKSPACE, "sparse_attn: workspace %zu bytes, need %zu", ws_bytes, need);
+  rc = launch_attn(q, qv, q_dtype, n_heads, dim, window, W, topk > 0 ? pool : nullptr, idx, topk, 1, 1, sinks,
+                   sm_scale, rope_dim, rope_theta, out, out_dtype, ws, max_rows, stream);
+  return rc ? rc : ok();
+}
+
+int dsv4_hca_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_t n_heads, int32_t dim,
+                  const dsv4_rows *window, int32_t W, const dsv4_rows *pool, int32_t m, const float *sinks,
+                  float sm_scale, int32_t rope_dim, double rope_theta, void *out, int32_t out_dtype, void *ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  if (m < 1) return fail(DSV4_EINVAL, "hca_attn: m %d", m);
+  const int have_pool = pool != nullptr;
+  int rc = attn_common("hca_attn", q, qv, q_dtype, n_heads, dim, window, W, pool, have_pool, rope_dim, rope_theta,
+                       out, out_dtype);
+  if (rc) return rc;
+  const int64_t max_rows = (int64_t)W + (have_pool ? pool->seq_stride : 0);
+  const size_t need = attn_ws(q->n_rows, n_heads, dim, max_rows);
+  if (q_dtype != DSV4_F32 && need > 0 && (!ws || ws_bytes < need))
+    return fail(DSV4_EWORKSPACE, "hca_attn: workspace %zu bytes, need %zu", ws_bytes, need);
+  rc = launch_attn(q, qv, q_dtype, n_heads, dim, window, W, have_pool ? pool : nullptr, nullptr, 0, m, 0, sinks,
+                   sm_scale, rope_dim, rope_theta, out, out_dtype, ws, max_rows, stream);
+  return rc ? rc : ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,643 @@
+// dsv4_attn.hip -- CSA / HCA core attention with one shared K=V head, for gfx950.
+//
+// HF DeepSeek-V4 page, "Hybrid attention" backbone: multi-query attention with a
+// single K=V head read as both key and value; partial RoPE on the last
+// qk_rope_head_dim channels with the inverse rotation (-p) on the output slice;
+// a learned per-head sink; a sliding-window K=V branch concatenated with the
+// compressor's entries.  "Attention mask layout": CSA queries see the
+// indexer's picks (-1 masked), HCA queries every entry w < (t+1)/m.
+//
+// Per query row r (sequence b, token t, position p) the row list is
+//   [window rows holding tokens max(t-W+1, first_tok) .. t] ++ [pool rows]
+// (CSA: the valid idx[r, :], HCA: entries 0 .. min(count, (t+1)/m) - 1).
+//
+// k_attn_mfma<D, NW, FP8>: one workgroup per (query row, row split).  The 64
+// query heads are the MFMA dimension that is shared by every row (MQA), so a
+// 32-row K=V tile is staged once in LDS and used by all heads:
+//   Ks [32][D+8]  row-major  -> A operand of S^T = K q~^T   (16x16x32 f16)
+//   Vt [D][32+4]  transposed -> A operand of O^T = V^T P^T  (16x16x32 f16)
+// Wave w owns heads 16w..16w+15: q~ (rotated, scaled by sm_scale*log2 e) stays
+// in registers as the B operand, the 16x16 score tile S^T lands with each lane
+// holding 8 rows of one head, which is exactly the B-operand layout P^T needs
+// for the PV product (no shuffle of P), and O^T accumulates with each lane
+// holding 4 dims of the same head (so the online-softmax rescale is per lane).
+// The tile, q~ and P are fp16 on the matrix cores: stored bf16 values are exact
+// in fp16 (|x| < 65504), and fp16's 11-bit significand keeps the rounding of
+// q~ and P four times smaller than bf16 would, which matters when a query has
+// only a few rows and every logit error moves the output directly.  FP8 rows
+// (E4M3 x row scale, bf16 rope channels) are decoded to fp16 while staging.
+// Several splits per query (decode) write unnormalised partials that
+// k_attn_combine merges with the sink.
+//
+// k_attn_f32: scalar fp32 path for small fp32 shapes.
+#include "dsv4_common.h"
+
+namespace dsv4 {
+
+struct RowSrc {
+  const uint8_t *data;
+  const float *rscale;
+  const int32_t *count;
+  const int32_t *first_tok;
+  int64_t stride;
+  int64_t rbytes;
+  int dtype, tail;
+};
+
+struct AttnArgs {
+  const int32_t *seq, *tok;
+  const int64_t *pos0;
+  const void *q;
+  int T, H, qdtype;
+  RowSrc win;
+  int W;
+  RowSrc pool;
+  const int32_t *idx;
+  int topk, m, csa;
+  const float *sinks;
+  float scale_log2;   // sm_scale * log2(e)
+  int rope_dim;
+  double theta;
+  void *out;
+  int out_dtype;
+  int nsplit;
+  float *part_o;      // [T*nsplit*H, D]
+  float *part_ml;     // [T*nsplit*H, 2]
+};
+
+constexpr int kMaxSel = 2048;
+
+// Rows of one query: window part [0, nwin) then pool part.
+struct RowPlan {
+  int b, t, nwin, nsel, wlo;
+  int64_t p;
+};
+
+__device__ __forceinline__ RowPlan row_plan(const AttnArgs &A, int r) {
+  RowPlan P;
+  P.b = A.seq[r];
+  P.t = A.tok[r];
+  P.p = (A.pos0 ? A.pos0[P.b] : 0) + P.t;
+  P.nwin = 0;
+  P.wlo = 0;
+  if (A.W > 0) {
+    const int ft = A.win.first_tok ? A.win.first_tok[P.b] : 0;
+    const int wc = A.win.count[P.b];
+    int lo = P.t - A.W + 1;
+    lo = lo < ft ? ft : lo;
+    lo = lo < 0 ? 0 : lo;
+    int hi = P.t;
+    hi = hi > ft + wc - 1 ? ft + wc - 1 : hi;
+    P.wlo = lo - ft;   // storage row of the first window token
+    P.nwin = hi >= lo ? hi - lo + 1 : 0;
+  }
+  P.nsel = 0;
+  if (!A.csa && A.pool.data) {
+    const int n = (P.t + 1) / A.m;
+    const int c = A.pool.count[P.b];
+    P.nsel = n < c ? n : c;
+  }
+  return P;
+}
+
+// Compact the valid entries of idx[r, :] (>= 0 and < count) into sel[],
+// preserving order.  Block-wide; returns the count.
+template <int NT>
+__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int cnt = A.pool.count[b];
+  int total = 0;
+  for (int base = 0; base < A.topk; base += NT) {
+    const int i = base + tid;
+    int v = -1;
+    if (i < A.topk) v = A.idx[(int64_t)r * A.topk + i];
+    const bool ok = v >= 0 && v < cnt;
+    const unsigned long long bal = __ballot(ok);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) sh_wave[wv] = __popcll(bal);
+    __syncthreads();
+    int off = total;
+    for (int w = 0; w < wv; ++w) off += sh_wave[w];
+    int tot = 0;
+    for (int w = 0; w < NT / 64; ++w) tot += sh_wave[w];
+    if (ok) sel[off + before] = v;
+    total += tot;
+    __syncthreads();
+  }
+  return total;
+}
+
+__device__ __forceinline__ const uint8_t *row_ptr(const AttnArgs &A, const RowPlan &P, const int *sel, int i,
+                                                  float *scale) {
+  if (i < P.nwin) {
+    const int64_t g = (int64_t)P.b * A.win.stride + P.wlo + i;
+    *scale = A.win.rscale ? A.win.rscale[g] : 1.f;
+    return A.win.data + g * A.win.rbytes;
+  }
+  const int s = A.csa ? sel[i - P.nwin] : i - P.nwin;
+  const int64_t g = (int64_t)P.b * A.pool.stride + s;
+  *scale = A.pool.rscale ? A.pool.rscale[g] : 1.f;
+  return A.pool.data + g * A.pool.rbytes;
+}
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  return pack_f16x2(bf16_to_f32((uint16_t)(v & 0xFFFFu)), bf16_to_f32((uint16_t)(v >> 16)));
+}
+
+// 8 channels [8*c8, 8*c8+8) of a stored row -> 8 fp16 (packed in a u32x4)
+template <int D, bool FP8>
+__device__ __forceinline__ u32x4 load8(const uint8_t *row, int c8, float scale, int tail) {
+  const int d0 = 8 * c8;
+  if (!FP8 || d0 >= D - tail) {
+    const u32x4 v = FP8 ? *reinterpret_cast<const u32x4 *>(row + (D - tail) + 2 * (d0 - (D - tail)))
+                        : *reinterpret_cast<const u32x4 *>(row + 16 * c8);
+    return u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+  }
+  const u32x2 v = *reinterpret_cast<const u32x2 *>(row + d0);
+  u32x4 o;
+  o.x = pack_f16x2(e4m3_to_f32(v.x & 255u) * scale, e4m3_to_f32((v.x >> 8) & 255u) * scale);
+  o.y = pack_f16x2(e4m3_to_f32((v.x >> 16) & 255u) * scale, e4m3_to_f32(v.x >> 24) * scale);
+  o.z = pack_f16x2(e4m3_to_f32(v.y & 255u) * scale, e4m3_to_f32((v.y >> 8) & 255u) * scale);
+  o.w = pack_f16x2(e4m3_to_f32((v.y >> 16) & 255u) * scale, e4m3_to_f32(v.y >> 24) * scale);
+  return o;
+}
+
+template <int D, int NW, bool FP8>
+__global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
+  constexpr int NT = NW * 64;
+  constexpr int KP = D + 8;   // Ks row pitch (fp16 elements)
+  constexpr int VP = 36;      // Vt row pitch (fp16 elements)
+  constexpr int NJ = D / 32;  // k-steps of the QK product
+  constexpr int NDB = D / 16; // 16-dim blocks of the output
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[32 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ int sel[kMaxSel];
+  __shared__ float rc[32], rs[32];
+  __shared__ int sh_wave[NW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int r = (A.T - 1) - (int)(blockIdx.x / A.nsplit);   // longest rows first
+  const int split = blockIdx.x % A.nsplit;
+  RowPlan P = row_plan(A, r);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_wave);
+  const int nrows = P.nwin + P.nsel;
+  const int ntiles = (nrows + 31) / 32;
+  const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
+  const int tile_lo = split * tps;
+  const int tile_hi = min(ntiles, tile_lo + tps);
+  const int R = A.rope_dim;
+
+  if (tid < R / 2) rope_cs((double)P.p, tid, R, A.theta, 1.f, &rc[tid], &rs[tid]);
+  __syncthreads();
+
+  // q~ = RoPE(q) * sm_scale * log2(e) as the B operand: lane holds head h,
+  // dims 32j + 8g .. +8
+  const int h = 16 * wv + c;
+  f16x8 qb[NJ];
+  {
+    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + h) * D;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int d0 = 32 * j + 8 * g;
+      const u32x4 raw = *reinterpret_cast<const u32x4 *>(qr + d0);
+      float x[8];
+      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_to_f32((uint16_t)(wds[k] & 0xFFFF));
+        x[2 * k + 1] = bf16_to_f32((uint16_t)(wds[k] >> 16));
+      }
+      if (d0 >= D - R) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pi = (d0 + 2 * k - (D - R)) >> 1;
+          const float cs = rc[pi], sn = rs[pi];
+          const float a = x[2 * k] * cs - x[2 * k + 1] * sn, bb = x[2 * k] * sn + x[2 * k + 1] * cs;
+          x[2 * k] = a;
+          x[2 * k + 1] = bb;
+        }
+      }
+      u32x4 o;
+      o.x = pack_f16x2(x[0] * A.scale_log2, x[1] * A.scale_log2);
+      o.y = pack_f16x2(x[2] * A.scale_log2, x[3] * A.scale_log2);
+      o.z = pack_f16x2(x[4] * A.scale_log2, x[5] * A.scale_log2);
+      o.w = pack_f16x2(x[6] * A.scale_log2, x[7] * A.scale_log2);
+      __builtin_memcpy(&qb[j], &o, 16);
+    }
+  }
+
+  f32x4 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int tile = tile_lo; tile < tile_hi; ++tile) {
+    const int base = tile * 32;
+    __syncthreads();   // previous tile fully consumed
+    // stage 32 rows: item = (row quad q4, 8-channel chunk c8)
+    for (int it = tid; it < 8 * (D / 8); it += NT) {
+      const int q4 = it / (D / 8), c8 = it % (D / 8);
+      u32x4 v[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = base + 4 * q4 + rr;
+        if (i < nrows) {
+          float sc;
+          const uint8_t *rp = row_ptr(A, P, sel, i, &sc);
+          v[rr] = load8<D, FP8>(rp, c8, sc, i < P.nwin ? A.win.tail : A.pool.tail);
+        } else {
+          v[rr] = u32x4{0u, 0u, 0u, 0u};
+        }
+        *reinterpret_cast<u32x4 *>(&Ks[(4 * q4 + rr) * KP + 8 * c8]) = v[rr];
+      }
+      // transpose into Vt[dim][row]: 4 rows of one dim are 8 contiguous bytes
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t a0 = v[0][k], a1 = v[1][k], a2 = v[2][k], a3 = v[3][k];
+        const u32x2 lo2 = u32x2{(a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16)};
+        const u32x2 hi2 = u32x2{(a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u)};
+        *reinterpret_cast<u32x2 *>(&Vt[(8 * c8 + 2 * k) * VP + 4 * q4]) = lo2;
+        *reinterpret_cast<u32x2 *>(&Vt[(8 * c8 + 2 * k + 1) * VP + 4 * q4]) = hi2;
+      }
+    }
+    __syncthreads();
+
+    // S^T (rows x heads) = K q~^T : two 16-row blocks
+    f32x4 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t *kr = &Ks[(16 * mb + c) * KP + 8 * g];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const f16x8 a = *reinterpret_cast<const f16x8 *>(kr + 32 * j);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[j], acc, 0, 0, 0);
+      }
+      s[mb] = acc;
+    }
+    // lane holds head h, rows base + 16mb + 4g + i
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = base + 16 * mb + 4 * g + i;
+        if (row >= nrows) s[mb][i] = -INFINITY;
+        mloc = fmaxf(mloc, s[mb][i]);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);   // finite: every tile has a valid row
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f, p[8];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[4 * mb + i] = exp2f(s[mb][i] - m_new);
+        psum += p[4 * mb + i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    u32x4 pw;
+    pw.x = pack_f16x2(p[0], p[1]);
+    pw.y = pack_f16x2(p[2], p[3]);
+    pw.z = pack_f16x2(p[4], p[5]);
+    pw.w = pack_f16x2(p[6], p[7]);
+    f16x8 pb;
+    __builtin_memcpy(&pb, &pw, 16);
+    // O^T (dims x heads) += V^T P^T ; k index 8g+i <-> tile row 4g+i (i<4), 16+4g+(i-4)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint16_t *vr = &Vt[(16 * db + c) * VP];
+      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 4 * g);
+      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 16 + 4 * g);
+      const u32x4 av = u32x4{lo.x, lo.y, hi.x, hi.y};
+      f16x8 a;
+      __builtin_memcpy(&a, &av, 16);
+      f32x4 o = acc_o[db];
+      o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
+      acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, o, 0, 0, 0);
+    }
+  }
+
+  // row sums of the four lane groups
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+
+  if (A.nsplit > 1) {
+    const int64_t pr = ((int64_t)r * A.nsplit + split) * A.H + h;
+    float *po = A.part_o + pr * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * g) = acc_o[db];
+    if (g == 0) {
+      A.part_ml[2 * pr] = m_run;
+      A.part_ml[2 * pr + 1] = l_run;
+    }
+    return;
+  }
+
+  float f = 1.f, den = l_run;
+  if (A.sinks) {
+    const float sg = A.sinks[h] * kLog2e;
+    const float M = fmaxf(m_run, sg);
+    f = exp2f(m_run - M);
+    den = l_run * f + exp2f(sg - M);
+  }
+  const float inv = den > 0.f ? f / den : 0.f;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    float o[4];
+    const int d0 = 16 * db + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = acc_o[db][i] * inv;
+    if (d0 >= D - R) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int pi = (d0 + 2 * k - (D - R)) >> 1;
+        const float cs = rc[pi], sn = rs[pi];
+        const float a = o[2 * k] * cs + o[2 * k + 1] * sn, bb = -o[2 * k] * sn + o[2 * k + 1] * cs;
+        o[2 * k] = a;
+        o[2 * k + 1] = bb;
+      }
+    }
+    const int64_t oe = ((int64_t)r * A.H + h) * D + d0;
+    if (A.out_dtype == DSV4_F32) {
+      *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
+    } else {
+      *reinterpret_cast<u32x2 *>((uint16_t *)A.out + oe) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+  }
+}
+
+// Merge split partials: grid (T * H), block D/2 threads (one channel pair each).
+template <int D>
+__global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
+  const int rh = blockIdx.x;
+  const int r = rh / A.H, h = rh % A.H;
+  const int pr = threadIdx.x;
+  __shared__ float rc[32], rs[32];
+  const int b = A.seq[r];
+  const int64_t p = (A.pos0 ? A.pos0[b] : 0) + A.tok[r];
+  const int R = A.rope_dim;
+  if (pr < R / 2) rope_cs((double)p, pr, R, A.theta, 1.f, &rc[pr], &rs[pr]);
+  __syncthreads();
+  float M = A.sinks ? A.sinks[h] * kLog2e : -INFINITY;
+  for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, A.part_ml[2 * (((int64_t)r * A.nsplit + s) * A.H + h)]);
+  float den = A.sinks ? exp2f(A.sinks[h] * kLog2e - M) : 0.f;
+  float o0 = 0.f, o1 = 0.f;
+  for (int s = 0; s < A.nsplit; ++s) {
+    const int64_t q = ((int64_t)r * A.nsplit + s) * A.H + h;
+    const float ms = A.part_ml[2 * q];
+    if (ms == -INFINITY) continue;   // split without rows
+    const float f = exp2f(ms - M);
+    den += A.part_ml[2 * q + 1] * f;
+    const float2 v = reinterpret_cast<const float2 *>(A.part_o + q * D)[pr];
+    o0 = fmaf(v.x, f, o0);
+    o1 = fmaf(v.y, f, o1);
+  }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  o0 *= inv;
+  o1 *= inv;
+  const int d0 = 2 * pr;
+  if (d0 >= D - R) {
+    const int pi = (d0 - (D - R)) >> 1;
+    const float a = o0 * rc[pi] + o1 * rs[pi], bb = -o0 * rs[pi] + o1 * rc[pi];
+    o0 = a;
+    o1 = bb;
+  }
+  const int64_t oe = ((int64_t)r * A.H + h) * D + d0;
+  if (A.out_dtype == DSV4_F32) *reinterpret_cast<float2 *>((float *)A.out + oe) = make_float2(o0, o1);
+  else *reinterpret_cast<uint32_t *>((uint16_t *)A.out + oe) = pack_bf16x2(o0, o1);
+}
+
+// -------------------------------------------------------------------- fp32 path
+// One workgroup (256 threads) per query row.  Requires H*D <= 8192, H <= 64,
+// D <= 512, float32 rows and queries.
+__global__ __launch_bounds__(256) void k_attn_f32(AttnArgs A, int D) {
+  extern __shared__ float sm[];
+  const int H = A.H;
+  float *qs = sm;                 // [H*D]
+  float *rows = qs + H * D;       // [32*D]
+  float *lg = rows + 32 * D;      // [H*32]
+  float *mrun = lg + H * 32;      // [H]
+  float *alph = mrun + H;         // [H]
+  float *lrun = alph + H;         // [H]
+  __shared__ int sel[kMaxSel];
+  __shared__ float rc[32], rs[32];
+  __shared__ int sh_wave[4];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
+  RowPlan P = row_plan(A, r);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_wave);
+  const int nrows = P.nwin + P.nsel;
+  const int R = A.rope_dim;
+  if (tid < R / 2) rope_cs((double)P.p, tid, R, A.theta, 1.f, &rc[tid], &rs[tid]);
+  __syncthreads();
+  const float *q = (const float *)A.q + (int64_t)r * H * D;
+  for (int e = tid; e < H * D / 2; e += 256) {
+    const int hh = e / (D / 2), d0 = 2 * (e % (D / 2));
+    float x0 = q[hh * D + d0], x1 = q[hh * D + d0 + 1];
+    if (d0 >= D - R) {
+      const int pi = (d0 - (D - R)) >> 1;
+      const float a = x0 * rc[pi] - x1 * rs[pi], bb = x0 * rs[pi] + x1 * rc[pi];
+      x0 = a;
+      x1 = bb;
+    }
+    qs[hh * D + d0] = x0 * A.scale_log2;
+    qs[hh * D + d0 + 1] = x1 * A.scale_log2;
+  }
+  for (int hh = tid; hh < H; hh += 256) { mrun[hh] = -INFINITY; lrun[hh] = 0.f; }
+  constexpr int MAXO = 32;        // (H*D/2) / 256 pairs per thread at most
+  float o0[MAXO], o1[MAXO];
+#pragma unroll
+  for (int u = 0; u < MAXO; ++u) { o0[u] = 0.f; o1[u] = 0.f; }
+  const int npairs = H * D / 2;
+  for (int base = 0; base < nrows; base += 32) {
+    __syncthreads();
+    for (int e = tid; e < 32 * D; e += 256) {
+      const int j = e / D, d = e % D;
+      float v = 0.f;
+      if (base + j < nrows) {
+        float sc;
+        const uint8_t *rp = row_ptr(A, P, sel, base + j, &sc);
+        v = reinterpret_cast<const float *>(rp)[d];
+      }
+      rows[e] = v;
+    }
+    __syncthreads();
+    for (int e = tid; e < H * 32; e += 256) {
+      const int hh = e / 32, j = e % 32;
+      float d = -INFINITY;
+      if (base + j < nrows) {
+        d = 0.f;
+        for (int k = 0; k < D; ++k) d = fmaf(qs[hh * D + k], rows[j * D + k], d);
+      }
+      lg[e] = d;
+    }
+    __syncthreads();
+    for (int hh = tid; hh < H; hh += 256) {
+      float mx = mrun[hh];
+      for (int j = 0; j < 32; ++j) mx = fmaxf(mx, lg[hh * 32 + j]);
+      const float al = exp2f(mrun[hh] - mx);
+      float sum = 0.f;
+      for (int j = 0; j < 32; ++j) {
+        const float pj = exp2f(lg[hh * 32 + j] - mx);
+        lg[hh * 32 + j] = pj;
+        sum += pj;
+      }
+      lrun[hh] = lrun[hh] * al + sum;
+      mrun[hh] = mx;
+      alph[hh] = al;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < MAXO; ++u) {
+      const int e = tid + 256 * u;
+      if (e < npairs) {
+        const int hh = e / (D / 2), d0 = 2 * (e % (D / 2));
+        const float al = alph[hh];
+        float a0 = o0[u] * al, a1 = o1[u] * al;
+        for (int j = 0; j < 32; ++j) {
+          const float pj = lg[hh * 32 + j];
+          a0 = fmaf(pj, rows[j * D + d0], a0);
+          a1 = fmaf(pj, rows[j * D + d0 + 1], a1);
+        }
+        o0[u] = a0;
+        o1[u] = a1;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < MAXO; ++u) {
+    const int e = tid + 256 * u;
+    if (e < npairs) {
+      const int hh = e / (D / 2), d0 = 2 * (e % (D / 2));
+      const float mr = mrun[hh];
+      float f = 1.f, den = lrun[hh];
+      if (A.sinks) {
+        const float sg = A.sinks[hh] * kLog2e;
+        const float M = fmaxf(mr, sg);
+        f = exp2f(mr - M);
+        den = lrun[hh] * f + exp2f(sg - M);
+      }
+      const float inv = den > 0.f ? f / den : 0.f;
+      float x0 = o0[u] * inv, x1 = o1[u] * inv;
+      if (d0 >= D - R) {
+        const int pi = (d0 - (D - R)) >> 1;
+        const float a = x0 * rc[pi] + x1 * rs[pi], bb = -x0 * rs[pi] + x1 * rc[pi];
+        x0 = a;
+        x1 = bb;
+      }
+      const int64_t oe = ((int64_t)r * H + hh) * D + d0;
+      if (A.out_dtype == DSV4_F32) *reinterpret_cast<float2 *>((float *)A.out + oe) = make_float2(x0, x1);
+      else *reinterpret_cast<uint32_t *>((uint16_t *)A.out + oe) = pack_bf16x2(x0, x1);
+    }
+  }
+}
+
+}  // namespace dsv4
+
+using namespace dsv4;
+
+namespace dsv4host {
+
+static RowSrc mk_src(const dsv4_rows *rw) {
+  RowSrc s{};
+  if (!rw) return s;
+  s.data = (const uint8_t *)rw->data;
+  s.rscale = rw->row_scale;
+  s.count = rw->count;
+  s.first_tok = rw->first_tok;
+  s.stride = rw->seq_stride;
+  s.dtype = rw->dtype;
+  s.tail = rw->tail;
+  switch (rw->dtype) {
+  case DSV4_F32: s.rbytes = 4LL * rw->dim; break;
+  case DSV4_BF16: s.rbytes = 2LL * rw->dim; break;
+  case DSV4_FP8R: s.rbytes = (int64_t)(rw->dim - rw->tail) + 2LL * rw->tail; break;
+  default: s.rbytes = 0;
+  }
+  return s;
+}
+
+// Splits per query: enough workgroups to fill the chip when rows are few.
+int attn_nsplit(int T, int64_t max_rows) {
+  const int64_t tiles = (max_rows + 31) / 32;
+  if (T >= 512 || tiles <= 1) return 1;
+  int64_t want = (512 + T - 1) / T;          // aim at >= 512 workgroups
+  int64_t cap = (tiles + 1) / 2;             // at least two tiles per split
+  if (want > cap) want = cap;
+  if (want > 64) want = 64;
+  return want < 1 ? 1 : (int)want;
+}
+
+size_t attn_ws(int T, int H, int D, int64_t max_rows) {
+  const int ns = attn_nsplit(T, max_rows);
+  if (ns <= 1) return 0;
+  return (size_t)T * ns * H * ((size_t)D + 2) * 4 + 256;
+}
+
+int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
+                const dsv4_rows *pool, const int32_t *idx, int topk, int m, int csa, const float *sinks,
+                float sm_scale, int rope_dim, double theta, void *out, int out_dtype, void *ws,
+                int64_t max_rows, hipStream_t st) {
+  const int T = q->n_rows;
+  if (T == 0) return DSV4_OK;
+  AttnArgs A{};
+  A.seq = q->seq;
+  A.tok = q->tok;
+  A.pos0 = q->pos0;
+  A.q = qv;
+  A.T = T;
+  A.H = H;
+  A.qdtype = q_dtype;
+  A.win = mk_src(W > 0 ? win : nullptr);
+  A.W = W > 0 ? W : 0;
+  A.pool = mk_src(pool);
+  A.idx = idx;
+  A.topk = csa ? topk : 0;
+  A.m = m;
+  A.csa = csa;
+  A.sinks = sinks;
+  A.scale_log2 = sm_scale * kLog2e;
+  A.rope_dim = rope_dim;
+  A.theta = theta;
+  A.out = out;
+  A.out_dtype = out_dtype;
+  if (q_dtype == DSV4_F32) {
+    A.nsplit = 1;
+    const size_t lds = ((size_t)H * D + 32 * (size_t)D + 32 * (size_t)H + 3 * (size_t)H) * 4;
+    hipLaunchKernelGGL(k_attn_f32, dim3(T), dim3(256), lds, st, A, D);
+    return check_launch("k_attn_f32");
+  }
+  const int ns = attn_nsplit(T, max_rows);
+  A.nsplit = ns;
+  if (ns > 1) {
+    A.part_o = (float *)ws;
+    A.part_ml = A.part_o + (size_t)T * ns * H * D;
+  }
+  const bool fp8 = (W > 0 && win->dtype == DSV4_FP8R) || (pool && pool->dtype == DSV4_FP8R);
+  dim3 grid((unsigned)((int64_t)T * ns));
+  switch (H / 16) {
+#define DSV4_ATT(NW)                                                                                  \
+  case NW:                                                                                            \
+    if (fp8) hipLaunchKernelGGL((k_attn_mfma<512, NW, true>), grid, dim3(NW * 64), 0, st, A);         \
+    else hipLaunchKernelGGL((k_attn_mfma<512, NW, false>), grid, dim3(NW * 64), 0, st, A);            \
+    break;
+    DSV4_ATT(1)
+    DSV4_ATT(2)
+    DSV4_ATT(3)
+    DSV4_ATT(4)
+#undef DSV4_ATT
+  }
+  int rc = check_launch("k_attn_mfma");
+  if (rc || ns == 1) return rc;
+  hipLaunchKernelGGL(k_attn_combine<512>, dim3((unsigned)((int64_t)T * H)), dim3(256), 0, st, A);
+  return check_launch("k_attn_combine");
+}
+
+}  // namespace dsv4host

@@ -1,0 +1,150 @@
+// dsv4_compress.hip -- KV compressor (softmax-gated pooling with a learned
+// position bias) and the partial interleaved RoPE kernel, for gfx950.
+//
+// HF DeepSeek-V4 page, "Hybrid attention": CSA pools every m = 4 tokens over
+// overlapping windows, HCA every m' = 128 tokens over non-overlapping windows;
+// insight.ai.kr: the pooling is softmax-gated with a learned per-position bias.
+//
+// Design: HBM-bound streaming.  One thread owns one (entry, channel pair) and
+// walks the entry's window with an online softmax (running max, rescaled sum),
+// so every c/z element is read once per window it belongs to (twice for the
+// overlapping CSA windows, the second read coming from L2).  Consecutive
+// threads own consecutive channel pairs: each window step is one coalesced
+// 4-byte (bf16x2) or 8-byte (f32x2) load per thread.  The rope epilogue
+// rotates the pair at P_s = pos0 + s*m with an fp64 angle.
+#include "dsv4_common.h"
+
+namespace dsv4 {
+
+template <typename T>
+struct Pair;
+template <>
+struct Pair<float> {
+  static __device__ __forceinline__ float2 load(const void *p, int64_t i) {
+    return reinterpret_cast<const float2 *>(p)[i];
+  }
+  static __device__ __forceinline__ void store(void *p, int64_t i, float a, float b) {
+    reinterpret_cast<float2 *>(p)[i] = make_float2(a, b);
+  }
+};
+template <>
+struct Pair<uint16_t> {
+  static __device__ __forceinline__ float2 load(const void *p, int64_t i) {
+    uint32_t u = reinterpret_cast<const uint32_t *>(p)[i];
+    return make_float2(bf16_to_f32((uint16_t)(u & 0xFFFF)), bf16_to_f32((uint16_t)(u >> 16)));
+  }
+  static __device__ __forceinline__ void store(void *p, int64_t i, float a, float b) {
+    reinterpret_cast<uint32_t *>(p)[i] = pack_bf16x2(a, b);
+  }
+};
+
+// grid: x = entry * pair_blocks + pair block, y = sequence
+template <typename TI, typename TO>
+__global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, const void *__restrict__ z,
+                                                  const float *__restrict__ bias, int S, int dim, int m,
+                                                  int overlap, int rope_dim, double theta,
+                                                  const int64_t *__restrict__ pos0, void *__restrict__ pool) {
+  const int half = dim >> 1;
+  const int pblocks = (half + blockDim.x - 1) / blockDim.x;
+  const int s = blockIdx.x / pblocks, b = blockIdx.y;
+  const int pr = (blockIdx.x % pblocks) * blockDim.x + threadIdx.x;   // channel pair
+  if (pr >= half) return;
+  const int N = S / m;
+  const int t0 = overlap ? (s - 1) * m : s * m;
+  const int width = overlap ? 2 * m : m;
+  const int jlo = t0 < 0 ? -t0 : 0;
+  const int64_t rowbase = (int64_t)b * S;
+  float mx0 = -INFINITY, mx1 = -INFINITY, den0 = 0.f, den1 = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int j = jlo; j < width; ++j) {
+    const int t = t0 + j;
+    if (t >= S) break;
+    const int64_t e = (rowbase + t) * half + pr;
+    const float2 zz = Pair<TI>::load(z, e);
+    const float2 cc = Pair<TI>::load(c, e);
+    const float2 bb = reinterpret_cast<const float2 *>(bias)[(int64_t)j * half + pr];
+    const float g0 = zz.x + bb.x, g1 = zz.y + bb.y;
+    // online softmax per channel
+    if (g0 > mx0) { const float r = __expf(mx0 - g0); den0 *= r; acc0 *= r; mx0 = g0; }
+    if (g1 > mx1) { const float r = __expf(mx1 - g1); den1 *= r; acc1 *= r; mx1 = g1; }
+    const float e0 = __expf(g0 - mx0), e1 = __expf(g1 - mx1);
+    den0 += e0; acc0 = fmaf(e0, cc.x, acc0);
+    den1 += e1; acc1 = fmaf(e1, cc.y, acc1);
+  }
+  float o0 = acc0 / den0, o1 = acc1 / den1;
+  const int d0 = 2 * pr;
+  if (rope_dim > 0 && d0 >= dim - rope_dim) {
+    const int pair = (d0 - (dim - rope_dim)) >> 1;
+    const double P = (double)((pos0 ? pos0[b] : 0) + (int64_t)s * m);
+    float cs, sn;
+    rope_cs(P, pair, rope_dim, theta, 1.f, &cs, &sn);
+    const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
+    o0 = r0; o1 = r1;
+  }
+  Pair<TO>::store(pool, ((int64_t)b * N + s) * half + pr, o0, o1);
+}
+
+// grid: x = pair blocks, y = row blocks.  y may alias x.
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope(const void *x, void *y, int64_t n_rows,
+                                              int dim, int rope_dim, const int64_t *__restrict__ pos,
+                                              double theta, float sign) {
+  const int half = dim >> 1;
+  const int pr = blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t r = blockIdx.y;
+  if (pr >= half || r >= n_rows) return;
+  const int64_t e = r * half + pr;
+  float2 v = Pair<T>::load(x, e);
+  const int d0 = 2 * pr;
+  if (d0 >= dim - rope_dim) {
+    float cs, sn;
+    rope_cs((double)pos[r], (d0 - (dim - rope_dim)) >> 1, rope_dim, theta, sign, &cs, &sn);
+    const float a = v.x * cs - v.y * sn, bq = v.x * sn + v.y * cs;
+    v.x = a; v.y = bq;
+  }
+  Pair<T>::store(y, e, v.x, v.y);
+}
+
+}  // namespace dsv4
+
+using namespace dsv4;
+
+namespace dsv4host {
+
+int launch_compress(const void *c, const void *z, int in_dtype, const float *bias, int B, int S, int dim,
+                    int m, int overlap, int rope_dim, double theta, const int64_t *pos0, void *pool,
+                    int out_dtype, hipStream_t st) {
+  const int N = S / m;
+  if (B == 0 || N == 0) return DSV4_OK;
+  dim3 grid((unsigned)(N * ((dim / 2 + 255) / 256)), B), block(256);
+#define DSV4_CMP(TI, TO)                                                                               \
+  hipLaunchKernelGGL((k_compress<TI, TO>), grid, block, 0, st, c, z, bias, S, dim, m, overlap, rope_dim, \
+                     theta, pos0, pool)
+  if (in_dtype == DSV4_F32 && out_dtype == DSV4_F32) DSV4_CMP(float, float);
+  else if (in_dtype == DSV4_F32 && out_dtype == DSV4_BF16) DSV4_CMP(float, uint16_t);
+  else if (in_dtype == DSV4_BF16 && out_dtype == DSV4_F32) DSV4_CMP(uint16_t, float);
+  else DSV4_CMP(uint16_t, uint16_t);
+#undef DSV4_CMP
+  return check_launch("k_compress");
+}
+
+int launch_rope(const void *x, void *y, int dtype, int64_t n_rows, int dim, int rope_dim, const int64_t *pos,
+                double theta, int inverse, hipStream_t st) {
+  if (n_rows == 0) return DSV4_OK;
+  const float sign = inverse ? -1.f : 1.f;
+  int64_t done = 0;
+  while (done < n_rows) {   // grid.y is limited to 65535 rows per launch
+    const int64_t n = (n_rows - done) < 65535 ? (n_rows - done) : 65535;
+    dim3 grid((dim / 2 + 255) / 256, (unsigned)n), block(256);
+    const int64_t off = done * (int64_t)dim * (dtype == DSV4_F32 ? 4 : 2);
+    const void *xs = (const char *)x + off;
+    void *ys = (char *)y + off;
+    if (dtype == DSV4_F32)
+      hipLaunchKernelGGL(k_rope<float>, grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, theta, sign);
+    else
+      hipLaunchKernelGGL(k_rope<uint16_t>, grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, theta, sign);
+    done += n;
+  }
+  return check_launch("k_rope");
+}
+
+}  // namespace dsv4host

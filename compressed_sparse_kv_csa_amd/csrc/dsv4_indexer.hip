@@ -1,0 +1,432 @@
+// dsv4_indexer.hip -- Lightning Indexer scoring and per-query top-k for gfx950.
+//
+// HF DeepSeek-V4 page, "Hybrid attention": the indexer scores each query
+// against the compressed pool and keeps the top index_topk blocks;
+// "Attention mask layout": a query sees entry s only once its window closed
+// (s < (t+1)/m) and unused slots carry the -1 sentinel.  insight.ai.kr: the
+// scores are ReLU multi-head dot products; MarkTechPost: the query/key path is
+// MXFP4.
+//
+//   I(r, s) = score_scale * sum_h w[r,h] * max(0, q_idx[r,h,:] . k_pool[b,s,:])
+//
+// Kernels
+//   k_index_scores_mfma<NHB, KS, FP4>  per (query row, entry chunk): 64 heads
+//       as the MFMA M dimension, 16 entries as N, the head dimension as K.
+//       bf16: v_mfma_f32_16x16x32_bf16, KS k-steps of 32.  MXFP4: one scaled
+//       v_mfma_f32_16x16x128_f8f6f4 per head block, the E8M0 block scales fed
+//       straight to the instruction (a lane's 32 k-values are one MX block).
+//       Keys are read once, straight from HBM into MFMA registers; the ReLU,
+//       the head weights and the head sum run on the accumulators.
+//   k_index_scores_f32  scalar fp32 path (small fp32 shapes).
+//   k_topk_chunk / k_topk_merge  exact radix select (4 x 8-bit digits of an
+//       order-preserving key) in LDS, ties to the lower index, stable
+//       compaction so indices come out ascending.
+#include "dsv4_common.h"
+
+namespace dsv4 {
+
+struct IdxQ {
+  const int32_t *seq, *tok;
+  const void *q;          // [T, H, Di] bf16/f32, or [T, H, Di/2] fp4 bytes
+  const uint8_t *qscale;  // [T, H, Di/32] (fp4)
+  const float *w;         // [T, H]
+  int H, Di;
+};
+struct IdxK {
+  const void *data;
+  const uint8_t *bscale;  // fp4 block scales [B*stride, Di/32]
+  const int32_t *count;
+  int64_t stride;
+  int m;
+};
+
+__device__ __forceinline__ int n_visible(int t, int m, int count) {
+  const int n = (t + 1) / m;
+  return n < count ? n : count;
+}
+
+// order-preserving float -> uint32 key (larger float, larger key)
+__device__ __forceinline__ uint32_t fkey(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float keyf(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// -------------------------------------------------------------------- scores (MFMA)
+// grid (T, n_chunks), block 256 (4 waves).  Wave wv handles entry blocks
+// chunk_lo + 16*(wv + 4*it).  Lane l = 16*g + c:
+//   A (query) : head 16*hb + c,   k-slice g   (bf16: dims 32j + 8g .. +8)
+//   B (keys)  : entry e0 + c,     k-slice g
+//   D         : heads 16*hb + 4g + i (i < 4), entry e0 + c
+template <int NHB, int KS, bool FP4>
+__global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, int chunk,
+                                                           float *__restrict__ scores, int64_t ld) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int b = Q.seq[r];
+  const int n = n_visible(Q.tok[r], K.m, K.count[b]);
+  const int lo = blockIdx.y * chunk;
+  const int hi = min(n, lo + chunk);
+  if (lo >= hi) return;
+  const int H = Q.H, Di = Q.Di;
+
+  // query operand and head weights in registers
+  bf16x8 qb[NHB][FP4 ? 1 : KS];
+  i32x8 qf[NHB];
+  int qs[NHB];
+  float wt[NHB][4];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int h = 16 * hb + c;
+    if constexpr (FP4) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>((const uint8_t *)Q.q + ((int64_t)r * H + h) * (Di / 2) + 16 * g);
+      qf[hb] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      qs[hb] = Q.qscale[((int64_t)r * H + h) * (Di / 32) + g];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        qb[hb][j] = *reinterpret_cast<const bf16x8 *>((const uint16_t *)Q.q + ((int64_t)r * H + h) * Di + 32 * j + 8 * g);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wt[hb][i] = Q.w[(int64_t)r * H + 16 * hb + 4 * g + i];
+  }
+
+  const int64_t kbase = (int64_t)b * K.stride;
+  for (int e0 = lo + 16 * wv; e0 < hi; e0 += 64) {
+    const int e = min(e0 + c, hi - 1);   // clamp: lanes past the end re-read a valid row
+    const int64_t row = kbase + e;
+    float s = 0.f;
+    if constexpr (FP4) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>((const uint8_t *)K.data + row * (Di / 2) + 16 * g);
+      const i32x8 kb = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      const int ks = K.bscale[row * (Di / 32) + g];
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[hb], kb, acc, 4, 4, 0, qs[hb], 0, ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], fmaxf(acc[i], 0.f), s);
+      }
+    } else {
+      bf16x8 kb[KS];
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        kb[j] = *reinterpret_cast<const bf16x8 *>((const uint16_t *)K.data + row * Di + 32 * j + 8 * g);
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KS; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][j], kb[j], acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], fmaxf(acc[i], 0.f), s);
+      }
+    }
+    // sum over the four lane groups (heads 4g..4g+3 of every head block)
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if (g == 0 && e0 + c < hi) scores[(int64_t)r * ld + e0 + c] = s * scale;
+  }
+}
+
+// -------------------------------------------------------------------- scores (fp32 VALU)
+// grid (T, n_chunks), block 256: one thread per entry, the query in LDS.
+__global__ __launch_bounds__(256) void k_index_scores_f32(IdxQ Q, IdxK K, float scale, int chunk,
+                                                          float *__restrict__ scores, int64_t ld) {
+  extern __shared__ float qsh[];   // [H*Di] then w[H]
+  const int r = blockIdx.x;
+  const int b = Q.seq[r];
+  const int n = n_visible(Q.tok[r], K.m, K.count[b]);
+  const int lo = blockIdx.y * chunk;
+  const int hi = min(n, lo + chunk);
+  if (lo >= hi) return;
+  const int H = Q.H, Di = Q.Di;
+  const float *q = (const float *)Q.q + (int64_t)r * H * Di;
+  for (int i = threadIdx.x; i < H * Di; i += blockDim.x) qsh[i] = q[i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) qsh[H * Di + i] = Q.w[(int64_t)r * H + i];
+  __syncthreads();
+  for (int e = lo + threadIdx.x; e < hi; e += blockDim.x) {
+    const float *k = (const float *)K.data + ((int64_t)b * K.stride + e) * Di;
+    float s = 0.f;
+    for (int h = 0; h < H; ++h) {
+      float d = 0.f;
+      for (int i = 0; i < Di; ++i) d = fmaf(qsh[h * Di + i], k[i], d);
+      s = fmaf(qsh[H * Di + h], fmaxf(d, 0.f), s);
+    }
+    scores[(int64_t)r * ld + e] = s * scale;
+  }
+}
+
+// -------------------------------------------------------------------- block radix select
+// Block of 256 threads.  keys[0..n) in LDS.  Finds the key value T of the
+// want-th largest element and how many elements equal to T must be taken
+// (the lowest-index ones).  Exact; deterministic.
+struct SelectResult {
+  uint32_t prefix, mask, take_eq;
+};
+
+__device__ SelectResult block_radix_select(const uint32_t *keys, int n, int want, uint32_t *hist,
+                                           uint32_t *sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t prefix = 0, mask = 0;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint32_t k = keys[i];
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      // lane owns bins 4*lane .. 4*lane+3; count of elements in higher bins
+      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
+      const uint32_t tot = c0 + c1 + c2 + c3;
+      uint32_t suf = tot;   // inclusive suffix sum over lanes >= lane
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += v;
+      }
+      uint32_t above = suf - tot;   // elements in bins of higher lanes
+      const uint32_t cs[4] = {c0, c1, c2, c3};
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (above < (uint32_t)want && (uint32_t)want <= above + cs[q]) {
+          sh[0] = prefix | ((uint32_t)(4 * lane + q) << shift);
+          sh[1] = (uint32_t)want - above;
+          sh[2] = cs[q];
+        }
+        above += cs[q];
+      }
+    }
+    __syncthreads();
+    prefix = sh[0];
+    want = (int)sh[1];
+    const uint32_t grp = sh[2];
+    mask |= 255u << shift;
+    __syncthreads();
+    if (grp == (uint32_t)want) break;   // the whole group is taken: no finer digit needed
+  }
+  return SelectResult{prefix, mask, (uint32_t)want};
+}
+
+// Block exclusive scan of one value per thread (256 threads).  Returns the
+// exclusive prefix; *total receives the block total.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh4, uint32_t *total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  if (lane == 63) sh4[wv] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < wv) base += sh4[i];
+    tot += sh4[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+// Select the top `kk` of keys[0..n) (kk <= n) and write, in ascending position
+// order, out_pos[j] = position and out_key[j] = key for j < kk.
+__device__ void block_topk_compact(const uint32_t *keys, int n, int kk, uint32_t *hist, uint32_t *sh,
+                                   int32_t *out_pos, uint32_t *out_key) {
+  const SelectResult sel = block_radix_select(keys, n, kk, hist, sh);
+  const int tid = threadIdx.x;
+  const int seg = (n + 255) / 256;
+  const int a = min(n, tid * seg), bnd = min(n, a + seg);
+  uint32_t gt = 0, eq = 0;
+  for (int i = a; i < bnd; ++i) {
+    const uint32_t k = keys[i] & sel.mask;
+    gt += k > sel.prefix;
+    eq += k == sel.prefix;
+  }
+  uint32_t tot;
+  const uint32_t eq_before = block_excl_scan(eq, sh + 4, &tot);
+  uint32_t eq_take = 0;
+  if (eq_before < sel.take_eq) eq_take = min(eq, sel.take_eq - eq_before);
+  const uint32_t off = block_excl_scan(gt + eq_take, sh + 8, &tot);
+  uint32_t o = off, eq_used = 0;
+  for (int i = a; i < bnd; ++i) {
+    const uint32_t kf = keys[i];
+    const uint32_t k = kf & sel.mask;
+    bool take = k > sel.prefix;
+    if (!take && k == sel.prefix && eq_used < eq_take) { take = true; ++eq_used; }
+    if (take) {
+      out_pos[o] = i;
+      if (out_key) out_key[o] = kf;
+      ++o;
+    }
+  }
+}
+
+// grid (T, n_chunks).  Chunk c covers entries [c*chunk, min(n, (c+1)*chunk)).
+// n_chunks == 1: writes the final idx/score rows.  Otherwise writes per-chunk
+// candidates (ascending entry order, key 0 in unused slots).
+__global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                    const int32_t *__restrict__ count, int m,
+                                                    const float *__restrict__ scores, int64_t ld, int chunk,
+                                                    int topk, int32_t *__restrict__ idx_out,
+                                                    float *__restrict__ score_out, uint32_t *__restrict__ cand_key,
+                                                    int32_t *__restrict__ cand_idx) {
+  extern __shared__ uint32_t smem[];
+  uint32_t *keys = smem;                       // [chunk]
+  int32_t *pos = (int32_t *)(smem + chunk);    // [topk]
+  uint32_t *kout = smem + chunk + topk;        // [topk]
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[16];
+  const int r = blockIdx.x, cidx = blockIdx.y, nch = gridDim.y;
+  const int n = n_visible(tok[r], m, count[seq[r]]);
+  const int lo = cidx * chunk;
+  const int len = max(0, min(n, lo + chunk) - lo);
+  const int kk = min(topk, len);
+  for (int i = threadIdx.x; i < len; i += 256) keys[i] = fkey(scores[(int64_t)r * ld + lo + i]);
+  __syncthreads();
+  if (kk > 0) block_topk_compact(keys, len, kk, hist, sh, pos, kout);
+  __syncthreads();
+  if (nch == 1) {
+    for (int j = threadIdx.x; j < topk; j += 256) {
+      idx_out[(int64_t)r * topk + j] = j < kk ? lo + pos[j] : -1;
+      if (score_out) score_out[(int64_t)r * topk + j] = j < kk ? keyf(kout[j]) : -INFINITY;
+    }
+  } else {
+    const int64_t base = ((int64_t)r * nch + cidx) * topk;
+    for (int j = threadIdx.x; j < topk; j += 256) {
+      cand_key[base + j] = j < kk ? kout[j] : 0u;
+      cand_idx[base + j] = j < kk ? lo + pos[j] : -1;
+    }
+  }
+}
+
+// grid (T).  Merges n_chunks*topk candidates (key 0 = empty) into the final row.
+__global__ __launch_bounds__(256) void k_topk_merge(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                    const int32_t *__restrict__ count, int m, int n_chunks,
+                                                    int topk, const uint32_t *__restrict__ cand_key,
+                                                    const int32_t *__restrict__ cand_idx,
+                                                    int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
+  extern __shared__ uint32_t smem[];
+  const int nc = n_chunks * topk;
+  uint32_t *keys = smem;                    // [nc]
+  int32_t *pos = (int32_t *)(smem + nc);    // [topk]
+  uint32_t *kout = smem + nc + topk;        // [topk]
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh[16];
+  const int r = blockIdx.x;
+  const int n = n_visible(tok[r], m, count[seq[r]]);
+  const int kk = min(topk, n);
+  const int64_t base = (int64_t)r * nc;
+  for (int i = threadIdx.x; i < nc; i += 256) keys[i] = cand_key[base + i];
+  __syncthreads();
+  if (kk > 0) block_topk_compact(keys, nc, kk, hist, sh, pos, kout);
+  __syncthreads();
+  for (int j = threadIdx.x; j < topk; j += 256) {
+    idx_out[(int64_t)r * topk + j] = j < kk ? cand_idx[base + pos[j]] : -1;
+    if (score_out) score_out[(int64_t)r * topk + j] = j < kk ? keyf(kout[j]) : -INFINITY;
+  }
+}
+
+}  // namespace dsv4
+
+using namespace dsv4;
+
+namespace dsv4host {
+
+// Chunking of the pool for scoring and top-k: the first-stage chunk holds at
+// most 16384 keys (64 KB of LDS); the merge stage holds n_chunks*topk keys.
+struct TopkPlan {
+  int chunk, n_chunks;
+  size_t scores_bytes, cand_bytes;
+};
+
+static TopkPlan plan_topk(int64_t n_rows, int64_t stride, int topk) {
+  TopkPlan p;
+  int64_t ch = 4096;
+  while (ch < 16384 && ((stride + ch - 1) / ch) * topk > 16384) ch *= 2;
+  if (stride <= ch) ch = stride > 0 ? stride : 1;
+  p.chunk = (int)ch;
+  p.n_chunks = (int)((stride + ch - 1) / ch);
+  if (p.n_chunks < 1) p.n_chunks = 1;
+  p.scores_bytes = (size_t)n_rows * (size_t)stride * 4;
+  p.scores_bytes = (p.scores_bytes + 255) & ~(size_t)255;
+  p.cand_bytes = p.n_chunks > 1 ? (size_t)n_rows * p.n_chunks * topk * 8 : 0;
+  return p;
+}
+
+size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk) {
+  const TopkPlan p = plan_topk(n_rows, stride, topk);
+  return p.scores_bytes + p.cand_bytes + 256;
+}
+
+int index_topk_supported(int64_t stride, int topk) {
+  const TopkPlan p = plan_topk(1, stride, topk);
+  return (int64_t)p.n_chunks * topk <= 16384 + 0 || p.n_chunks == 1;
+}
+
+int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qscale, int q_dtype, const float *w,
+                      int H, int Di, const dsv4_rows *kp, int m, int topk, float scale, int32_t *idx_out,
+                      float *score_out, void *ws, hipStream_t st) {
+  const int T = q->n_rows;
+  if (T == 0) return DSV4_OK;
+  const TopkPlan p = plan_topk(T, kp->seq_stride, topk);
+  float *scores = (float *)ws;
+  uint32_t *cand_key = (uint32_t *)((char *)ws + p.scores_bytes);
+  int32_t *cand_idx = (int32_t *)(cand_key + (size_t)T * p.n_chunks * topk);
+  IdxQ Q{q->seq, q->tok, qv, qscale, w, H, Di};
+  IdxK K{kp->data, kp->blk_scale, kp->count, kp->seq_stride, m};
+  const int64_t ld = kp->seq_stride;
+  // scoring chunk: 1024 entries per workgroup (16 blocks per wave)
+  const int sc_chunk = 1024;
+  const int sc_chunks = (int)((kp->seq_stride + sc_chunk - 1) / sc_chunk);
+  dim3 sgrid(T, sc_chunks > 0 ? sc_chunks : 1);
+  if (q_dtype == DSV4_F32) {
+    hipLaunchKernelGGL(k_index_scores_f32, sgrid, dim3(256), (size_t)(H * Di + H) * 4, st, Q, K, scale, sc_chunk,
+                       scores, ld);
+  } else if (q_dtype == DSV4_MXFP4) {
+    switch (H / 16) {
+    case 1: hipLaunchKernelGGL((k_index_scores_mfma<1, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
+    case 2: hipLaunchKernelGGL((k_index_scores_mfma<2, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
+    case 3: hipLaunchKernelGGL((k_index_scores_mfma<3, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
+    default: hipLaunchKernelGGL((k_index_scores_mfma<4, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
+    }
+  } else {
+#define DSV4_IS(NHB, KS) hipLaunchKernelGGL((k_index_scores_mfma<NHB, KS, false>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld)
+#define DSV4_IS_H(KS)                  \
+  switch (H / 16) {                    \
+  case 1: DSV4_IS(1, KS); break;       \
+  case 2: DSV4_IS(2, KS); break;       \
+  case 3: DSV4_IS(3, KS); break;       \
+  default: DSV4_IS(4, KS); break;      \
+  }
+    switch (Di / 32) {
+    case 1: DSV4_IS_H(1); break;
+    case 2: DSV4_IS_H(2); break;
+    case 3: DSV4_IS_H(3); break;
+    default: DSV4_IS_H(4); break;
+    }
+#undef DSV4_IS_H
+#undef DSV4_IS
+  }
+  int rc = check_launch("k_index_scores");
+  if (rc) return rc;
+  const size_t lds1 = ((size_t)p.chunk + 2 * (size_t)topk) * 4;
+  hipLaunchKernelGGL(k_topk_chunk, dim3(T, p.n_chunks), dim3(256), lds1, st, q->seq, q->tok, kp->count, m, scores, ld,
+                     p.chunk, topk, idx_out, score_out, cand_key, cand_idx);
+  rc = check_launch("k_topk_chunk");
+  if (rc || p.n_chunks == 1) return rc;
+  const size_t lds2 = ((size_t)p.n_chunks * topk + 2 * (size_t)topk) * 4;
+  hipLaunchKernelGGL(k_topk_merge, dim3(T), dim3(256), lds2, st, q->seq, q->tok, kp->count, m, p.n_chunks, topk,
+                     cand_key, cand_idx, idx_out, score_out);
+  return check_launch("k_topk_merge");
+}
+
+}  // namespace dsv4host

@@ -1,0 +1,192 @@
+/*
+ * dsv4.h -- C ABI of the MI355X (gfx950) DeepSeek-V4 hybrid-attention hot path:
+ * the KV compressor, the Lightning Indexer with top-k, Compressed Sparse
+ * Attention (CSA) and Heavily Compressed Attention (HCA).
+ *
+ * Sources: the Hugging Face Transformers DeepSeek-V4 model page ("Hybrid
+ * attention", "Attention mask layout", "Cache layers"); the jagaldol.com review
+ * of the V4 paper ("CSA", "HCA"); the insight.ai.kr write-up of the HF blog
+ * (pooling, indexer, storage precisions); the llm-atlas DeepSeek-V4-Flash card
+ * (config.json fields); the MarkTechPost summary (MXFP4 indexer path).
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major and
+ *     contiguous as described per argument.  The library allocates nothing,
+ *     keeps no pointer after the call returns (apart from work already queued)
+ *     and holds no global state beyond its code objects and a thread-local
+ *     error string.
+ *   - Every call validates its arguments on the host first; a call that returns
+ *     an error has launched nothing.  dsv4_last_error() describes the failure.
+ *   - Work is queued on `stream` (a hipStream_t; 0 = the null stream) with no
+ *     host synchronisation.  A kernel fault surfaces at the caller's next
+ *     synchronisation, or as DSV4_EHIP from a later call.
+ *   - Positions: token t of sequence b has absolute position pos0[b] + t.
+ *     pos0 may be NULL (all zero).
+ */
+#ifndef DSV4_H
+#define DSV4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define DSV4_OK 0
+#define DSV4_EINVAL (-1)     /* bad pointer, size or combination of arguments */
+#define DSV4_ENOTSUP (-2)    /* valid but unsupported shape / dtype combination */
+#define DSV4_EHIP (-3)       /* a HIP runtime call failed (launch error, earlier fault) */
+#define DSV4_EWORKSPACE (-4) /* workspace pointer NULL or smaller than required */
+
+/* ---- storage types ----
+ * DSV4_F32   : float32.
+ * DSV4_BF16  : bfloat16 (stored as 16-bit patterns).
+ * DSV4_FP8R  : a K=V row of `dim` channels stored as (dim - tail) OCP FP8 E4M3
+ *              bytes followed by `tail` bfloat16 values (the rope channels), plus
+ *              one float32 scale per row applied to the E4M3 part (the FP8 KV,
+ *              BF16 rope-dimension layout the insight.ai.kr write-up describes).
+ *              Row size (dim - tail) + 2*tail bytes (576 for 512/64).
+ * DSV4_MXFP4 : OCP MXFP4: E2M1 nibbles, low nibble = even element, dim/2 bytes
+ *              per row, with one E8M0 scale byte per 32-element block in a
+ *              separate plane (the MXFP4 indexer path of the MarkTechPost
+ *              summary). */
+#define DSV4_F32 0
+#define DSV4_BF16 1
+#define DSV4_FP8R 2
+#define DSV4_MXFP4 3
+
+/* Query rows of one call: row r belongs to sequence seq[r] and is token tok[r]
+ * (0-based) of that sequence.  Prefill: every token of every sequence; decode:
+ * one row per sequence with tok = L_b - 1.  All arrays are device memory. */
+typedef struct {
+  int32_t n_rows;       /* T >= 0 */
+  int32_t n_seq;        /* B >= 1 */
+  const int32_t *seq;   /* [T], values in [0, B) */
+  const int32_t *tok;   /* [T], values >= 0 */
+  const int64_t *pos0;  /* [B] or NULL */
+} dsv4_queries;
+
+/* Per-sequence stored rows: a compressed pool or a sliding window.
+ * Row i of sequence b lives at data + (b*seq_stride + i) * row_bytes(dtype).
+ * count[b] rows are valid.  For a window, row i holds token first_tok[b] + i;
+ * for a pool, first_tok is NULL and row s is compressed entry s. */
+typedef struct {
+  const void *data;
+  const float *row_scale;    /* DSV4_FP8R: [B*seq_stride]; else NULL */
+  const uint8_t *blk_scale;  /* DSV4_MXFP4: [B*seq_stride, dim/32]; else NULL */
+  int32_t dtype;
+  int32_t dim;
+  int32_t tail;              /* DSV4_FP8R: trailing bf16 channels; else 0 */
+  int64_t seq_stride;        /* rows reserved per sequence (>= every count[b]) */
+  const int32_t *count;      /* [B] */
+  const int32_t *first_tok;  /* [B] (windows) or NULL (pools) */
+} dsv4_rows;
+
+/* dsv4_compress -- softmax-gated pooling with a learned position bias.
+ * HF DeepSeek-V4 page, "Hybrid attention": CSA pools with overlapping windows
+ * (compress_rate_csa m = 4), HCA with non-overlapping windows (m' = 128);
+ * insight.ai.kr: softmax-gated pooling with a learned per-position bias.
+ * Entry s, per channel d: weights softmax_t(z[t,d] + pos_bias[j(t),d]) over its
+ * window, pooled[s,d] = sum_t weight * c[t,d].  overlap = 1: window
+ * [(s-1)m, (s+1)m) with j = t - (s-1)m; overlap = 0: window [s m, (s+1)m) with
+ * j = t - s m; tokens outside [0, seq_len) take no part.  Then, if rope_dim > 0,
+ * the last rope_dim channels are rotated (interleaved pairs, frequencies
+ * rope_theta^(-2i/rope_dim)) at position pos0[b] + s*m.
+ *   c, z     : [n_seq, seq_len, dim], in_dtype DSV4_F32 or DSV4_BF16
+ *   pos_bias : [2m or m, dim] float32
+ *   pool     : [n_seq, seq_len / m, dim], out_dtype DSV4_F32 or DSV4_BF16
+ * Partial trailing windows are not pooled.  dim even, <= 4096. */
+int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *pos_bias,
+                  int32_t n_seq, int32_t seq_len, int32_t dim, int32_t m, int32_t overlap,
+                  int32_t rope_dim, double rope_theta, const int64_t *pos0, void *pool,
+                  int32_t out_dtype, hipStream_t stream);
+
+/* dsv4_rope -- partial interleaved RoPE (HF page, "Hybrid attention", partial
+ * RoPE bullet): for i < rope_dim/2 the channel pair (dim-R+2i, dim-R+2i+1) of
+ * row r turns by angle sign * pos[r] * rope_theta^(-2i/R), sign = -1 when
+ * inverse != 0.  Other channels are copied.  x, y: [n_rows, dim] in dtype
+ * (DSV4_F32 or DSV4_BF16); y may equal x.  pos: [n_rows] int64 device. */
+int dsv4_rope(const void *x, void *y, int32_t dtype, int64_t n_rows, int32_t dim,
+              int32_t rope_dim, const int64_t *pos, double rope_theta, int32_t inverse,
+              hipStream_t stream);
+
+/* dsv4_index_topk -- Lightning Indexer scores and per-query top-k.
+ * HF page "Hybrid attention" (the indexer scores queries against the pool and
+ * keeps the top index_topk blocks) and "Attention mask layout" (-1 sentinel
+ * before the first window closes); insight.ai.kr (ReLU-scored multi-head dot
+ * products).  For query row r (sequence b, token t) and visible entry
+ * s < n = min(k_pool->count[b], (t+1)/m):
+ *     I(r,s) = score_scale * sum_h w[r,h] * max(0, q_idx[r,h,:] . k_pool[b,s,:])
+ * idx_out[r, 0..min(topk,n)) receives the indices of the min(topk, n) largest
+ * scores (equal scores: lower index first) in ascending index order; the rest
+ * of the row is -1.  Scores are accumulated in fp32.
+ *   q_idx       : [T, n_heads, head_dim] in q_dtype (DSV4_BF16, or DSV4_MXFP4 as
+ *                 [T, n_heads, head_dim/2] bytes with q_idx_scale
+ *                 [T, n_heads, head_dim/32] E8M0)
+ *   w           : [T, n_heads] float32
+ *   k_pool      : dtype equal to q_dtype, dim == head_dim
+ *   idx_out     : [T, topk] int32
+ *   score_out   : [T, topk] float32 scores of the picks (or -inf), may be NULL
+ *   ws          : scratch of at least dsv4_index_topk_workspace(...) bytes
+ * Supported: head_dim 128 (bf16: multiple of 32), n_heads multiple of 16 and
+ * <= 64, 1 <= topk <= 2048, m >= 1. */
+size_t dsv4_index_topk_workspace(int32_t n_rows, int64_t pool_seq_stride, int32_t topk);
+int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale,
+                    int32_t q_dtype, const float *w, int32_t n_heads, int32_t head_dim,
+                    const dsv4_rows *k_pool, int32_t m, int32_t topk, float score_scale,
+                    int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* dsv4_sparse_attn -- CSA core attention (HF page, "Hybrid attention" backbone
+ * bullets and "Attention mask layout", CSA paragraph).  One shared K=V head:
+ * for query row r (sequence b, token t, position p = pos0[b] + t) and head h,
+ * the key/value rows are the window rows holding tokens [t-W+1, t] and the pool
+ * entries idx[r, 0..topk) that are not -1.  With q~ = RoPE(q[r,h], p):
+ *     l_x = sm_scale * (q~ . x),  M = max(sinks[h], max_x l_x)
+ *     o   = sum_x e^(l_x - M) x / (e^(sinks[h] - M) + sum_x e^(l_x - M))
+ * and the last rope_dim channels of o are rotated back by -p.  Window and pool
+ * rows are read as stored (already rotated).
+ *   q      : [T, n_heads, dim] in q_dtype (DSV4_BF16 or DSV4_F32)
+ *   window : W > 0 -> rows holding tokens (DSV4_BF16 / DSV4_F32 / DSV4_FP8R);
+ *            W = 0 -> no window branch (window may be NULL)
+ *   pool   : same dtype family as window, dim equal; may be NULL when topk = 0
+ *   idx    : [T, topk] int32 in [-1, pool->count[b]); topk = 0: no pool branch
+ *   sinks  : [n_heads] float32 or NULL (no sink)
+ *   out    : [T, n_heads, dim] in out_dtype (DSV4_BF16 or DSV4_F32)
+ *   ws     : scratch of at least dsv4_attn_workspace(...) bytes (may be 0 bytes)
+ * A query with no rows and no sink gets a zero output.
+ * Supported: dim 512 or 64, n_heads multiple of 16 and <= 64, rope_dim even
+ * and <= 64, topk <= 2048. */
+size_t dsv4_attn_workspace(int32_t n_rows, int32_t n_heads, int32_t dim, int64_t max_rows_per_query);
+int dsv4_sparse_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_t n_heads,
+                     int32_t dim, const dsv4_rows *window, int32_t W, const dsv4_rows *pool,
+                     const int32_t *idx, int32_t topk, const float *sinks, float sm_scale,
+                     int32_t rope_dim, double rope_theta, void *out, int32_t out_dtype,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* dsv4_hca_attn -- HCA core attention (HF page "Hybrid attention", HCA bullet:
+ * no indexer, every pooled entry contributes; "Attention mask layout", HCA
+ * paragraph: entry w is visible to token t iff w < (t+1)/m).  As
+ * dsv4_sparse_attn with the pool rows s < min(pool->count[b], (t+1)/m) in place
+ * of the idx set. */
+int dsv4_hca_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_t n_heads,
+                  int32_t dim, const dsv4_rows *window, int32_t W, const dsv4_rows *pool,
+                  int32_t m, const float *sinks, float sm_scale, int32_t rope_dim,
+                  double rope_theta, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* Thread-local description of the last error (empty string after success). */
+const char *dsv4_last_error(void);
+
+/* Library version string. */
+const char *dsv4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV4_H */

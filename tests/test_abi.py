@@ -1,0 +1,135 @@
+"""The C ABI library: it loads, exports every entry point the header declares,
+and rejects bad arguments on the host before anything is launched.  No kernel
+runs here (CPU-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsv4.h")
+
+
+@pytest.fixture(scope="module")
+def K():
+    import torch  # noqa: F401  (one HIP runtime for torch and the library)
+    import compressed_sparse_kv_csa_amd as K
+    if not os.path.exists(K.LIB_PATH):
+        from compressed_sparse_kv_csa_amd import build
+        build.build()
+    K.lib()
+    return K
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsv4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(K):
+    names = declared_symbols()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(K.lib(), n), n
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_version_and_empty_error(K):
+    assert K.dsv4_version().startswith("dsv4")
+
+
+def _rc(v):
+    return ctypes.c_int(v).value
+
+
+def test_compress_rejects_bad_args(K):
+    L = K.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert _rc(L.dsv4_compress(None, fake, 1, fake, 1, 8, 8, 4, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_EINVAL
+    assert "NULL" in K.dsv4_last_error()
+    assert _rc(L.dsv4_compress(fake, fake, 1, fake, 1, 8, 7, 4, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_compress(fake, fake, 1, fake, 1, 8, 8, 0, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_compress(fake, fake, 7, fake, 1, 8, 8, 4, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_compress(fake, fake, 1, fake, 1, 8, 8, 4, 1, 3, 1e4, None, fake, 1, None)) == K.DSV4_EINVAL
+
+
+def test_rope_rejects_bad_args(K):
+    L = K.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert _rc(L.dsv4_rope(fake, fake, 1, 4, 8, 16, fake, 1e4, 0, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_rope(fake, fake, 2, 4, 8, 4, fake, 1e4, 0, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_rope(fake, fake, 1, 4, 8, 4, fake, 0.0, 0, None)) == K.DSV4_EINVAL
+
+
+def _queries(K, n=4):
+    fake = ctypes.c_void_p(0x1000)
+    return K.Queries(n, 1, fake.value, fake.value, None)
+
+
+def _rows(K, dtype, dim, **kw):
+    fake = 0x1000
+    r = K.Rows(fake, None, None, dtype, dim, 0, 16, fake, None)
+    for k, v in kw.items():
+        setattr(r, k, v)
+    return r
+
+
+def test_index_topk_rejects_bad_args(K):
+    L = K.lib()
+    fake = ctypes.c_void_p(0x1000)
+    q = _queries(K)
+    kp = _rows(K, K.DSV4_BF16, 128)
+    ws_need = L.dsv4_index_topk_workspace(4, 16, 8)
+    assert ws_need > 0
+    args = lambda **o: [ctypes.byref(o.get("q", q)), fake, None, o.get("qdt", K.DSV4_BF16), fake, o.get("H", 64),
+                        o.get("Di", 128), ctypes.byref(o.get("kp", kp)), 4, o.get("k", 8), o.get("sc", 0.1), fake,
+                        None, o.get("ws", fake), o.get("wsb", ws_need), None]
+    assert _rc(L.dsv4_index_topk(*args(k=0))) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_index_topk(*args(k=4096))) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_index_topk(*args(H=8))) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_index_topk(*args(Di=100, kp=_rows(K, K.DSV4_BF16, 100)))) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_index_topk(*args(kp=_rows(K, K.DSV4_F32, 128)))) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_index_topk(*args(sc=-1.0))) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_index_topk(*args(ws=None))) == K.DSV4_EWORKSPACE
+    assert _rc(L.dsv4_index_topk(*args(wsb=ws_need - 1))) == K.DSV4_EWORKSPACE
+    assert _rc(L.dsv4_index_topk(*args(qdt=K.DSV4_MXFP4, kp=_rows(K, K.DSV4_MXFP4, 128)))) == K.DSV4_EINVAL
+    bad_q = K.Queries(4, 0, fake.value, fake.value, None)
+    assert _rc(L.dsv4_index_topk(*args(q=bad_q))) == K.DSV4_EINVAL
+    huge = _rows(K, K.DSV4_BF16, 128, seq_stride=1 << 22)
+    assert _rc(L.dsv4_index_topk(*args(kp=huge, k=2048, ws=fake, wsb=1 << 62))) == K.DSV4_ENOTSUP
+
+
+def test_attention_rejects_bad_args(K):
+    L = K.lib()
+    fake = ctypes.c_void_p(0x1000)
+    q = _queries(K)
+    win = _rows(K, K.DSV4_BF16, 512, first_tok=0x1000)
+    pool = _rows(K, K.DSV4_BF16, 512)
+    base = dict(qdt=K.DSV4_BF16, H=64, D=512, W=128, k=16, win=win, pool=pool, R=64, odt=K.DSV4_BF16)
+
+    def call(**o):
+        a = dict(base, **o)
+        return _rc(L.dsv4_sparse_attn(ctypes.byref(q), fake, a["qdt"], a["H"], a["D"], ctypes.byref(a["win"]),
+                                      a["W"], ctypes.byref(a["pool"]), fake, a["k"], None, 0.04, a["R"], 1.6e5,
+                                      fake, a["odt"], fake, 1 << 40, None))
+    assert call(D=256, win=_rows(K, K.DSV4_BF16, 256, first_tok=0x1000), pool=_rows(K, K.DSV4_BF16, 256)) == K.DSV4_ENOTSUP
+    assert call(D=256) == K.DSV4_EINVAL                              # rows of another dim
+    assert call(H=8) == K.DSV4_ENOTSUP
+    assert call(k=4096) == K.DSV4_EINVAL
+    assert call(R=65) == K.DSV4_EINVAL
+    assert call(odt=3) == K.DSV4_ENOTSUP
+    assert call(win=_rows(K, K.DSV4_BF16, 512)) == K.DSV4_EINVAL     # window without first_tok
+    assert call(pool=_rows(K, K.DSV4_FP8R, 512, tail=64)) == K.DSV4_EINVAL   # FP8R without row_scale
+    assert call(qdt=K.DSV4_F32) == K.DSV4_ENOTSUP                    # fp32 queries, bf16 rows
+    assert _rc(L.dsv4_hca_attn(ctypes.byref(q), fake, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
+                               ctypes.byref(pool), 0, None, 0.04, 64, 1.6e5, fake, K.DSV4_BF16, fake, 1 << 40,
+                               None)) == K.DSV4_EINVAL
+
+
+def test_workspace_sizes(K):
+    L = K.lib()
+    assert L.dsv4_attn_workspace(8192, 64, 512, 640) == 0          # prefill: no split partials
+    assert L.dsv4_attn_workspace(8, 64, 512, 8320) > 8 * 64 * 512 * 4
+    assert L.dsv4_index_topk_workspace(8, 262144, 1024) >= 8 * 262144 * 4
