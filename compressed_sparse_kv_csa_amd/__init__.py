@@ -178,14 +178,16 @@ def dsv4_rope(x: torch.Tensor, pos: torch.Tensor, rope_dim: int, rope_theta: flo
 
 def dsv4_index_topk(q: QueryRows, q_idx: torch.Tensor, w: torch.Tensor, k_pool: RowStore, m: int, topk: int,
                     score_scale: float, q_idx_scale: Optional[torch.Tensor] = None, q_dtype: Optional[int] = None,
-                    want_scores: bool = False, ws: Optional[torch.Tensor] = None):
+                    want_scores: bool = False, ws: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None):
     """Lightning Indexer + top-k.  Returns idx [T, topk] int32 (and scores)."""
     T = q.seq.numel()
     H = w.shape[-1]
     if q_dtype is None:
         q_dtype = DSV4_MXFP4 if q_idx.dtype == torch.uint8 else _code(q_idx)
     Di = k_pool.dim
-    idx = torch.empty(T, topk, dtype=torch.int32, device=w.device)
+    idx = out if out is not None else torch.empty(T, topk, dtype=torch.int32, device=w.device)
+    assert idx.dtype == torch.int32 and idx.shape == (T, topk)
     sc = torch.empty(T, topk, dtype=torch.float32, device=w.device) if want_scores else None
     need = lib().dsv4_index_topk_workspace(T, k_pool.stride, topk)
     if ws is None or ws.numel() < need:
@@ -195,6 +197,18 @@ def dsv4_index_topk(q: QueryRows, q_idx: torch.Tensor, w: torch.Tensor, k_pool: 
                                  ctypes.byref(kc), m, topk, float(score_scale), _ptr(idx), _ptr(sc), _ptr(ws),
                                  ws.numel(), _stream()))
     return (idx, sc) if want_scores else idx
+
+
+def index_topk_workspace(n_rows: int, pool_stride: int, topk: int, device="cuda") -> torch.Tensor:
+    """A workspace tensor large enough for dsv4_index_topk."""
+    return torch.empty(max(1, lib().dsv4_index_topk_workspace(n_rows, pool_stride, topk)), dtype=torch.uint8,
+                       device=device)
+
+
+def attn_workspace(n_rows: int, n_heads: int, dim: int, max_rows: int, device="cuda") -> Optional[torch.Tensor]:
+    """A workspace tensor for dsv4_sparse_attn / dsv4_hca_attn (None if none is needed)."""
+    need = lib().dsv4_attn_workspace(n_rows, n_heads, dim, max_rows)
+    return torch.empty(need, dtype=torch.uint8, device=device) if need else None
 
 
 def _attn_ws(T, H, D, max_rows, device, ws):

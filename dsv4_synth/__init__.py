@@ -399,3 +399,67 @@ def decode_layer(seed: int, kind: str, B: int, L, H: int = 64, D: int = 512, R: 
             layer.q_idx = bf16_to_f32(bf16_bits(qi))
         layer.kpool = rowset_from_values(keys, idx_kind, count=N)
     return layer
+
+
+# --------------------------------------------------------------------------- device-side drawing
+# Full-size benchmark inputs (GiBs) are drawn on the device with torch's
+# counter-based generator, seeded per tensor name, and packed there with the
+# same storage recipes as above (torch ports of fp8r_pack / mxfp4_pack, checked
+# equal to the numpy packers on the CPU).  Samples the oracle needs are copied
+# back to the host from these tensors.
+def _name_seed(seed: int, name: str) -> int:
+    h = 1469598103934665603
+    for ch in f"{seed}:{name}".encode():
+        h = ((h ^ ch) * 1099511628211) & 0xFFFFFFFFFFFFFFFF
+    return h & 0x7FFFFFFFFFFFFFFF
+
+
+def draw_torch(seed: int, name: str, shape, std: float = 1.0, dtype=None, device="cuda"):
+    """N(0, std^2) of `shape` from torch's generator on `device` (dtype float32
+    unless given; bf16 rounds to nearest even as torch's cast does)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(_name_seed(seed, name))
+    x = torch.randn(tuple(int(s) for s in shape), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x if dtype is None else x.to(dtype)
+
+
+def fp8r_pack_torch(x, tail: int):
+    """torch version of fp8r_pack: x [..., dim] float32 -> (rows uint8 [..., (dim-tail)+2*tail],
+    scales float32 [...])."""
+    import torch
+    dim = x.shape[-1]
+    head = x[..., : dim - tail]
+    amax = head.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+    codes = (head / s[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    rope = x[..., dim - tail:].to(torch.bfloat16).contiguous().view(torch.uint8)
+    return torch.cat([codes, rope], dim=-1).contiguous(), s.contiguous()
+
+
+def mxfp4_pack_torch(x):
+    """torch version of mxfp4_pack (same scale recipe, same rounding)."""
+    import torch
+    dim = x.shape[-1]
+    lead = x.shape[:-1]
+    blk = x.reshape(-1, dim // 32, 32).to(torch.float32)
+    amax = blk.abs().amax(dim=-1)
+    safe = torch.where(amax > 0, amax, torch.ones_like(amax))
+    e = torch.where(amax > 0, torch.floor(torch.log2(safe)) - 2, torch.full_like(amax, -127.0)).clamp(-127, 127)
+    v = blk / torch.exp2(e)[..., None]
+    a = v.abs().clamp(max=6.0)
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=x.device)
+    d = (a[..., None] - grid).abs()
+    best = d.argmin(dim=-1)
+    dmin = d.gather(-1, best[..., None])[..., 0]
+    nxt = (best + 1).clamp(max=7)
+    dn = d.gather(-1, nxt[..., None])[..., 0]
+    tie = (dn == dmin) & (nxt != best) & (best % 2 == 1)
+    code = torch.where(tie, nxt, best).to(torch.uint8)
+    code = code | ((torch.signbit(v) & (code != 0)).to(torch.uint8) << 3)
+    code = code.reshape(*lead, dim)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).contiguous()
+    scales = (e + 127).to(torch.uint8).reshape(*lead, dim // 32).contiguous()
+    return packed, scales
