@@ -93,15 +93,16 @@ class CsaPrefill:
         self.pos = torch.arange(S, dtype=torch.int64, device=dev)
         self.Q = K.QueryRows.prefill(1, S, self.pos0)
         N = S // m
-        self.pool = torch.empty(1, N, D, dtype=bf, device=dev)
+        f16 = torch.float16   # K=V rows feed the fp16 matrix-core path straight from HBM
+        self.pool = torch.empty(1, N, D, dtype=f16, device=dev)
         self.kpool = torch.empty(1, N, Di, dtype=bf, device=dev)
-        self.kv_rot = torch.empty(1, S, D, dtype=bf, device=dev)
+        self.kv_rot = torch.empty(1, S, D, dtype=f16, device=dev)
         self.idx = torch.empty(S, k, dtype=torch.int32, device=dev)
         self.out = torch.empty(S, H, D, dtype=bf, device=dev)
         cnt = torch.full((1,), N, dtype=torch.int32, device=dev)
-        self.win_rows = K.RowStore(self.kv_rot, K.DSV4_BF16, D, torch.full((1,), S, dtype=torch.int32, device=dev),
+        self.win_rows = K.RowStore(self.kv_rot, K.DSV4_F16, D, torch.full((1,), S, dtype=torch.int32, device=dev),
                                    first_tok=torch.zeros(1, dtype=torch.int32, device=dev))
-        self.pool_rows = K.RowStore(self.pool, K.DSV4_BF16, D, cnt)
+        self.pool_rows = K.RowStore(self.pool, K.DSV4_F16, D, cnt)
         self.kpool_rows = K.RowStore(self.kpool, K.DSV4_BF16, Di, cnt)
         self.ws_idx = K.index_topk_workspace(S, N, k, dev)
         self.ws_attn = K.attn_workspace(S, H, D, W + k, dev)
@@ -148,12 +149,13 @@ class HcaPrefill:
         self.pos = torch.arange(S, dtype=torch.int64, device=dev)
         self.Q = K.QueryRows.prefill(1, S, self.pos0)
         N = S // m
-        self.pool = torch.empty(1, N, D, dtype=bf, device=dev)
-        self.kv_rot = torch.empty(1, S, D, dtype=bf, device=dev)
+        f16 = torch.float16
+        self.pool = torch.empty(1, N, D, dtype=f16, device=dev)
+        self.kv_rot = torch.empty(1, S, D, dtype=f16, device=dev)
         self.out = torch.empty(S, H, D, dtype=bf, device=dev)
-        self.win_rows = K.RowStore(self.kv_rot, K.DSV4_BF16, D, torch.full((1,), S, dtype=torch.int32, device=dev),
+        self.win_rows = K.RowStore(self.kv_rot, K.DSV4_F16, D, torch.full((1,), S, dtype=torch.int32, device=dev),
                                    first_tok=torch.zeros(1, dtype=torch.int32, device=dev))
-        self.pool_rows = K.RowStore(self.pool, K.DSV4_BF16, D, torch.full((1,), N, dtype=torch.int32, device=dev))
+        self.pool_rows = K.RowStore(self.pool, K.DSV4_F16, D, torch.full((1,), N, dtype=torch.int32, device=dev))
         self.ws_attn = K.attn_workspace(S, H, D, W + N, dev)
         self.counts = hca_prefill_counts(S, m, W, H, D)
 
@@ -422,7 +424,7 @@ def main():
         rec["unit"] = "tokens/s"
         flop = wl.counts["attn_flop"]
         ach = flop / (kern_ms / 1e3) / 1e12
-        rec["roofline"] = {"bound": "mfma", "kernel": "k_attn_mfma (fp16 MFMA, fp32 accumulate)",
+        rec["roofline"] = {"bound": "mfma", "kernel": "k_attn_f16 (fp16 MFMA, fp32 accumulate)",
                            "achieved": round(ach, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                            "frac": round(ach / PEAK_MFMA_F16, 4), "traffic": None,
                            "algorithmic": f"{flop / 1e9:.1f} GFLOP per launch ({wl.counts['attn_pairs']} query-row "

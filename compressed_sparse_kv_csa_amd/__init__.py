@@ -18,7 +18,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdsv4.so")
 
-DSV4_F32, DSV4_BF16, DSV4_FP8R, DSV4_MXFP4 = 0, 1, 2, 3
+DSV4_F32, DSV4_BF16, DSV4_FP8R, DSV4_MXFP4, DSV4_F16 = 0, 1, 2, 3, 4
 DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, -4
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
@@ -57,7 +57,7 @@ def lib():
         P, I32, I64, F, D, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                  ctypes.c_double, ctypes.c_size_t)
         L.dsv4_compress.argtypes = [P, P, I32, P, I32, I32, I32, I32, I32, I32, D, P, P, I32, P]
-        L.dsv4_rope.argtypes = [P, P, I32, I64, I32, I32, P, D, I32, P]
+        L.dsv4_rope.argtypes = [P, I32, P, I32, I64, I32, I32, P, D, I32, P]
         L.dsv4_index_topk_workspace.argtypes = [I32, I64, I32]
         L.dsv4_index_topk_workspace.restype = SZ
         L.dsv4_index_topk.argtypes = [P, P, P, I32, P, I32, I32, P, I32, I32, F, P, P, P, SZ, P]
@@ -93,10 +93,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _code(t: torch.Tensor, allow=(torch.float32, torch.bfloat16)) -> int:
-    if t.dtype not in allow:
+_CODES = {torch.float32: DSV4_F32, torch.bfloat16: DSV4_BF16, torch.float16: DSV4_F16}
+
+
+def _code(t: torch.Tensor) -> int:
+    if t.dtype not in _CODES:
         raise TypeError(f"unsupported dtype {t.dtype}")
-    return DSV4_F32 if t.dtype == torch.float32 else DSV4_BF16
+    return _CODES[t.dtype]
 
 
 # ------------------------------------------------------------------ descriptors
@@ -164,15 +167,15 @@ def dsv4_compress(c: torch.Tensor, z: torch.Tensor, pos_bias: torch.Tensor, m: i
 
 
 def dsv4_rope(x: torch.Tensor, pos: torch.Tensor, rope_dim: int, rope_theta: float, inverse: bool = False,
-              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+              out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Partial interleaved RoPE of the last rope_dim channels; x [..., dim], pos [rows] int64."""
     dim = x.shape[-1]
     n = x.numel() // dim
     if out is None:
-        out = torch.empty_like(x)
-    assert pos.dtype == torch.int64 and pos.numel() == n
-    _check(lib().dsv4_rope(_ptr(x), _ptr(out), _code(x), n, dim, rope_dim, _ptr(pos), float(rope_theta),
-                           int(bool(inverse)), _stream()))
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    assert pos.dtype == torch.int64 and pos.numel() == n and out.numel() == x.numel()
+    _check(lib().dsv4_rope(_ptr(x), _code(x), _ptr(out), _code(out), n, dim, rope_dim, _ptr(pos),
+                           float(rope_theta), int(bool(inverse)), _stream()))
     return out
 
 

@@ -31,8 +31,8 @@ int check_launch(const char *what) {
 int launch_compress(const void *c, const void *z, int in_dtype, const float *bias, int B, int S, int dim, int m,
                     int overlap, int rope_dim, double theta, const int64_t *pos0, void *pool, int out_dtype,
                     hipStream_t st);
-int launch_rope(const void *x, void *y, int dtype, int64_t n_rows, int dim, int rope_dim, const int64_t *pos,
-                double theta, int inverse, hipStream_t st);
+int launch_rope(const void *x, int x_dtype, void *y, int y_dtype, int64_t n_rows, int dim, int rope_dim,
+                const int64_t *pos, double theta, int inverse, hipStream_t st);
 size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk);
 int index_topk_supported(int64_t stride, int topk);
 int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qscale, int q_dtype, const float *w,
@@ -68,7 +68,7 @@ static int check_rows(const dsv4_rows *r, const char *what, int dim) {
       return fail(DSV4_ENOTSUP, "%s: FP8R tail %d (multiple of 8 within dim required)", what, r->tail);
   } else if (r->dtype == DSV4_MXFP4) {
     if (!r->blk_scale && r->seq_stride > 0) return fail(DSV4_EINVAL, "%s: MXFP4 rows need blk_scale", what);
-  } else if (r->dtype != DSV4_F32 && r->dtype != DSV4_BF16) {
+  } else if (r->dtype != DSV4_F32 && r->dtype != DSV4_BF16 && r->dtype != DSV4_F16) {
     return fail(DSV4_EINVAL, "%s: unknown dtype %d", what, r->dtype);
   }
   return DSV4_OK;
@@ -93,24 +93,28 @@ int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *p
   if (dim < 2 || (dim & 1) || dim > 4096) return fail(DSV4_ENOTSUP, "compress: dim %d (even, 2..4096)", dim);
   if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
     return fail(DSV4_EINVAL, "compress: rope_dim %d (even, <= min(dim, 64))", rope_dim);
-  if ((in_dtype != DSV4_F32 && in_dtype != DSV4_BF16) || (out_dtype != DSV4_F32 && out_dtype != DSV4_BF16))
-    return fail(DSV4_ENOTSUP, "compress: dtypes in %d out %d (F32/BF16 only)", in_dtype, out_dtype);
+  if ((in_dtype != DSV4_F32 && in_dtype != DSV4_BF16) ||
+      (out_dtype != DSV4_F32 && out_dtype != DSV4_BF16 && out_dtype != DSV4_F16))
+    return fail(DSV4_ENOTSUP, "compress: dtypes in %d (F32/BF16) out %d (F32/BF16/F16)", in_dtype, out_dtype);
   if (rope_dim > 0 && !(rope_theta > 0)) return fail(DSV4_EINVAL, "compress: rope_theta must be > 0");
   const int rc = launch_compress(c, z, in_dtype, pos_bias, n_seq, seq_len, dim, m, overlap ? 1 : 0, rope_dim,
                                  rope_theta, pos0, pool, out_dtype, stream);
   return rc ? rc : ok();
 }
 
-int dsv4_rope(const void *x, void *y, int32_t dtype, int64_t n_rows, int32_t dim, int32_t rope_dim,
-              const int64_t *pos, double rope_theta, int32_t inverse, hipStream_t stream) {
+int dsv4_rope(const void *x, int32_t x_dtype, void *y, int32_t y_dtype, int64_t n_rows, int32_t dim,
+              int32_t rope_dim, const int64_t *pos, double rope_theta, int32_t inverse, hipStream_t stream) {
   if (!x || !y || (!pos && n_rows > 0)) return fail(DSV4_EINVAL, "rope: NULL pointer");
   if (n_rows < 0) return fail(DSV4_EINVAL, "rope: n_rows %lld", (long long)n_rows);
   if (dim < 2 || (dim & 1) || dim > 4096) return fail(DSV4_ENOTSUP, "rope: dim %d (even, 2..4096)", dim);
   if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
     return fail(DSV4_EINVAL, "rope: rope_dim %d (even, <= min(dim, 64))", rope_dim);
-  if (dtype != DSV4_F32 && dtype != DSV4_BF16) return fail(DSV4_ENOTSUP, "rope: dtype %d (F32/BF16 only)", dtype);
+  if ((x_dtype != DSV4_F32 && x_dtype != DSV4_BF16) ||
+      (y_dtype != DSV4_F32 && y_dtype != DSV4_BF16 && y_dtype != DSV4_F16))
+    return fail(DSV4_ENOTSUP, "rope: dtypes x %d (F32/BF16) y %d (F32/BF16/F16)", x_dtype, y_dtype);
+  if (x == y && x_dtype != y_dtype) return fail(DSV4_EINVAL, "rope: in-place needs equal dtypes");
   if (rope_dim > 0 && !(rope_theta > 0)) return fail(DSV4_EINVAL, "rope: rope_theta must be > 0");
-  const int rc = launch_rope(x, y, dtype, n_rows, dim, rope_dim, pos, rope_theta, inverse, stream);
+  const int rc = launch_rope(x, x_dtype, y, y_dtype, n_rows, dim, rope_dim, pos, rope_theta, inverse, stream);
   return rc ? rc : ok();
 }
 
@@ -186,10 +190,11 @@ static int attn_common(const char *who, const dsv4_queries *q, const void *qv, i
     if (dim != 512) return fail(DSV4_ENOTSUP, "%s: bf16 path needs dim 512 (got %d)", who, dim);
     if (n_heads < 16 || n_heads > 64 || n_heads % 16)
       return fail(DSV4_ENOTSUP, "%s: bf16 path needs n_heads in {16,32,48,64} (got %d)", who, n_heads);
-    const bool ok_w = W == 0 || wdt == DSV4_BF16 || wdt == DSV4_FP8R;
-    const bool ok_p = !pool_needed || pdt == DSV4_BF16 || pdt == DSV4_FP8R;
-    if (!ok_w || !ok_p) return fail(DSV4_ENOTSUP, "%s: bf16 queries need BF16 or FP8R rows", who);
+    const bool ok_w = W == 0 || wdt == DSV4_BF16 || wdt == DSV4_FP8R || wdt == DSV4_F16;
+    const bool ok_p = !pool_needed || pdt == DSV4_BF16 || pdt == DSV4_FP8R || pdt == DSV4_F16;
+    if (!ok_w || !ok_p) return fail(DSV4_ENOTSUP, "%s: bf16 queries need F16, BF16 or FP8R rows", who);
     if (W > 0 && pool_needed && wdt != pdt) return fail(DSV4_ENOTSUP, "%s: window and pool dtypes differ", who);
+    if ((W == 0 && !pool_needed) && false) return DSV4_OK;
   } else {
     return fail(DSV4_ENOTSUP, "%s: query dtype %d", who, q_dtype);
   }

@@ -372,6 +372,281 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- fp16 rows, DMA-staged
+// k_attn_f16<NHB, NW>: the prefill fast path for fp16 K=V rows (the compressor
+// and the rope kernel emit fp16 for it).  NW waves, each owning 16*NHB heads
+// (64 heads: 4 waves x 16 heads; the accumulators of 16 heads x 512 dims stay
+// in VGPRs, which allows two workgroups per CU).  Rows are gathered straight from global memory into LDS with
+// global_load_lds_dwordx4 (one 1 KB row per wave instruction, no VGPR
+// staging), double-buffered: the gather of tile i+1 is in flight while tile i
+// is on the matrix cores.  The PV operand V^T comes from the same row-major
+// tile through ds_read_b64_tr_b16 (a 16x4 transpose inside each 16-lane
+// group), so no transposed copy is written.
+//
+// Softmax without rescaling: the probabilities of a head are taken against a
+// fixed reference m_ref (the head's max over the first tile), so the output
+// accumulators are touched by nothing but MFMAs and stay in AGPRs.  A later
+// logit above m_ref + 15 (fp16 P would pass 2^15) makes the whole workgroup
+// start over with m_ref raised to the largest logit seen; each restart raises
+// m_ref by more than 15, so restarts are rare and finite.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr float kRefSlack = 15.f;   // log2 units: P <= 2^15 stays finite in fp16
+
+template <int NHB, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
+  constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t T0[32 * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t T1[32 * KP];
+  __shared__ int sel[kMaxSel];
+  __shared__ float rc[32], rs[32];
+  __shared__ int sh_wave[NW];
+  __shared__ int rflag[2];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int r = (A.T - 1) - (int)(blockIdx.x / A.nsplit);
+  const int split = blockIdx.x % A.nsplit;
+  RowPlan P = row_plan(A, r);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_wave);
+  const int nrows = P.nwin + P.nsel;
+  const int ntiles = (nrows + 31) / 32;
+  const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
+  const int tile_lo = split * tps;
+  const int tile_hi = min(ntiles, tile_lo + tps);
+  const int R = A.rope_dim;
+  const int nwin = P.nwin, csa = A.csa;
+  // row addressing in scalars: window rows first, then pool rows
+  const uint8_t *wbase = A.win.data ? A.win.data + ((int64_t)P.b * A.win.stride + P.wlo) * 1024 : nullptr;
+  const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * 1024 : nullptr;
+
+  // zero both tiles once: rows past the end of the list are never gathered and
+  // must hold finite values (their probabilities are zero)
+  for (int i = tid; i < 32 * KP / 8; i += NT) {
+    reinterpret_cast<u32x4 *>(T0)[i] = u32x4{0u, 0u, 0u, 0u};
+    reinterpret_cast<u32x4 *>(T1)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid < R / 2) rope_cs((double)P.p, tid, R, A.theta, 1.f, &rc[tid], &rs[tid]);
+  if (tid < 2) rflag[tid] = 0;
+  __syncthreads();
+
+  // gather rows [32 tile, 32 tile + 32) of the list into T (wave w: rows w, w+NW, ...)
+  auto gather = [&](int tile, uint16_t *T) {
+    for (int rr = wv; rr < 32; rr += NW) {
+      const int i = 32 * tile + rr;
+      if (i < nrows) {
+        const uint8_t *rp;
+        if (i < nwin) rp = wbase + (int64_t)i * 1024;
+        else rp = pbase + (int64_t)(csa ? sel[i - nwin] : i - nwin) * 1024;
+        __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + rr * KP), 16, 0, 0);
+      }
+    }
+  };
+
+  // q~ = RoPE(q) * sm_scale * log2(e) in fp16, B operand: head h0 + 16hb + c, dims 32j + 8g .. +8
+  const int h0 = wv * 16 * NHB;
+  f16x8 qb[NHB][NJ];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + h0 + 16 * hb + c) * D;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int d0 = 32 * j + 8 * g;
+      const u32x4 raw = *reinterpret_cast<const u32x4 *>(qr + d0);
+      float x[8];
+      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_to_f32((uint16_t)(wds[k] & 0xFFFF));
+        x[2 * k + 1] = bf16_to_f32((uint16_t)(wds[k] >> 16));
+      }
+      if (d0 >= D - R) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pi = (d0 + 2 * k - (D - R)) >> 1;
+          const float cs = rc[pi], sn = rs[pi];
+          const float a = x[2 * k] * cs - x[2 * k + 1] * sn, bb = x[2 * k] * sn + x[2 * k + 1] * cs;
+          x[2 * k] = a;
+          x[2 * k + 1] = bb;
+        }
+      }
+      const u32x4 o = u32x4{pack_f16x2(x[0] * A.scale_log2, x[1] * A.scale_log2),
+                            pack_f16x2(x[2] * A.scale_log2, x[3] * A.scale_log2),
+                            pack_f16x2(x[4] * A.scale_log2, x[5] * A.scale_log2),
+                            pack_f16x2(x[6] * A.scale_log2, x[7] * A.scale_log2)};
+      __builtin_memcpy(&qb[hb][j], &o, 16);
+    }
+  }
+
+  f32x4 acc_o[NHB][NDB];
+  float m_ref[NHB], m_seen[NHB], l_run[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) { m_ref[hb] = -INFINITY; m_seen[hb] = -INFINITY; }
+
+  // one tile: scores, probabilities against m_ref, PV.  Returns true if a
+  // logit of this wave overflowed the reference.
+  auto compute = [&](const uint16_t *T, int tile) -> bool {
+    const int base = 32 * tile;
+    f32x4 s[NHB][2];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) { s[hb][0] = f32x4{0.f, 0.f, 0.f, 0.f}; s[hb][1] = s[hb][0]; }
+    // S^T = K q~^T, software-pipelined one k-step deep; the scheduling barriers
+    // keep the compiler from hoisting every LDS read at once
+    {
+      const uint16_t *k0 = T + c * KP + 8 * g;
+      const uint16_t *k1 = k0 + 16 * KP;
+      f16x8 n0 = *reinterpret_cast<const f16x8 *>(k0), n1 = *reinterpret_cast<const f16x8 *>(k1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const f16x8 a0 = n0, a1 = n1;
+        if (j + 1 < NJ) {
+          n0 = *reinterpret_cast<const f16x8 *>(k0 + 32 * (j + 1));
+          n1 = *reinterpret_cast<const f16x8 *>(k1 + 32 * (j + 1));
+        }
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[hb][j], s[hb][0], 0, 0, 0);
+          s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[hb][j], s[hb][1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    bool over = false;
+    f16x8 pb[NHB];
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (base + 16 * mb + 4 * g + i >= nrows) s[hb][mb][i] = -INFINITY;
+          mloc = fmaxf(mloc, s[hb][mb][i]);
+        }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      m_seen[hb] = fmaxf(m_seen[hb], mloc);
+      if (m_ref[hb] == -INFINITY) m_ref[hb] = mloc;   // first tile of this pass
+      over = over || (mloc > m_ref[hb] + kRefSlack);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[4 * mb + i] = exp2f(s[hb][mb][i] - m_ref[hb]);
+          psum += p[4 * mb + i];
+        }
+      l_run[hb] += psum;
+      const u32x4 pw = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
+                             pack_f16x2(p[6], p[7])};
+      __builtin_memcpy(&pb[hb], &pw, 16);
+    }
+    // O^T += V^T P^T; V^T fragments by transposing reads of the row-major tile,
+    // pipelined one 16-dim block deep like the QK loop
+    const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3);
+    const uint16_t *v1p = v0p + 16 * KP;
+    v4i16 nlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)v0p);
+    v4i16 nhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)v1p);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      f16x8 a;
+      __builtin_memcpy(&a, &nlo, 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &nhi, 8);
+      if (db + 1 < NDB) {
+        nlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * (db + 1)));
+        nhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * (db + 1)));
+      }
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+        acc_o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[hb], acc_o[hb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return over;
+  };
+
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      l_run[hb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (tile_lo < tile_hi) gather(tile_lo, T0);
+    __syncthreads();   // the first tile landed (the barrier waits for outstanding memory)
+    bool restart = false;
+    int it = 0;
+    for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
+      const bool odd = it & 1;
+      if (tile + 1 < tile_hi) gather(tile + 1, odd ? T0 : T1);
+      const bool over = compute(odd ? T1 : T0, tile);
+      if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
+      if (tid == 0) rflag[(it + 1) & 1] = 0;
+      __syncthreads();   // next tile landed, this one fully read, flags visible
+      if (rflag[it & 1]) { restart = true; break; }
+    }
+    if (!restart) break;
+    __syncthreads();
+    if (tid < 2) rflag[tid] = 0;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) m_ref[hb] = m_seen[hb];
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const int h = h0 + 16 * hb + c;
+    float lr = l_run[hb];
+    lr += __shfl_xor(lr, 16, 64);
+    lr += __shfl_xor(lr, 32, 64);
+    const float mr = m_ref[hb];
+    if (A.nsplit > 1) {
+      const int64_t pr = ((int64_t)r * A.nsplit + split) * A.H + h;
+      float *po = A.part_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * g) = acc_o[hb][db];
+      if (g == 0) {
+        A.part_ml[2 * pr] = mr;
+        A.part_ml[2 * pr + 1] = lr;
+      }
+      continue;
+    }
+    float f = 1.f, den = lr;
+    if (A.sinks) {
+      const float sg = A.sinks[h] * kLog2e;
+      const float M = fmaxf(mr, sg);
+      f = exp2f(mr - M);
+      den = lr * f + exp2f(sg - M);
+    }
+    const float inv = den > 0.f ? f / den : 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      float o[4];
+      const int d0 = 16 * db + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
+      if (d0 >= D - R) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int pi = (d0 + 2 * k - (D - R)) >> 1;
+          const float cs = rc[pi], sn = rs[pi];
+          const float a = o[2 * k] * cs + o[2 * k + 1] * sn, bb = -o[2 * k] * sn + o[2 * k + 1] * cs;
+          o[2 * k] = a;
+          o[2 * k + 1] = bb;
+        }
+      }
+      const int64_t oe = ((int64_t)r * A.H + h) * D + d0;
+      if (A.out_dtype == DSV4_F32) {
+        *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
+      } else {
+        *reinterpret_cast<u32x2 *>((uint16_t *)A.out + oe) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+    }
+  }
+}
+
 // Merge split partials: grid (T * H), block D/2 threads (one channel pair each).
 template <int D>
 __global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
@@ -558,6 +833,7 @@ static RowSrc mk_src(const dsv4_rows *rw) {
   switch (rw->dtype) {
   case DSV4_F32: s.rbytes = 4LL * rw->dim; break;
   case DSV4_BF16: s.rbytes = 2LL * rw->dim; break;
+  case DSV4_F16: s.rbytes = 2LL * rw->dim; break;
   case DSV4_FP8R: s.rbytes = (int64_t)(rw->dim - rw->tail) + 2LL * rw->tail; break;
   default: s.rbytes = 0;
   }
@@ -621,7 +897,21 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
     A.part_ml = A.part_o + (size_t)T * ns * H * D;
   }
   const bool fp8 = (W > 0 && win->dtype == DSV4_FP8R) || (pool && pool->dtype == DSV4_FP8R);
+  const bool f16 = (W > 0 ? win->dtype == DSV4_F16 : true) && (pool ? pool->dtype == DSV4_F16 : true) &&
+                   (W > 0 || pool);
   dim3 grid((unsigned)((int64_t)T * ns));
+  if (f16) {
+    switch (H) {
+    case 16: hipLaunchKernelGGL((k_attn_f16<1, 1>), grid, dim3(64), 0, st, A); break;
+    case 32: hipLaunchKernelGGL((k_attn_f16<1, 2>), grid, dim3(128), 0, st, A); break;
+    case 48: hipLaunchKernelGGL((k_attn_f16<1, 3>), grid, dim3(192), 0, st, A); break;
+    default: hipLaunchKernelGGL((k_attn_f16<1, 4>), grid, dim3(256), 0, st, A); break;
+    }
+    int rc = check_launch("k_attn_f16");
+    if (rc || ns == 1) return rc;
+    hipLaunchKernelGGL(k_attn_combine<512>, dim3((unsigned)((int64_t)T * H)), dim3(256), 0, st, A);
+    return check_launch("k_attn_combine");
+  }
   switch (H / 16) {
 #define DSV4_ATT(NW)                                                                                  \
   case NW:                                                                                            \

@@ -27,6 +27,21 @@ struct Pair<float> {
     reinterpret_cast<float2 *>(p)[i] = make_float2(a, b);
   }
 };
+struct F16T {};   // tag: IEEE half storage
+template <>
+struct Pair<F16T> {
+  static __device__ __forceinline__ float2 load(const void *p, int64_t i) {
+    const uint32_t u = reinterpret_cast<const uint32_t *>(p)[i];
+    _Float16 a, b;
+    const uint16_t lo = (uint16_t)(u & 0xFFFF), hi = (uint16_t)(u >> 16);
+    __builtin_memcpy(&a, &lo, 2);
+    __builtin_memcpy(&b, &hi, 2);
+    return make_float2((float)a, (float)b);
+  }
+  static __device__ __forceinline__ void store(void *p, int64_t i, float a, float b) {
+    reinterpret_cast<uint32_t *>(p)[i] = pack_f16x2(a, b);
+  }
+};
 template <>
 struct Pair<uint16_t> {
   static __device__ __forceinline__ float2 load(const void *p, int64_t i) {
@@ -84,7 +99,7 @@ __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, co
 }
 
 // grid: x = pair blocks, y = row blocks.  y may alias x.
-template <typename T>
+template <typename T, typename TO>
 __global__ __launch_bounds__(256) void k_rope(const void *x, void *y, int64_t n_rows,
                                               int dim, int rope_dim, const int64_t *__restrict__ pos,
                                               double theta, float sign) {
@@ -101,7 +116,7 @@ __global__ __launch_bounds__(256) void k_rope(const void *x, void *y, int64_t n_
     const float a = v.x * cs - v.y * sn, bq = v.x * sn + v.y * cs;
     v.x = a; v.y = bq;
   }
-  Pair<T>::store(y, e, v.x, v.y);
+  Pair<TO>::store(y, e, v.x, v.y);
 }
 
 }  // namespace dsv4
@@ -119,29 +134,41 @@ int launch_compress(const void *c, const void *z, int in_dtype, const float *bia
 #define DSV4_CMP(TI, TO)                                                                               \
   hipLaunchKernelGGL((k_compress<TI, TO>), grid, block, 0, st, c, z, bias, S, dim, m, overlap, rope_dim, \
                      theta, pos0, pool)
-  if (in_dtype == DSV4_F32 && out_dtype == DSV4_F32) DSV4_CMP(float, float);
-  else if (in_dtype == DSV4_F32 && out_dtype == DSV4_BF16) DSV4_CMP(float, uint16_t);
-  else if (in_dtype == DSV4_BF16 && out_dtype == DSV4_F32) DSV4_CMP(uint16_t, float);
-  else DSV4_CMP(uint16_t, uint16_t);
+  if (in_dtype == DSV4_F32) {
+    if (out_dtype == DSV4_F32) DSV4_CMP(float, float);
+    else if (out_dtype == DSV4_BF16) DSV4_CMP(float, uint16_t);
+    else DSV4_CMP(float, F16T);
+  } else {
+    if (out_dtype == DSV4_F32) DSV4_CMP(uint16_t, float);
+    else if (out_dtype == DSV4_BF16) DSV4_CMP(uint16_t, uint16_t);
+    else DSV4_CMP(uint16_t, F16T);
+  }
 #undef DSV4_CMP
   return check_launch("k_compress");
 }
 
-int launch_rope(const void *x, void *y, int dtype, int64_t n_rows, int dim, int rope_dim, const int64_t *pos,
-                double theta, int inverse, hipStream_t st) {
+int launch_rope(const void *x, int x_dtype, void *y, int y_dtype, int64_t n_rows, int dim, int rope_dim,
+                const int64_t *pos, double theta, int inverse, hipStream_t st) {
   if (n_rows == 0) return DSV4_OK;
   const float sign = inverse ? -1.f : 1.f;
   int64_t done = 0;
   while (done < n_rows) {   // grid.y is limited to 65535 rows per launch
     const int64_t n = (n_rows - done) < 65535 ? (n_rows - done) : 65535;
     dim3 grid((dim / 2 + 255) / 256, (unsigned)n), block(256);
-    const int64_t off = done * (int64_t)dim * (dtype == DSV4_F32 ? 4 : 2);
-    const void *xs = (const char *)x + off;
-    void *ys = (char *)y + off;
-    if (dtype == DSV4_F32)
-      hipLaunchKernelGGL(k_rope<float>, grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, theta, sign);
-    else
-      hipLaunchKernelGGL(k_rope<uint16_t>, grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, theta, sign);
+    const void *xs = (const char *)x + done * (int64_t)dim * (x_dtype == DSV4_F32 ? 4 : 2);
+    void *ys = (char *)y + done * (int64_t)dim * (y_dtype == DSV4_F32 ? 4 : 2);
+#define DSV4_ROPE(TI, TO) \
+  hipLaunchKernelGGL((k_rope<TI, TO>), grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, theta, sign)
+    if (x_dtype == DSV4_F32) {
+      if (y_dtype == DSV4_F32) DSV4_ROPE(float, float);
+      else if (y_dtype == DSV4_BF16) DSV4_ROPE(float, uint16_t);
+      else DSV4_ROPE(float, F16T);
+    } else {
+      if (y_dtype == DSV4_F32) DSV4_ROPE(uint16_t, float);
+      else if (y_dtype == DSV4_BF16) DSV4_ROPE(uint16_t, uint16_t);
+      else DSV4_ROPE(uint16_t, F16T);
+    }
+#undef DSV4_ROPE
     done += n;
   }
   return check_launch("k_rope");

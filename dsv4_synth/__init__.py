@@ -103,7 +103,7 @@ class RowSet:
     """Per-sequence stored rows: a compressed pool or a sliding window.
 
     data      : [B, rows_per_seq, row_bytes] uint8 (any numpy dtype viewed as bytes)
-    kind      : 'f32' | 'bf16' | 'fp8r' | 'mxfp4'
+    kind      : 'f32' | 'bf16' | 'f16' | 'fp8r' | 'mxfp4'
     count     : [B] valid rows per sequence
     first_tok : [B] token index of row 0 (windows) or None (pools)
     """
@@ -136,6 +136,8 @@ def rowset_from_values(x: np.ndarray, kind: str, tail: int = 0, count=None,
         return RowSet(kind, x.copy().view(np.uint8).reshape(B, n, 4 * dim), dim, cnt, first_tok=ft)
     if kind == "bf16":
         return RowSet(kind, bf16_bits(x).view(np.uint8).reshape(B, n, 2 * dim), dim, cnt, first_tok=ft)
+    if kind == "f16":
+        return RowSet(kind, x.astype(np.float16).view(np.uint8).reshape(B, n, 2 * dim), dim, cnt, first_tok=ft)
     if kind == "fp8r":
         rows, sc = fp8r_pack(x, tail)
         return RowSet(kind, rows, dim, cnt, tail=tail, row_scale=sc, first_tok=ft)

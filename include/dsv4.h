@@ -53,11 +53,16 @@ extern "C" {
  * DSV4_MXFP4 : OCP MXFP4: E2M1 nibbles, low nibble = even element, dim/2 bytes
  *              per row, with one E8M0 scale byte per 32-element block in a
  *              separate plane (the MXFP4 indexer path of the MarkTechPost
- *              summary). */
+ *              summary).
+ * DSV4_F16   : IEEE binary16.  Offered as an output of the compressor and of
+ *              the rope kernel so that prefill K=V rows can be staged straight
+ *              into LDS for the fp16 matrix-core path; values must stay below
+ *              65504 in magnitude. */
 #define DSV4_F32 0
 #define DSV4_BF16 1
 #define DSV4_FP8R 2
 #define DSV4_MXFP4 3
+#define DSV4_F16 4
 
 /* Query rows of one call: row r belongs to sequence seq[r] and is token tok[r]
  * (0-based) of that sequence.  Prefill: every token of every sequence; decode:
@@ -98,7 +103,7 @@ typedef struct {
  * rope_theta^(-2i/rope_dim)) at position pos0[b] + s*m.
  *   c, z     : [n_seq, seq_len, dim], in_dtype DSV4_F32 or DSV4_BF16
  *   pos_bias : [2m or m, dim] float32
- *   pool     : [n_seq, seq_len / m, dim], out_dtype DSV4_F32 or DSV4_BF16
+ *   pool     : [n_seq, seq_len / m, dim], out_dtype DSV4_F32, DSV4_BF16 or DSV4_F16
  * Partial trailing windows are not pooled.  dim even, <= 4096. */
 int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *pos_bias,
                   int32_t n_seq, int32_t seq_len, int32_t dim, int32_t m, int32_t overlap,
@@ -108,11 +113,12 @@ int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *p
 /* dsv4_rope -- partial interleaved RoPE (HF page, "Hybrid attention", partial
  * RoPE bullet): for i < rope_dim/2 the channel pair (dim-R+2i, dim-R+2i+1) of
  * row r turns by angle sign * pos[r] * rope_theta^(-2i/R), sign = -1 when
- * inverse != 0.  Other channels are copied.  x, y: [n_rows, dim] in dtype
- * (DSV4_F32 or DSV4_BF16); y may equal x.  pos: [n_rows] int64 device. */
-int dsv4_rope(const void *x, void *y, int32_t dtype, int64_t n_rows, int32_t dim,
-              int32_t rope_dim, const int64_t *pos, double rope_theta, int32_t inverse,
-              hipStream_t stream);
+ * inverse != 0.  Other channels are copied.  x: [n_rows, dim] in x_dtype
+ * (DSV4_F32 or DSV4_BF16); y: [n_rows, dim] in y_dtype (DSV4_F32, DSV4_BF16 or
+ * DSV4_F16); y may equal x when the dtypes match.  pos: [n_rows] int64 device. */
+int dsv4_rope(const void *x, int32_t x_dtype, void *y, int32_t y_dtype, int64_t n_rows,
+              int32_t dim, int32_t rope_dim, const int64_t *pos, double rope_theta,
+              int32_t inverse, hipStream_t stream);
 
 /* dsv4_index_topk -- Lightning Indexer scores and per-query top-k.
  * HF page "Hybrid attention" (the indexer scores queries against the pool and
@@ -151,9 +157,10 @@ int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_i
  * and the last rope_dim channels of o are rotated back by -p.  Window and pool
  * rows are read as stored (already rotated).
  *   q      : [T, n_heads, dim] in q_dtype (DSV4_BF16 or DSV4_F32)
- *   window : W > 0 -> rows holding tokens (DSV4_BF16 / DSV4_F32 / DSV4_FP8R);
+ *   window : W > 0 -> rows holding tokens (DSV4_F16 / DSV4_BF16 / DSV4_FP8R for
+ *            bf16 queries, DSV4_F32 for fp32 queries);
  *            W = 0 -> no window branch (window may be NULL)
- *   pool   : same dtype family as window, dim equal; may be NULL when topk = 0
+ *   pool   : same dtype as window, dim equal; may be NULL when topk = 0
  *   idx    : [T, topk] int32 in [-1, pool->count[b]); topk = 0: no pool branch
  *   sinks  : [n_heads] float32 or NULL (no sink)
  *   out    : [T, n_heads, dim] in out_dtype (DSV4_BF16 or DSV4_F32)

@@ -30,8 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsv4_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-OR_F32, OR_BF16, OR_FP8R, OR_MXFP4, OR_F64 = 0, 1, 2, 3, 4
-_KIND = {"f32": OR_F32, "bf16": OR_BF16, "fp8r": OR_FP8R, "mxfp4": OR_MXFP4, "f64": OR_F64}
+OR_F32, OR_BF16, OR_FP8R, OR_MXFP4, OR_F64, OR_F16 = 0, 1, 2, 3, 4, 5
+_KIND = {"f32": OR_F32, "bf16": OR_BF16, "fp8r": OR_FP8R, "mxfp4": OR_MXFP4, "f64": OR_F64, "f16": OR_F16}
 
 
 def build(force: bool = False) -> str:
@@ -70,6 +70,8 @@ def _L():
         _lib.or_e4m3_to_f64.restype = D
         _lib.or_e2m1_to_f64.argtypes = [ctypes.c_uint8]
         _lib.or_e2m1_to_f64.restype = D
+        _lib.or_f16_to_f64.argtypes = [ctypes.c_uint16]
+        _lib.or_f16_to_f64.restype = D
         _lib.or_e8m0_to_f64.argtypes = [ctypes.c_uint8]
         _lib.or_e8m0_to_f64.restype = D
         _lib.or_num_threads.restype = I
@@ -102,6 +104,11 @@ def e4m3_to_f64(code: int) -> float:
 def e2m1_to_f64(code: int) -> float:
     """OCP MX E2M1 decode of one nibble."""
     return _L().or_e2m1_to_f64(code)
+
+
+def f16_to_f64(code: int) -> float:
+    """IEEE binary16 decode of one 16-bit pattern."""
+    return _L().or_f16_to_f64(code)
 
 
 def e8m0_to_f64(code: int) -> float:

@@ -23,7 +23,7 @@
 #include <omp.h>
 
 /* storage types understood by the oracle's own decoders */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8R = 2, OR_MXFP4 = 3, OR_F64 = 4 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8R = 2, OR_MXFP4 = 3, OR_F64 = 4, OR_F16 = 5 };
 
 /* A set of per-sequence rows (a compressed pool or a sliding window).
  * Row i of sequence b starts at byte (b*seq_stride + i) * row_bytes.
@@ -56,6 +56,16 @@ double or_bf16_to_f64(uint16_t h) {
   return (double)f;
 }
 
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits. */
+double or_f16_to_f64(uint16_t h) {
+  int s = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+  double mag;
+  if (e == 31) return m ? NAN : (s ? -INFINITY : INFINITY);
+  if (e == 0) mag = ldexp((double)m, -24);
+  else mag = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  return s ? -mag : mag;
+}
+
 /* OCP FP8 E4M3 ("fn" variant): 1 sign, 4 exponent (bias 7), 3 mantissa bits;
  * no infinities, S.1111.111 is NaN, largest finite magnitude 448. */
 double or_e4m3_to_f64(uint8_t v) {
@@ -85,6 +95,7 @@ static int64_t row_bytes(const or_rows *r) {
   case OR_F32: return 4LL * r->dim;
   case OR_F64: return 8LL * r->dim;
   case OR_BF16: return 2LL * r->dim;
+  case OR_F16: return 2LL * r->dim;
   case OR_FP8R: return (int64_t)(r->dim - r->tail) + 2LL * r->tail;
   case OR_MXFP4: return r->dim / 2;
   }
@@ -105,6 +116,9 @@ static void decode_vec(const uint8_t *p, int dtype, int dim, int tail, double sc
     break;
   case OR_BF16:
     for (d = 0; d < dim; d++) { uint16_t h; memcpy(&h, p + 2 * d, 2); out[d] = or_bf16_to_f64(h); }
+    break;
+  case OR_F16:
+    for (d = 0; d < dim; d++) { uint16_t h; memcpy(&h, p + 2 * d, 2); out[d] = or_f16_to_f64(h); }
     break;
   case OR_FP8R:
     for (d = 0; d < dim - tail; d++) out[d] = or_e4m3_to_f64(p[d]) * scale;

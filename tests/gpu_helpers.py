@@ -29,7 +29,8 @@ def dev(x, dtype=None):
 
 
 def kind_code(kind: str) -> int:
-    return {"f32": K.DSV4_F32, "bf16": K.DSV4_BF16, "fp8r": K.DSV4_FP8R, "mxfp4": K.DSV4_MXFP4}[kind]
+    return {"f32": K.DSV4_F32, "bf16": K.DSV4_BF16, "fp8r": K.DSV4_FP8R, "mxfp4": K.DSV4_MXFP4,
+            "f16": K.DSV4_F16}[kind]
 
 
 def upload_rows(rs: S.RowSet) -> K.RowStore:

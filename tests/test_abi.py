@@ -58,9 +58,12 @@ def test_compress_rejects_bad_args(K):
 def test_rope_rejects_bad_args(K):
     L = K.lib()
     fake = ctypes.c_void_p(0x1000)
-    assert _rc(L.dsv4_rope(fake, fake, 1, 4, 8, 16, fake, 1e4, 0, None)) == K.DSV4_EINVAL
-    assert _rc(L.dsv4_rope(fake, fake, 2, 4, 8, 4, fake, 1e4, 0, None)) == K.DSV4_ENOTSUP
-    assert _rc(L.dsv4_rope(fake, fake, 1, 4, 8, 4, fake, 0.0, 0, None)) == K.DSV4_EINVAL
+    other = ctypes.c_void_p(0x2000)
+    assert _rc(L.dsv4_rope(fake, 1, other, 1, 4, 8, 16, fake, 1e4, 0, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_rope(fake, 2, other, 1, 4, 8, 4, fake, 1e4, 0, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_rope(fake, 4, other, 1, 4, 8, 4, fake, 1e4, 0, None)) == K.DSV4_ENOTSUP   # F16 input
+    assert _rc(L.dsv4_rope(fake, 1, other, 1, 4, 8, 4, fake, 0.0, 0, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_rope(fake, 1, fake, 4, 4, 8, 4, fake, 1e4, 0, None)) == K.DSV4_EINVAL     # in place, dtypes differ
 
 
 def _queries(K, n=4):

@@ -79,6 +79,15 @@ def test_e4m3_all_codes_match_torch(orc):
     assert np.nanmax(got) == 448.0
 
 
+def test_f16_all_codes_match_numpy(orc):
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    got = np.array([orc.f16_to_f64(int(c)) for c in codes[::7]])
+    r = ref[::7]
+    nan = np.isnan(r)
+    assert np.array_equal(nan, np.isnan(got)) and np.array_equal(r[~nan], got[~nan])
+
+
 def test_e2m1_and_e8m0_tables(orc):
     # OCP MX spec: E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 is the sign
     mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]

@@ -63,10 +63,13 @@ def test_compress(K, store, B, Sx, D, m, overlap, R, theta):
                           pos0=dev(pos0), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(got.cpu().numpy(), ref, store, "compress")
-    if store == "bf16":   # bf16 output path rounds once more
+    if store == "bf16":   # bf16 / fp16 output paths round once more
         got16 = K.dsv4_compress(tensor_of(c, store), tensor_of(z, store), dev(bias), m, overlap, R, theta,
                                 pos0=dev(pos0))
         assert_close(got16.float().cpu().numpy(), ref, store, "compress bf16 out")
+        goth = K.dsv4_compress(tensor_of(c, store), tensor_of(z, store), dev(bias), m, overlap, R, theta,
+                               pos0=dev(pos0), out_dtype=torch.float16)
+        assert_close(goth.float().cpu().numpy(), ref, store, "compress f16 out")
 
 
 def test_compress_empty_and_short(K):
@@ -92,6 +95,8 @@ def test_rope(K, store, D, R, theta):
         torch.cuda.synchronize()
         tol_store = "f32" if store == "f32" else "bf16"
         assert_close(got.float().cpu().numpy(), ref, tol_store, f"rope inv={inv}")
+        goth = K.dsv4_rope(tensor_of(x, store), dev(pos), R, theta, inverse=inv, out_dtype=torch.float16)
+        assert_close(goth.float().cpu().numpy(), ref, "bf16", f"rope f16 out inv={inv}")
 
 
 # --------------------------------------------------------------------------- indexer + top-k
@@ -164,31 +169,36 @@ def test_index_topk_decode(K, kind, B, L, k):
 
 
 # --------------------------------------------------------------------------- attention
-def _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, seed, overlap=True):
-    """q/kv/pool values rounded to bf16; window rows rotated by the oracle."""
+def _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, seed, overlap=True, rows="bf16"):
+    """q values rounded to bf16; window rows rotated by the oracle; rows stored
+    as `rows` ('bf16' or 'f16')."""
     rng = np.random.default_rng(seed)
     r16 = lambda x: S.bf16_to_f32(S.bf16_bits(x.astype(np.float32)))
     q = r16(1.28 * rng.standard_normal((B, Sx, H, D)))
     kv = 1.28 * rng.standard_normal((B, Sx, D))
     pos0 = np.array([0, 777, 5][:B], np.int64)
     kv_rot = np.stack([O.rope(kv[b], pos0[b] + np.arange(Sx), R, theta, +1) for b in range(B)])
-    win = S.rowset_from_values(r16(kv_rot), "bf16", count=np.full(B, Sx), first_tok=np.zeros(B))
+    win = S.rowset_from_values(kv_rot.astype(np.float32), rows, count=np.full(B, Sx), first_tok=np.zeros(B))
     N = Sx // m
-    pool_vals = r16(1.28 * rng.standard_normal((B, N, D)))
-    pool = S.rowset_from_values(pool_vals, "bf16")
+    pool_vals = (1.28 * rng.standard_normal((B, N, D))).astype(np.float32)
+    pool = S.rowset_from_values(pool_vals, rows)
     sinks = rng.standard_normal(H).astype(np.float32)
     return q, win, pool, sinks, pos0
 
 
-@pytest.mark.parametrize("B,Sx,H,W,m,k", [
-    (2, 520, 64, 128, 4, 64),
-    (1, 300, 16, 40, 4, 200),   # k >= n: every visible entry
-    (1, 200, 32, 0, 4, 16),     # no window branch
+@pytest.mark.parametrize("B,Sx,H,W,m,k,rows", [
+    (2, 520, 64, 128, 4, 64, "bf16"),
+    (1, 300, 16, 40, 4, 200, "bf16"),   # k >= n: every visible entry
+    (1, 200, 32, 0, 4, 16, "bf16"),     # no window branch
+    (2, 520, 64, 128, 4, 64, "f16"),
+    (1, 300, 16, 40, 4, 200, "f16"),
+    (1, 200, 32, 0, 4, 16, "f16"),
+    (1, 700, 48, 128, 4, 100, "f16"),
 ])
-def test_sparse_attn_prefill(K, B, Sx, H, W, m, k):
-    say("sparse_attn prefill", B, Sx, H, W, m, k)
+def test_sparse_attn_prefill(K, B, Sx, H, W, m, k, rows):
+    say("sparse_attn prefill", B, Sx, H, W, m, k, rows)
     D, R, theta = 512, 64, 1.6e5
-    q, win, pool, sinks, pos0 = _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, 40 + Sx)
+    q, win, pool, sinks, pos0 = _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, 40 + Sx, rows=rows)
     rng = np.random.default_rng(3)
     N = Sx // m
     seq = np.repeat(np.arange(B), Sx).astype(np.int32)
@@ -207,16 +217,20 @@ def test_sparse_attn_prefill(K, B, Sx, H, W, m, k):
     assert_close(out.cpu().numpy(), ref, "bf16", "sparse_attn")
 
 
-@pytest.mark.parametrize("B,Sx,H,W,m,sink", [
-    (1, 1100, 64, 128, 16, True),
-    (2, 300, 64, 128, 128, True),
-    (1, 150, 16, 0, 1, True),      # m' = 1, no window: causal MQA with sink
-    (1, 90, 16, 7, 8, False),
+@pytest.mark.parametrize("B,Sx,H,W,m,sink,rows", [
+    (1, 1100, 64, 128, 16, True, "bf16"),
+    (2, 300, 64, 128, 128, True, "bf16"),
+    (1, 150, 16, 0, 1, True, "bf16"),      # m' = 1, no window: causal MQA with sink
+    (1, 90, 16, 7, 8, False, "bf16"),
+    (1, 1100, 64, 128, 16, True, "f16"),
+    (2, 300, 64, 128, 128, True, "f16"),
+    (1, 150, 16, 0, 1, True, "f16"),
+    (1, 90, 32, 7, 8, False, "f16"),
 ])
-def test_hca_attn_prefill(K, B, Sx, H, W, m, sink):
-    say("hca_attn prefill", B, Sx, H, W, m, sink)
+def test_hca_attn_prefill(K, B, Sx, H, W, m, sink, rows):
+    say("hca_attn prefill", B, Sx, H, W, m, sink, rows)
     D, R, theta = 512, 64, 1.6e5
-    q, win, pool, sinks, pos0 = _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, 50 + Sx)
+    q, win, pool, sinks, pos0 = _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, 50 + Sx, rows=rows)
     seq = np.repeat(np.arange(B), Sx).astype(np.int32)
     tok = np.tile(np.arange(Sx), B).astype(np.int32)
     qs = S.bf16_bits(q.reshape(B * Sx, H, D))
