@@ -398,6 +398,8 @@ def main():
     ap.add_argument("--no-legs", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--leg-steps", type=int, default=5)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy 1 GiB device-to-device once (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the path is "
@@ -444,6 +446,13 @@ def main():
                            "peak": PEAK_HBM, "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "traffic": None,
                            "kernel_ms_mean": round(kern_ms, 4)}
         rec["config"] = {"workload": wl.name, "bytes_per_step": wl.bytes}
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_probe_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu and isinstance(wl, CsaPrefill):
         log("cpu baseline (oracle on a sample)")
         rec["cpu_baseline"] = cpu_baseline_csa_prefill(torch, wl)

@@ -493,18 +493,24 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
     f32x4 s[NHB][2];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) { s[hb][0] = f32x4{0.f, 0.f, 0.f, 0.f}; s[hb][1] = s[hb][0]; }
-    // S^T = K q~^T, software-pipelined one k-step deep; the scheduling barriers
+    // S^T = K q~^T, software-pipelined QD k-steps deep; the scheduling barriers
     // keep the compiler from hoisting every LDS read at once
     {
+      constexpr int QD = 2;
       const uint16_t *k0 = T + c * KP + 8 * g;
       const uint16_t *k1 = k0 + 16 * KP;
-      f16x8 n0 = *reinterpret_cast<const f16x8 *>(k0), n1 = *reinterpret_cast<const f16x8 *>(k1);
+      f16x8 r0[QD], r1[QD];
+#pragma unroll
+      for (int j = 0; j < QD; ++j) {
+        r0[j] = *reinterpret_cast<const f16x8 *>(k0 + 32 * j);
+        r1[j] = *reinterpret_cast<const f16x8 *>(k1 + 32 * j);
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const f16x8 a0 = n0, a1 = n1;
-        if (j + 1 < NJ) {
-          n0 = *reinterpret_cast<const f16x8 *>(k0 + 32 * (j + 1));
-          n1 = *reinterpret_cast<const f16x8 *>(k1 + 32 * (j + 1));
+        const f16x8 a0 = r0[j % QD], a1 = r1[j % QD];
+        if (j + QD < NJ) {
+          r0[j % QD] = *reinterpret_cast<const f16x8 *>(k0 + 32 * (j + QD));
+          r1[j % QD] = *reinterpret_cast<const f16x8 *>(k1 + 32 * (j + QD));
         }
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
@@ -545,19 +551,24 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
       __builtin_memcpy(&pb[hb], &pw, 16);
     }
     // O^T += V^T P^T; V^T fragments by transposing reads of the row-major tile,
-    // pipelined one 16-dim block deep like the QK loop
+    // pipelined VD 16-dim blocks deep
+    constexpr int VD = 4;
     const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3);
     const uint16_t *v1p = v0p + 16 * KP;
-    v4i16 nlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)v0p);
-    v4i16 nhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)v1p);
+    v4i16 vlo[VD], vhi[VD];
+#pragma unroll
+    for (int db = 0; db < VD; ++db) {
+      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * db));
+      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * db));
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       f16x8 a;
-      __builtin_memcpy(&a, &nlo, 8);
-      __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &nhi, 8);
-      if (db + 1 < NDB) {
-        nlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * (db + 1)));
-        nhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * (db + 1)));
+      __builtin_memcpy(&a, &vlo[db % VD], 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &vhi[db % VD], 8);
+      if (db + VD < NDB) {
+        vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * (db + VD)));
+        vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * (db + VD)));
       }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
