@@ -58,6 +58,7 @@ struct AttnArgs {
   float scale_log2;   // sm_scale * log2(e)
   int rope_dim;
   double theta;
+  double inv_freq[32];   // theta^(-2i/rope_dim), fp64, filled on the host
   void *out;
   int out_dtype;
   int nsplit;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
   const int tile_hi = min(ntiles, tile_lo + tps);
   const int R = A.rope_dim;
 
-  if (tid < R / 2) rope_cs((double)P.p, tid, R, A.theta, 1.f, &rc[tid], &rs[tid]);
+  if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   __syncthreads();
 
   // q~ = RoPE(q) * sm_scale * log2(e) as the B operand: lane holds head h,
@@ -410,6 +411,15 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
   const int c = lane & 15, g = lane >> 4;
   const int r = (A.T - 1) - (int)(blockIdx.x / A.nsplit);
   const int split = blockIdx.x % A.nsplit;
+  // raw bf16 query loads first: their latency hides behind the setup below
+  const int h0 = wv * 16 * NHB;
+  f16x8 qb[NHB][NJ];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + h0 + 16 * hb + c) * D + 8 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qb[hb][j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
+  }
   RowPlan P = row_plan(A, r);
   if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_wave);
   const int nrows = P.nwin + P.nsel;
@@ -420,8 +430,8 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
   const int R = A.rope_dim;
   const int nwin = P.nwin, csa = A.csa;
   // row addressing in scalars: window rows first, then pool rows
-  const uint8_t *wbase = A.win.data ? A.win.data + ((int64_t)P.b * A.win.stride + P.wlo) * 1024 : nullptr;
   const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * 1024 : nullptr;
+  const uint8_t *wbase = A.win.data ? A.win.data + ((int64_t)P.b * A.win.stride + P.wlo) * 1024 : pbase;
 
   // zero both tiles once: rows past the end of the list are never gathered and
   // must hold finite values (their probabilities are zero)
@@ -429,33 +439,37 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
     reinterpret_cast<u32x4 *>(T0)[i] = u32x4{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4 *>(T1)[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  if (tid < R / 2) rope_cs((double)P.p, tid, R, A.theta, 1.f, &rc[tid], &rs[tid]);
+  if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   if (tid < 2) rflag[tid] = 0;
   __syncthreads();
 
-  // gather rows [32 tile, 32 tile + 32) of the list into T (wave w: rows w, w+NW, ...)
+  // gather rows [32 tile, 32 tile + 32) of the list into T (wave w: rows w, w+NW, ...):
+  // all row offsets first (pool picks come from LDS), then one DMA per row
   auto gather = [&](int tile, uint16_t *T) {
-    for (int rr = wv; rr < 32; rr += NW) {
-      const int i = 32 * tile + rr;
-      if (i < nrows) {
-        const uint8_t *rp;
-        if (i < nwin) rp = wbase + (int64_t)i * 1024;
-        else rp = pbase + (int64_t)(csa ? sel[i - nwin] : i - nwin) * 1024;
-        __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + rr * KP), 16, 0, 0);
+    constexpr int RPW = (32 + NW - 1) / NW;
+    // lane k < RPW looks up row wv + NW*k: window index (>= 0) or -1 - pool entry
+    const int i = 32 * tile + wv + NW * lane;
+    int rid = 0x7fffffff;
+    if (lane < RPW && wv + NW * lane < 32 && i < nrows) rid = i < nwin ? i : -1 - (csa ? sel[i - nwin] : i - nwin);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const int rk = __builtin_amdgcn_readlane(rid, k);
+      if (rk != 0x7fffffff) {
+        const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * 1024 : pbase + (int64_t)(-1 - rk) * 1024;
+        __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wv + NW * k) * KP), 16, 0, 0);
       }
     }
   };
 
-  // q~ = RoPE(q) * sm_scale * log2(e) in fp16, B operand: head h0 + 16hb + c, dims 32j + 8g .. +8
-  const int h0 = wv * 16 * NHB;
-  f16x8 qb[NHB][NJ];
+  // q~ = RoPE(q) * sm_scale * log2(e) in fp16, B operand: head h0 + 16hb + c,
+  // dims 32j + 8g .. +8; the raw loads were issued before the setup work
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) {
-    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + h0 + 16 * hb + c) * D;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d0 = 32 * j + 8 * g;
-      const u32x4 raw = *reinterpret_cast<const u32x4 *>(qr + d0);
+      u32x4 raw;
+      __builtin_memcpy(&raw, &qb[hb][j], 16);
       float x[8];
       const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -552,7 +566,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
     }
     // O^T += V^T P^T; V^T fragments by transposing reads of the row-major tile,
     // pipelined VD 16-dim blocks deep
-    constexpr int VD = 4;
+    constexpr int VD = 3;
     const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3);
     const uint16_t *v1p = v0p + 16 * KP;
     v4i16 vlo[VD], vhi[VD];
@@ -668,7 +682,7 @@ __global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
   const int b = A.seq[r];
   const int64_t p = (A.pos0 ? A.pos0[b] : 0) + A.tok[r];
   const int R = A.rope_dim;
-  if (pr < R / 2) rope_cs((double)p, pr, R, A.theta, 1.f, &rc[pr], &rs[pr]);
+  if (pr < R / 2) rope_cs_f((double)p, A.inv_freq[pr], 1.f, &rc[pr], &rs[pr]);
   __syncthreads();
   float M = A.sinks ? A.sinks[h] * kLog2e : -INFINITY;
   for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, A.part_ml[2 * (((int64_t)r * A.nsplit + s) * A.H + h)]);
@@ -720,7 +734,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs A, int D) {
   if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_wave);
   const int nrows = P.nwin + P.nsel;
   const int R = A.rope_dim;
-  if (tid < R / 2) rope_cs((double)P.p, tid, R, A.theta, 1.f, &rc[tid], &rs[tid]);
+  if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   __syncthreads();
   const float *q = (const float *)A.q + (int64_t)r * H * D;
   for (int e = tid; e < H * D / 2; e += 256) {
@@ -893,6 +907,7 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   A.scale_log2 = sm_scale * kLog2e;
   A.rope_dim = rope_dim;
   A.theta = theta;
+  for (int i = 0; i < 32; ++i) A.inv_freq[i] = (i < rope_dim / 2) ? pow(theta, -2.0 * i / (double)rope_dim) : 0.0;
   A.out = out;
   A.out_dtype = out_dtype;
   if (q_dtype == DSV4_F32) {

@@ -49,19 +49,23 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t v) {
   return __uint_as_float(__float_as_uint(mag) | s);
 }
 
-// ---- fp64 rope angle -> (cos, sin) in fp32 ----
-// The angle p * theta^(-2i/R) is formed and reduced in fp64 so positions up to
-// 2^20 keep a sub-microradian angle error; sin/cos of the reduced angle are fp64.
+// ---- rope angle -> (cos, sin) in fp32 ----
+// The angle p * f (f = theta^(-2i/R), fp64) is formed and reduced modulo 2 pi in
+// fp64, so positions up to 2^20 keep an angle error below a microradian; the
+// reduced angle is then rounded to fp32 (< 4e-7 rad) for sin/cos.
+__device__ __forceinline__ void rope_cs_f(double pos, double inv_freq, float sign, float *c, float *s) {
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = pos * inv_freq;
+  a = a - two_pi * floor(a / two_pi);
+  float sn, cs;
+  sincosf((float)a, &sn, &cs);
+  *c = cs;
+  *s = sn * sign;
+}
+
 __device__ __forceinline__ void rope_cs(double pos, int pair, int rope_dim, double theta, float sign,
                                         float *c, float *s) {
-  double f = pow(theta, -2.0 * (double)pair / (double)rope_dim);
-  double a = pos * f;
-  const double two_pi = 6.283185307179586476925286766559;
-  a = a - two_pi * floor(a / two_pi);
-  double sn, cs;
-  sincos(a, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn * sign;
+  rope_cs_f(pos, pow(theta, -2.0 * (double)pair / (double)rope_dim), sign, c, s);
 }
 
 __device__ __forceinline__ int64_t row_bytes(int dtype, int dim, int tail) {
