@@ -132,6 +132,119 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
   }
 }
 
+// -------------------------------------------------------------------- scores, many queries (MFMA)
+// k_index_scores_q8<NHB>: prefill form.  One workgroup scores 8 query rows
+// (2 per wave) against 64-entry key tiles staged once in LDS, so each key is
+// read from L2 once per 8 queries instead of once per query.  Same MFMA
+// mapping as above (heads = M, entries = N, head dim = K); queries of the group
+// that belong to different sequences are handled one sequence at a time.
+template <int NHB>
+__global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float scale, int T,
+                                                         float *__restrict__ scores, int64_t ld) {
+  constexpr int KS = 4;          // head dim 128 = 4 k-steps of 32
+  constexpr int DI = 128;
+  constexpr int KP = DI + 8;     // LDS row pitch (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * KP];
+  __shared__ int sh_b[8], sh_n[8];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int r0 = blockIdx.x * 8;
+  const int H = Q.H;
+  if (tid < 8) {
+    const int r = r0 + tid;
+    sh_b[tid] = r < T ? Q.seq[r] : -1;
+    sh_n[tid] = r < T ? n_visible(Q.tok[r], K.m, K.count[Q.seq[r]]) : 0;
+  }
+  // this wave's two queries: operands and weights in registers
+  bf16x8 qa[2][NHB][KS];
+  float wt[2][NHB][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int r = min(r0 + 2 * wv + qq, T - 1);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int h = 16 * hb + c;
+#pragma unroll
+      for (int j = 0; j < KS; ++j)
+        qa[qq][hb][j] = *reinterpret_cast<const bf16x8 *>((const uint16_t *)Q.q + ((int64_t)r * H + h) * DI + 32 * j + 8 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wt[qq][hb][i] = Q.w[(int64_t)r * H + 16 * hb + 4 * g + i];
+    }
+  }
+  __syncthreads();
+  for (int sgi = 0; sgi < 8; ++sgi) {
+    const int b = sh_b[sgi];
+    if (b < 0) break;
+    bool seen = false;
+    for (int k = 0; k < sgi; ++k) seen |= sh_b[k] == b;
+    if (seen) continue;
+    int nmax = 0;
+    for (int k = 0; k < 8; ++k)
+      if (sh_b[k] == b) nmax = max(nmax, sh_n[k]);
+    int nq[2];
+    bool mine[2];
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      mine[qq] = sh_b[2 * wv + qq] == b;
+      nq[qq] = mine[qq] ? sh_n[2 * wv + qq] : 0;
+    }
+    const int ntile = (nmax + 63) / 64;
+    const uint16_t *kbase = (const uint16_t *)K.data + (int64_t)b * K.stride * DI;
+    // staging: thread moves 16 B chunks it = tid + 256 k (k < 4) of the 64 x 128 tile
+    auto load = [&](int tile, u32x4 *v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int it = tid + 256 * k, row = it >> 4, ch = it & 15;
+        const int e = min(64 * tile + row, nmax - 1);
+        v[k] = *reinterpret_cast<const u32x4 *>(kbase + (int64_t)e * DI + 8 * ch);
+      }
+    };
+    auto store = [&](int buf, const u32x4 *v) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int it = tid + 256 * k, row = it >> 4, ch = it & 15;
+        *reinterpret_cast<u32x4 *>(&kt[buf][row * KP + 8 * ch]) = v[k];
+      }
+    };
+    u32x4 stg[4];
+    if (ntile > 0) {
+      load(0, stg);
+      store(0, stg);
+    }
+    __syncthreads();
+    for (int tile = 0; tile < ntile; ++tile) {
+      const int buf = tile & 1;
+      if (tile + 1 < ntile) load(tile + 1, stg);
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) {
+        const int e0 = 64 * tile + 16 * eb;
+        bf16x8 kb[KS];
+#pragma unroll
+        for (int j = 0; j < KS; ++j)
+          kb[j] = *reinterpret_cast<const bf16x8 *>(&kt[buf][(16 * eb + c) * KP + 32 * j + 8 * g]);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          if (!mine[qq] || e0 >= nq[qq]) continue;   // wave-uniform
+          float sacc = 0.f;
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < KS; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qq][hb][j], kb[j], acc, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc = fmaf(wt[qq][hb][i], fmaxf(acc[i], 0.f), sacc);
+          }
+          sacc += __shfl_xor(sacc, 16, 64);
+          sacc += __shfl_xor(sacc, 32, 64);
+          if (g == 0 && e0 + c < nq[qq]) scores[(int64_t)(r0 + 2 * wv + qq) * ld + e0 + c] = sacc * scale;
+        }
+      }
+      if (tile + 1 < ntile) store(buf ^ 1, stg);
+      __syncthreads();
+    }
+  }
+}
+
 // -------------------------------------------------------------------- scores (fp32 VALU)
 // grid (T, n_chunks), block 256: one thread per entry, the query in LDS.
 __global__ __launch_bounds__(256) void k_index_scores_f32(IdxQ Q, IdxK K, float scale, int chunk,
@@ -397,6 +510,14 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
     case 2: hipLaunchKernelGGL((k_index_scores_mfma<2, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
     case 3: hipLaunchKernelGGL((k_index_scores_mfma<3, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
     default: hipLaunchKernelGGL((k_index_scores_mfma<4, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
+    }
+  } else if (Di == 128 && T >= 2048) {
+    dim3 g8((T + 7) / 8);
+    switch (H / 16) {
+    case 1: hipLaunchKernelGGL((k_index_scores_q8<1>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 2: hipLaunchKernelGGL((k_index_scores_q8<2>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 3: hipLaunchKernelGGL((k_index_scores_q8<3>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    default: hipLaunchKernelGGL((k_index_scores_q8<4>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
     }
   } else {
 #define DSV4_IS(NHB, KS) hipLaunchKernelGGL((k_index_scores_mfma<NHB, KS, false>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld)
