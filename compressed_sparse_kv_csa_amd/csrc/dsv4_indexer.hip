@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
   __shared__ int sh_b[8], sh_n[8];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int r0 = blockIdx.x * 8;
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * 8;   // later (longer) rows first
   const int H = Q.H;
   if (tid < 8) {
     const int r = r0 + tid;
@@ -274,59 +274,6 @@ __global__ __launch_bounds__(256) void k_index_scores_f32(IdxQ Q, IdxK K, float 
 }
 
 // -------------------------------------------------------------------- block radix select
-// Block of 256 threads.  keys[0..n) in LDS.  Finds the key value T of the
-// want-th largest element and how many elements equal to T must be taken
-// (the lowest-index ones).  Exact; deterministic.
-struct SelectResult {
-  uint32_t prefix, mask, take_eq;
-};
-
-__device__ SelectResult block_radix_select(const uint32_t *keys, int n, int want, uint32_t *hist,
-                                           uint32_t *sh) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  uint32_t prefix = 0, mask = 0;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t k = keys[i];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wv == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; count of elements in higher bins
-      const uint32_t c0 = hist[4 * lane], c1 = hist[4 * lane + 1], c2 = hist[4 * lane + 2], c3 = hist[4 * lane + 3];
-      const uint32_t tot = c0 + c1 + c2 + c3;
-      uint32_t suf = tot;   // inclusive suffix sum over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += v;
-      }
-      uint32_t above = suf - tot;   // elements in bins of higher lanes
-      const uint32_t cs[4] = {c0, c1, c2, c3};
-#pragma unroll
-      for (int q = 3; q >= 0; --q) {
-        if (above < (uint32_t)want && (uint32_t)want <= above + cs[q]) {
-          sh[0] = prefix | ((uint32_t)(4 * lane + q) << shift);
-          sh[1] = (uint32_t)want - above;
-          sh[2] = cs[q];
-        }
-        above += cs[q];
-      }
-    }
-    __syncthreads();
-    prefix = sh[0];
-    want = (int)sh[1];
-    const uint32_t grp = sh[2];
-    mask |= 255u << shift;
-    __syncthreads();
-    if (grp == (uint32_t)want) break;   // the whole group is taken: no finer digit needed
-  }
-  return SelectResult{prefix, mask, (uint32_t)want};
-}
-
 // Block exclusive scan of one value per thread (256 threads).  Returns the
 // exclusive prefix; *total receives the block total.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh4, uint32_t *total) {
@@ -348,6 +295,61 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh4, u
   __syncthreads();
   *total = tot;
   return base + inc - v;
+}
+
+// Block of 256 threads.  keys[0..n) in LDS.  Finds the key value T of the
+// want-th largest element and how many elements equal to T must be taken
+// (the lowest-index ones).  Exact; deterministic.  Three digits of 12, 12 and
+// 8 bits: a 4096-bin first digit spreads scores that share a sign and most of
+// an exponent, which keeps the LDS histogram atomics mostly conflict-free.
+struct SelectResult {
+  uint32_t prefix, mask, take_eq;
+};
+
+constexpr int kHistBins = 4096;
+
+__device__ SelectResult block_radix_select(const uint32_t *keys, int n, int want, uint32_t *hist,
+                                           uint32_t *sh) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, mask = 0;
+  const int shifts[3] = {20, 8, 0};
+  const int widths[3] = {12, 12, 8};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const uint32_t dmask = (1u << widths[pass]) - 1u;
+    const int nb = 1 << widths[pass];
+    for (int i = tid; i < nb; i += 256) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint32_t k = keys[i];
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // thread owns bins [per*tid, per*tid + per); elements in higher bins
+    const int per = nb / 256;
+    uint32_t v = 0;
+    for (int q = 0; q < per; ++q) v += hist[per * tid + q];
+    uint32_t tot;
+    const uint32_t before = block_excl_scan(v, sh + 12, &tot);
+    uint32_t above = tot - before - v;
+    for (int q = per - 1; q >= 0; --q) {
+      const uint32_t cq = hist[per * tid + q];
+      if (above < (uint32_t)want && (uint32_t)want <= above + cq) {
+        sh[0] = prefix | ((uint32_t)(per * tid + q) << shift);
+        sh[1] = (uint32_t)want - above;
+        sh[2] = cq;
+      }
+      above += cq;
+    }
+    __syncthreads();
+    prefix = sh[0];
+    want = (int)sh[1];
+    const uint32_t grp = sh[2];
+    mask |= dmask << shift;
+    __syncthreads();
+    if (grp == (uint32_t)want) break;   // the whole group is taken: no finer digit needed
+  }
+  return SelectResult{prefix, mask, (uint32_t)want};
 }
 
 // Select the top `kk` of keys[0..n) (kk <= n) and write, in ascending position
@@ -396,9 +398,9 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ 
   uint32_t *keys = smem;                       // [chunk]
   int32_t *pos = (int32_t *)(smem + chunk);    // [topk]
   uint32_t *kout = smem + chunk + topk;        // [topk]
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t sh[16];
-  const int r = blockIdx.x, cidx = blockIdx.y, nch = gridDim.y;
+  const int r = gridDim.x - 1 - blockIdx.x, cidx = blockIdx.y, nch = gridDim.y;   // long rows first
   const int n = n_visible(tok[r], m, count[seq[r]]);
   const int lo = cidx * chunk;
   const int len = max(0, min(n, lo + chunk) - lo);
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(256) void k_topk_merge(const int32_t *__restrict__ 
   uint32_t *keys = smem;                    // [nc]
   int32_t *pos = (int32_t *)(smem + nc);    // [topk]
   uint32_t *kout = smem + nc + topk;        // [topk]
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t sh[16];
   const int r = blockIdx.x;
   const int n = n_visible(tok[r], m, count[seq[r]]);
