@@ -180,6 +180,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
   const int c = lane & 15, g = lane >> 4;
   const int r = (A.T - 1) - (int)(blockIdx.x / A.nsplit);   // longest rows first
   const int split = blockIdx.x % A.nsplit;
+  // raw bf16 query loads first: their latency hides behind the setup below
+  const int h = 16 * wv + c;
+  f16x8 qb[NJ];
+  {
+    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + h) * D + 8 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qb[j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
+  }
   RowPlan P = row_plan(A, r);
   if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_wave);
   const int nrows = P.nwin + P.nsel;
@@ -194,14 +202,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
 
   // q~ = RoPE(q) * sm_scale * log2(e) as the B operand: lane holds head h,
   // dims 32j + 8g .. +8
-  const int h = 16 * wv + c;
-  f16x8 qb[NJ];
   {
-    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + h) * D;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int d0 = 32 * j + 8 * g;
-      const u32x4 raw = *reinterpret_cast<const u32x4 *>(qr + d0);
+      u32x4 raw;
+      __builtin_memcpy(&raw, &qb[j], 16);
       float x[8];
       const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -865,12 +871,14 @@ static RowSrc mk_src(const dsv4_rows *rw) {
   return s;
 }
 
-// Splits per query: enough workgroups to fill the chip when rows are few.
+// Splits per query (decode): enough workgroups to occupy the chip, but at least
+// four 32-row tiles per split, because every split writes a 64 x 512 fp32
+// partial that the combine kernel reads back.
 int attn_nsplit(int T, int64_t max_rows) {
   const int64_t tiles = (max_rows + 31) / 32;
-  if (T >= 512 || tiles <= 1) return 1;
-  int64_t want = (512 + T - 1) / T;          // aim at >= 512 workgroups
-  int64_t cap = (tiles + 1) / 2;             // at least two tiles per split
+  if (T >= 512 || tiles < 8) return 1;
+  int64_t want = (256 + T - 1) / T;
+  const int64_t cap = tiles / 4;
   if (want > cap) want = cap;
   if (want > 64) want = 64;
   return want < 1 ? 1 : (int)want;
