@@ -379,35 +379,44 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
   }
 }
 
-// ---------------------------------------------------------------- fp16 rows, DMA-staged
-// k_attn_f16<NHB, NW>: the prefill fast path for fp16 K=V rows (the compressor
-// and the rope kernel emit fp16 for it).  NW waves, each owning 16*NHB heads
+// ---------------------------------------------------------------- fp16 / FP8 rows, DMA-staged
+// k_attn_f16<NHB, NW, FP8>: the fast path.  NW waves, each owning 16*NHB heads
 // (64 heads: 4 waves x 16 heads; the accumulators of 16 heads x 512 dims stay
-// in VGPRs, which allows two workgroups per CU).  Rows are gathered straight from global memory into LDS with
-// global_load_lds_dwordx4 (one 1 KB row per wave instruction, no VGPR
-// staging), double-buffered: the gather of tile i+1 is in flight while tile i
-// is on the matrix cores.  The PV operand V^T comes from the same row-major
-// tile through ds_read_b64_tr_b16 (a 16x4 transpose inside each 16-lane
-// group), so no transposed copy is written.
+// in VGPRs).  Rows are gathered straight from global memory into LDS with
+// global_load_lds_dwordx4 (no VGPR staging), double-buffered: the gather of
+// tile i+1 is in flight while tile i is on the matrix cores.  The PV operand
+// V^T comes from the same row-major fp16 tile through ds_read_b64_tr_b16 (a
+// 16x4 transpose inside each 16-lane group), so no transposed copy is written.
 //
-// Softmax without rescaling: the probabilities of a head are taken against a
-// fixed reference m_ref (the head's max over the first tile), so the output
-// accumulators are touched by nothing but MFMAs and stay in AGPRs.  A later
-// logit above m_ref + 15 (fp16 P would pass 2^15) makes the whole workgroup
-// start over with m_ref raised to the largest logit seen; each restart raises
-// m_ref by more than 15, so restarts are rare and finite.
+// fp16 rows (prefill: the compressor and the rope kernel emit fp16) land in
+// the tile as they are, one 1 KB row per wave instruction.  FP8 rows (decode
+// caches: 448 E4M3 bytes x row scale, then 64 bf16 rope channels, 576 B) land
+// as raw bytes, with their scales, in a second double buffer; one block-wide
+// pass then decodes the raw tile into the fp16 tile (every E4M3 value times its
+// fp32 scale, rounded once to fp16), so decoding is paid once per row per
+// workgroup instead of once per wave and MFMA operand.
+//
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 constexpr float kRefSlack = 15.f;   // log2 units: P <= 2^15 stays finite in fp16
 
-template <int NHB, int NW>
+// FP8 rows: 448 E4M3 channels, then 64 bf16 channels
+constexpr int kF8Nope = 448, kF8Row = kF8Nope + 2 * 64;
+constexpr int kF8Chunks = 32 * kF8Row / 1024;   // 1 KB DMA instructions per 32-row raw tile
+
+template <int NHB, int NW, bool FP8>
 __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
   constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
+  constexpr int RB = FP8 ? kF8Row : 2 * D;   // stored row bytes
+  static_assert(!FP8 || 32 * kF8Row % 1024 == 0, "raw tile must be whole DMA instructions");
   __shared__ __attribute__((aligned(16))) uint16_t T0[32 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t T1[32 * KP];
+  __shared__ __attribute__((aligned(16))) uint8_t RW[FP8 ? 2 * 32 * kF8Row : 16];
+  __shared__ float RSC[FP8 ? 2 * 32 : 1];
   __shared__ int sel[kMaxSel];
   __shared__ float rc[32], rs[32];
   __shared__ int sh_wave[NW];
@@ -436,14 +445,21 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
   const int R = A.rope_dim;
   const int nwin = P.nwin, csa = A.csa;
   // row addressing in scalars: window rows first, then pool rows
-  const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * 1024 : nullptr;
-  const uint8_t *wbase = A.win.data ? A.win.data + ((int64_t)P.b * A.win.stride + P.wlo) * 1024 : pbase;
+  const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * RB : nullptr;
+  const uint8_t *wbase = A.win.data ? A.win.data + ((int64_t)P.b * A.win.stride + P.wlo) * RB : pbase;
+  const float *psc = FP8 && A.pool.data ? A.pool.rscale + (int64_t)P.b * A.pool.stride : nullptr;
+  const float *wsc = FP8 && A.win.data ? A.win.rscale + (int64_t)P.b * A.win.stride + P.wlo : psc;
 
-  // zero both tiles once: rows past the end of the list are never gathered and
-  // must hold finite values (their probabilities are zero)
+  // zero both tiles once (and the raw FP8 buffers): rows past the end of the
+  // list are never gathered and must hold finite values (their probabilities
+  // are zero)
   for (int i = tid; i < 32 * KP / 8; i += NT) {
     reinterpret_cast<u32x4 *>(T0)[i] = u32x4{0u, 0u, 0u, 0u};
     reinterpret_cast<u32x4 *>(T1)[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (FP8) {
+    for (int i = tid; i < 2 * 32 * kF8Row / 16; i += NT) reinterpret_cast<u32x4 *>(RW)[i] = u32x4{0u, 0u, 0u, 0u};
+    if (tid < 64) RSC[tid] = 0.f;
   }
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   if (tid < 2) rflag[tid] = 0;
@@ -461,9 +477,54 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
     for (int k = 0; k < RPW; ++k) {
       const int rk = __builtin_amdgcn_readlane(rid, k);
       if (rk != 0x7fffffff) {
-        const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * 1024 : pbase + (int64_t)(-1 - rk) * 1024;
+        const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB;
         __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wv + NW * k) * KP), 16, 0, 0);
       }
+    }
+  };
+  // FP8: the raw 32-row tile is 18 KB of consecutive 1 KB DMA chunks (wave w:
+  // chunks w, w+NW, ...); lane l of chunk q copies bytes [1024q + 16l, +16) of
+  // the tile, i.e. part of row (1024q + 16l) / 576.  The last wave also copies
+  // the 32 row scales.
+  auto gather_raw = [&](int tile, int buf) {
+    const int i = 32 * tile + lane;
+    int rid = 0x7fffffff;
+    if (lane < 32 && i < nrows) rid = i < nwin ? i : -1 - (csa ? sel[i - nwin] : i - nwin);
+    uint8_t *R = RW + buf * (32 * kF8Row);
+#pragma unroll
+    for (int q = wv; q < kF8Chunks; q += NW) {
+      const int o = 1024 * q + 16 * lane;
+      const int row = o / kF8Row;
+      const int rk = __shfl(rid, row, 64);
+      if (rk != 0x7fffffff) {
+        const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB;
+        __builtin_amdgcn_global_load_lds(rp + (o - row * kF8Row), (lds_void *)(R + 1024 * q), 16, 0, 0);
+      }
+    }
+    if (wv == NW - 1 && rid != 0x7fffffff) {
+      const float *sp = rid >= 0 ? wsc + rid : psc + (-1 - rid);
+      __builtin_amdgcn_global_load_lds(sp, (lds_void *)(RSC + 32 * buf), 4, 0, 0);
+    }
+  };
+  // FP8: decode raw tile buf into the fp16 tile T
+  auto convert = [&](int buf, uint16_t *T) {
+    const uint8_t *R = RW + buf * (32 * kF8Row);
+    const float *sc = RSC + 32 * buf;
+    for (int u = tid; u < 32 * (kF8Nope / 8); u += NT) {   // 8 E4M3 codes per item
+      const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
+      const u32x2 v = *reinterpret_cast<const u32x2 *>(R + row * kF8Row + 8 * c8);
+      const float s = sc[row];
+      const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false), a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
+      const v2f a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false), a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
+      *reinterpret_cast<u32x4 *>(T + row * KP + 8 * c8) =
+          u32x4{pack_f16x2(a0.x * s, a0.y * s), pack_f16x2(a1.x * s, a1.y * s), pack_f16x2(a2.x * s, a2.y * s),
+                pack_f16x2(a3.x * s, a3.y * s)};
+    }
+    for (int u = tid; u < 32 * 8; u += NT) {   // 8 bf16 rope channels per item
+      const int row = u >> 3, c8 = u & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(R + row * kF8Row + kF8Nope + 16 * c8);
+      *reinterpret_cast<u32x4 *>(T + row * KP + kF8Nope + 8 * c8) =
+          u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
     }
   };
 
@@ -605,18 +666,41 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (tile_lo < tile_hi) gather(tile_lo, T0);
-    __syncthreads();   // the first tile landed (the barrier waits for outstanding memory)
     bool restart = false;
     int it = 0;
-    for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
-      const bool odd = it & 1;
-      if (tile + 1 < tile_hi) gather(tile + 1, odd ? T0 : T1);
-      const bool over = compute(odd ? T1 : T0, tile);
-      if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
-      if (tid == 0) rflag[(it + 1) & 1] = 0;
-      __syncthreads();   // next tile landed, this one fully read, flags visible
-      if (rflag[it & 1]) { restart = true; break; }
+    if constexpr (!FP8) {
+      if (tile_lo < tile_hi) gather(tile_lo, T0);
+      __syncthreads();   // the first tile landed (the barrier waits for outstanding memory)
+      for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
+        const bool odd = it & 1;
+        if (tile + 1 < tile_hi) gather(tile + 1, odd ? T0 : T1);
+        const bool over = compute(odd ? T1 : T0, tile);
+        if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
+        if (tid == 0) rflag[(it + 1) & 1] = 0;
+        __syncthreads();   // next tile landed, this one fully read, flags visible
+        if (rflag[it & 1]) { restart = true; break; }
+      }
+    } else {
+      // raw tile i+1 is in flight while tile i is on the matrix cores; the
+      // decode of raw i+1 into the other fp16 tile sits between two barriers
+      if (tile_lo < tile_hi) gather_raw(tile_lo, 0);
+      __syncthreads();   // raw tile landed (the barrier waits for outstanding memory)
+      if (tile_lo < tile_hi) convert(0, T0);
+      if (tile_lo + 1 < tile_hi) gather_raw(tile_lo + 1, 1);
+      __syncthreads();
+      for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
+        const bool odd = it & 1;
+        const bool over = compute(odd ? T1 : T0, tile);
+        if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
+        if (tid == 0) rflag[(it + 1) & 1] = 0;
+        __syncthreads();   // raw tile+1 landed, this tile fully read, flags visible
+        if (rflag[it & 1]) { restart = true; break; }
+        if (tile + 1 < tile_hi) convert(odd ? 0 : 1, odd ? T0 : T1);
+        if (tile + 2 < tile_hi) gather_raw(tile + 2, odd ? 1 : 0);
+        // make the decoded tile visible without waiting for the gather just issued
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+      }
     }
     if (!restart) break;
     __syncthreads();
@@ -933,14 +1017,20 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   const bool fp8 = (W > 0 && win->dtype == DSV4_FP8R) || (pool && pool->dtype == DSV4_FP8R);
   const bool f16 = (W > 0 ? win->dtype == DSV4_F16 : true) && (pool ? pool->dtype == DSV4_F16 : true) &&
                    (W > 0 || pool);
+  // FP8 rows in the 448 E4M3 + 64 bf16 layout take the DMA-staged path too
+  const bool fp8fast = fp8 && D == 512 && (W > 0 ? win->tail == 64 : true) && (pool ? pool->tail == 64 : true);
   dim3 grid((unsigned)((int64_t)T * ns));
-  if (f16) {
+  if (f16 || fp8fast) {
+#define DSV4_F16K(NW)                                                                                 \
+  if (f16) hipLaunchKernelGGL((k_attn_f16<1, NW, false>), grid, dim3(NW * 64), 0, st, A);             \
+  else hipLaunchKernelGGL((k_attn_f16<1, NW, true>), grid, dim3(NW * 64), 0, st, A);
     switch (H) {
-    case 16: hipLaunchKernelGGL((k_attn_f16<1, 1>), grid, dim3(64), 0, st, A); break;
-    case 32: hipLaunchKernelGGL((k_attn_f16<1, 2>), grid, dim3(128), 0, st, A); break;
-    case 48: hipLaunchKernelGGL((k_attn_f16<1, 3>), grid, dim3(192), 0, st, A); break;
-    default: hipLaunchKernelGGL((k_attn_f16<1, 4>), grid, dim3(256), 0, st, A); break;
+    case 16: DSV4_F16K(1) break;
+    case 32: DSV4_F16K(2) break;
+    case 48: DSV4_F16K(3) break;
+    default: DSV4_F16K(4) break;
     }
+#undef DSV4_F16K
     int rc = check_launch("k_attn_f16");
     if (rc || ns == 1) return rc;
     hipLaunchKernelGGL(k_attn_combine<512>, dim3((unsigned)((int64_t)T * H)), dim3(256), 0, st, A);

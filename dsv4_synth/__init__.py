@@ -369,12 +369,14 @@ class DecodeLayer:
 
 def decode_layer(seed: int, kind: str, B: int, L, H: int = 64, D: int = 512, R: int = 64,
                  W: int = 128, m: Optional[int] = None, topk: int = 512, Hi: int = 64, Di: int = 128,
-                 idx_kind: str = "bf16", theta: float = 160000.0, pool_rows: Optional[int] = None) -> DecodeLayer:
+                 idx_kind: str = "bf16", theta: float = 160000.0, pool_rows: Optional[int] = None,
+                 tail: Optional[int] = None) -> DecodeLayer:
     """Synthetic decode state: pools/windows N(0,1) then stored as FP8 E4M3 (+bf16
     rope channels, per-row scale); indexer keys N(0,1) as bf16 or MXFP4.
 
     L: tokens per sequence (scalar or [B]); the new token is token L-1 (its K=V
-    row is the last window row), the pool holds L//m entries."""
+    row is the last window row), the pool holds L//m entries.  tail: bf16 channels
+    at the end of each stored row (default R, the rope channels)."""
     if m is None:
         m = 4 if kind == "csa" else 128
     L = np.broadcast_to(np.asarray(L, np.int64), (B,)).copy()
@@ -382,9 +384,10 @@ def decode_layer(seed: int, kind: str, B: int, L, H: int = 64, D: int = 512, R: 
     Nmax = int(pool_rows if pool_rows is not None else N.max())
     t = _Tree(seed, ["q", "pool", "win", "sinks", "q_idx", "w_idx", "kpool"])
     q = bf16_to_f32(bf16_bits(t.draw("q", (B, H, D), 1.0)))
-    pool = rowset_from_values(t.draw("pool", (B, Nmax, D), 1.0), "fp8r", tail=R, count=N)
+    tail = R if tail is None else tail
+    pool = rowset_from_values(t.draw("pool", (B, Nmax, D), 1.0), "fp8r", tail=tail, count=N)
     wcount = np.minimum(L, W).astype(np.int32)
-    win = rowset_from_values(t.draw("win", (B, W, D), 1.0), "fp8r", tail=R, count=wcount,
+    win = rowset_from_values(t.draw("win", (B, W, D), 1.0), "fp8r", tail=tail, count=wcount,
                              first_tok=(L - wcount).astype(np.int32))
     layer = DecodeLayer(kind, B, L, H, D, R, theta, m, W, q, t.draw("sinks", (H,), 1.0), pool, win,
                         sm_scale=1.0 / np.sqrt(D), pos0=np.zeros(B, np.int64))

@@ -246,15 +246,17 @@ def test_hca_attn_prefill(K, B, Sx, H, W, m, sink, rows):
     assert_close(out.cpu().numpy(), ref, "bf16", "hca_attn")
 
 
-@pytest.mark.parametrize("kind,B,L,k", [
-    ("csa", 3, [1000, 4093, 2050], 256),
-    ("csa", 2, [131072, 700], 512),
-    ("hca", 2, [70000, 3000], 0),
-    ("hca", 1, [100], 0),
+@pytest.mark.parametrize("kind,B,L,k,H,tail", [
+    ("csa", 3, [1000, 4093, 2050], 256, 64, 64),
+    ("csa", 2, [131072, 700], 512, 64, 64),
+    ("csa", 2, [9000, 37], 512, 16, 64),      # 16 heads; a sequence shorter than the window
+    ("csa", 2, [5000, 2222], 256, 32, 32),    # 32 bf16 tail channels: the generic FP8 kernel
+    ("hca", 2, [70000, 3000], 0, 64, 64),
+    ("hca", 1, [100], 0, 48, 64),
 ])
-def test_attn_decode_fp8(K, kind, B, L, k):
-    say("attn decode fp8", kind, B, L, k)
-    layer = S.decode_layer(60 + B, kind, B, L, topk=max(k, 1))
+def test_attn_decode_fp8(K, kind, B, L, k, H, tail):
+    say("attn decode fp8", kind, B, L, k, H, tail)
+    layer = S.decode_layer(60 + B, kind, B, L, H=H, topk=max(k, 1), tail=tail)
     seq = np.arange(B, dtype=np.int32)
     tok = layer.tok
     qs = S.bf16_bits(layer.q)
