@@ -102,28 +102,39 @@ __device__ __forceinline__ RowPlan row_plan(const AttnArgs &A, int r) {
 }
 
 // Compact the valid entries of idx[r, :] (>= 0 and < count) into sel[],
-// preserving order.  Block-wide; returns the count.
+// preserving order.  Block-wide; every index load is issued before the one
+// barrier; returns the count (sel[] is visible after the caller's next
+// barrier).  sh_cnt holds kMaxSel/64 ints.
 template <int NT>
-__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_wave) {
+__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cnt) {
+  constexpr int NWV = NT / 64, PER = kMaxSel / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int cnt = A.pool.count[b];
+  const int nq = (A.topk + NT - 1) / NT;
+  int v[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = q * NT + tid;
+    v[q] = (q < nq && i < A.topk) ? A.idx[(int64_t)r * A.topk + i] : -1;
+  }
+  unsigned long long bal[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    bal[q] = __ballot(v[q] >= 0 && v[q] < cnt);
+    if (lane == 0 && q < nq) sh_cnt[q * NWV + wv] = __popcll(bal[q]);
+  }
+  __syncthreads();
   int total = 0;
-  for (int base = 0; base < A.topk; base += NT) {
-    const int i = base + tid;
-    int v = -1;
-    if (i < A.topk) v = A.idx[(int64_t)r * A.topk + i];
-    const bool ok = v >= 0 && v < cnt;
-    const unsigned long long bal = __ballot(ok);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sh_wave[wv] = __popcll(bal);
-    __syncthreads();
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    if (q >= nq) break;
     int off = total;
-    for (int w = 0; w < wv; ++w) off += sh_wave[w];
-    int tot = 0;
-    for (int w = 0; w < NT / 64; ++w) tot += sh_wave[w];
-    if (ok) sel[off + before] = v;
-    total += tot;
-    __syncthreads();
+    for (int w = 0; w < NWV; ++w) {
+      const int cw = sh_cnt[q * NWV + w];
+      off += w < wv ? cw : 0;
+      total += cw;
+    }
+    if ((bal[q] >> lane) & 1ull) sel[off + __popcll(bal[q] & ((1ull << lane) - 1ull))] = v[q];
   }
   return total;
 }
@@ -174,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
   __shared__ int sel[kMaxSel];
   __shared__ float rc[32], rs[32];
-  __shared__ int sh_wave[NW];
+  __shared__ int sh_cnt[kMaxSel / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -189,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
     for (int j = 0; j < NJ; ++j) qb[j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
   }
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_wave);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_cnt);
   const int nrows = P.nwin + P.nsel;
   const int ntiles = (nrows + 31) / 32;
   const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
@@ -409,7 +420,7 @@ constexpr int kF8Nope = 448, kF8Row = kF8Nope + 2 * 64;
 constexpr int kF8Chunks = 32 * kF8Row / 1024;   // 1 KB DMA instructions per 32-row raw tile
 
 template <int NHB, int NW, bool FP8>
-__global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
+__global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs A) {
   constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
   constexpr int RB = FP8 ? kF8Row : 2 * D;   // stored row bytes
   static_assert(!FP8 || 32 * kF8Row % 1024 == 0, "raw tile must be whole DMA instructions");
@@ -419,7 +430,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
   __shared__ float RSC[FP8 ? 2 * 32 : 1];
   __shared__ int sel[kMaxSel];
   __shared__ float rc[32], rs[32];
-  __shared__ int sh_wave[NW];
+  __shared__ int sh_cnt[kMaxSel / 64];
   __shared__ int rflag[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -436,12 +447,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
     for (int j = 0; j < NJ; ++j) qb[hb][j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
   }
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_wave);
-  const int nrows = P.nwin + P.nsel;
-  const int ntiles = (nrows + 31) / 32;
-  const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
-  const int tile_lo = split * tps;
-  const int tile_hi = min(ntiles, tile_lo + tps);
   const int R = A.rope_dim;
   const int nwin = P.nwin, csa = A.csa;
   // row addressing in scalars: window rows first, then pool rows
@@ -450,46 +455,54 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
   const float *psc = FP8 && A.pool.data ? A.pool.rscale + (int64_t)P.b * A.pool.stride : nullptr;
   const float *wsc = FP8 && A.win.data ? A.win.rscale + (int64_t)P.b * A.win.stride + P.wlo : psc;
 
-  // zero both tiles once (and the raw FP8 buffers): rows past the end of the
-  // list are never gathered and must hold finite values (their probabilities
-  // are zero)
-  for (int i = tid; i < 32 * KP / 8; i += NT) {
-    reinterpret_cast<u32x4 *>(T0)[i] = u32x4{0u, 0u, 0u, 0u};
-    reinterpret_cast<u32x4 *>(T1)[i] = u32x4{0u, 0u, 0u, 0u};
+  // Row ids: window index (>= 0) or -1 - pool entry.  Positions past the end of
+  // the list are clamped to its last row, so every gathered tile row holds
+  // finite stored values (their probabilities are zero) and no buffer needs
+  // clearing.  nrows is provisional (window + HCA rows) until CSA compaction.
+  int nrows = nwin + P.nsel;
+  auto row_id = [&](int i) -> int {
+    i = min(i, nrows - 1);
+    return i < nwin ? i : -1 - (csa ? sel[i - nwin] : i - nwin);
+  };
+  constexpr int RPW = (32 + NW - 1) / NW;   // tile rows per wave (wave w: rows w, w+NW, ...)
+  auto tile_ids = [&](int tile) -> int {    // lane k < RPW: id of row wv + NW*k of the tile
+    return (lane < RPW && wv + NW * lane < 32) ? row_id(32 * tile + wv + NW * lane) : 0x7fffffff;
+  };
+  auto dma_row = [&](int ids, int k, uint16_t *T) {   // row wv + NW*k of a tile, one 1 KB DMA
+    const int rk = __builtin_amdgcn_readlane(ids, k);
+    if (rk != 0x7fffffff) {
+      const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB;
+      __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wv + NW * k) * KP), 16, 0, 0);
+    }
+  };
+  auto gather = [&](int tile, uint16_t *T) {
+    const int ids = tile_ids(tile);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) dma_row(ids, k, T);
+  };
+  // the first tile can be in flight during the compaction when its rows are
+  // known without it: window rows (CSA prefill: the newest 32 tokens) or HCA rows
+  const bool early = !FP8 && A.nsplit == 1 && (csa ? nwin >= 32 : nrows > 0);
+  if (early) gather(0, T0);
+  if (csa && A.topk > 0) {
+    P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_cnt);
+    nrows = nwin + P.nsel;
   }
-  if constexpr (FP8) {
-    for (int i = tid; i < 2 * 32 * kF8Row / 16; i += NT) reinterpret_cast<u32x4 *>(RW)[i] = u32x4{0u, 0u, 0u, 0u};
-    if (tid < 64) RSC[tid] = 0.f;
-  }
+  const int ntiles = (nrows + 31) / 32;
+  const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
+  const int tile_lo = split * tps;
+  const int tile_hi = min(ntiles, tile_lo + tps);
+
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   if (tid < 2) rflag[tid] = 0;
   __syncthreads();
 
-  // gather rows [32 tile, 32 tile + 32) of the list into T (wave w: rows w, w+NW, ...):
-  // all row offsets first (pool picks come from LDS), then one DMA per row
-  auto gather = [&](int tile, uint16_t *T) {
-    constexpr int RPW = (32 + NW - 1) / NW;
-    // lane k < RPW looks up row wv + NW*k: window index (>= 0) or -1 - pool entry
-    const int i = 32 * tile + wv + NW * lane;
-    int rid = 0x7fffffff;
-    if (lane < RPW && wv + NW * lane < 32 && i < nrows) rid = i < nwin ? i : -1 - (csa ? sel[i - nwin] : i - nwin);
-#pragma unroll
-    for (int k = 0; k < RPW; ++k) {
-      const int rk = __builtin_amdgcn_readlane(rid, k);
-      if (rk != 0x7fffffff) {
-        const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB;
-        __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wv + NW * k) * KP), 16, 0, 0);
-      }
-    }
-  };
   // FP8: the raw 32-row tile is 18 KB of consecutive 1 KB DMA chunks (wave w:
   // chunks w, w+NW, ...); lane l of chunk q copies bytes [1024q + 16l, +16) of
   // the tile, i.e. part of row (1024q + 16l) / 576.  The last wave also copies
   // the 32 row scales.
   auto gather_raw = [&](int tile, int buf) {
-    const int i = 32 * tile + lane;
-    int rid = 0x7fffffff;
-    if (lane < 32 && i < nrows) rid = i < nwin ? i : -1 - (csa ? sel[i - nwin] : i - nwin);
+    const int rid = lane < 32 ? row_id(32 * tile + lane) : 0x7fffffff;
     uint8_t *R = RW + buf * (32 * kF8Row);
 #pragma unroll
     for (int q = wv; q < kF8Chunks; q += NW) {
@@ -569,7 +582,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
 
   // one tile: scores, probabilities against m_ref, PV.  Returns true if a
   // logit of this wave overflowed the reference.
-  auto compute = [&](const uint16_t *T, int tile) -> bool {
+  // Tn/idn: the next tile's buffer and row ids (Tn == nullptr: nothing to
+  // gather); its DMAs are spread over the k-steps of S^T so that their issue
+  // (the texture path moves 64 B per clock per CU) overlaps the matrix cores
+  auto compute = [&](const uint16_t *T, int tile, uint16_t *Tn, int idn) -> bool {
     const int base = 32 * tile;
     f32x4 s[NHB][2];
 #pragma unroll
@@ -597,6 +613,10 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
         for (int hb = 0; hb < NHB; ++hb) {
           s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[hb][j], s[hb][0], 0, 0, 0);
           s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[hb][j], s[hb][1], 0, 0, 0);
+        }
+        if (Tn) {
+#pragma unroll
+          for (int k = (j * RPW) / NJ; k < ((j + 1) * RPW) / NJ; ++k) dma_row(idn, k, Tn);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -669,12 +689,12 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
     bool restart = false;
     int it = 0;
     if constexpr (!FP8) {
-      if (tile_lo < tile_hi) gather(tile_lo, T0);
+      if (tile_lo < tile_hi && !(early && pass == 0)) gather(tile_lo, T0);
       __syncthreads();   // the first tile landed (the barrier waits for outstanding memory)
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool odd = it & 1;
-        if (tile + 1 < tile_hi) gather(tile + 1, odd ? T0 : T1);
-        const bool over = compute(odd ? T1 : T0, tile);
+        const bool more = tile + 1 < tile_hi;
+        const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_ids(tile + 1) : 0);
         if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
         if (tid == 0) rflag[(it + 1) & 1] = 0;
         __syncthreads();   // next tile landed, this one fully read, flags visible
@@ -690,7 +710,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_f16(AttnArgs A) {
       __syncthreads();
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool odd = it & 1;
-        const bool over = compute(odd ? T1 : T0, tile);
+        const bool over = compute(odd ? T1 : T0, tile, nullptr, 0);
         if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
         if (tid == 0) rflag[(it + 1) & 1] = 0;
         __syncthreads();   // raw tile+1 landed, this tile fully read, flags visible
@@ -817,11 +837,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs A, int D) {
   float *lrun = alph + H;         // [H]
   __shared__ int sel[kMaxSel];
   __shared__ float rc[32], rs[32];
-  __shared__ int sh_wave[4];
+  __shared__ int sh_cnt[kMaxSel / 64];
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_wave);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_cnt);
   const int nrows = P.nwin + P.nsel;
   const int R = A.rope_dim;
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);

@@ -18,10 +18,15 @@
 //       Keys are read once, straight from HBM into MFMA registers; the ReLU,
 //       the head weights and the head sum run on the accumulators.
 //   k_index_scores_f32  scalar fp32 path (small fp32 shapes).
-//   k_topk_chunk / k_topk_merge  exact radix select (4 x 8-bit digits of an
-//       order-preserving key) in LDS, ties to the lower index, stable
-//       compaction so indices come out ascending.
+//   k_topk_chunk / k_topk_merge  exact radix select in LDS over an
+//       order-preserving key (digits of up to 12 bits, counted from the top of
+//       the keys' own range), ties to the lower index, stable compaction so
+//       indices come out ascending.
 #include "dsv4_common.h"
+
+#include <algorithm>
+#include <map>
+#include <mutex>
 
 namespace dsv4 {
 
@@ -56,22 +61,28 @@ __device__ __forceinline__ float keyf(uint32_t k) {
 }
 
 // -------------------------------------------------------------------- scores (MFMA)
-// grid (T, n_chunks), block 256 (4 waves).  Wave wv handles entry blocks
-// chunk_lo + 16*(wv + 4*it).  Lane l = 16*g + c:
+// grid (T, G), block 256 (4 waves).  The row's entries are dealt out in
+// super-blocks of 64*EB: workgroup y takes super-blocks y, y + G, y + 2G, ...,
+// so at any moment the G workgroups of a row stream one contiguous stretch of
+// the pool (DRAM pages stay open).  Wave wv takes the EB 16-entry blocks
+// 16*EB*wv + 16*eb of a super-block.  Lane l = 16*g + c:
 //   A (query) : head 16*hb + c,   k-slice g   (bf16: dims 32j + 8g .. +8)
 //   B (keys)  : entry e0 + c,     k-slice g
 //   D         : heads 16*hb + 4g + i (i < 4), entry e0 + c
-template <int NHB, int KS, bool FP4>
+// The key loads of iteration it+1 are issued before the MFMAs of iteration it
+// (two register stages), so each wave keeps 2*EB*16 key rows in flight: the
+// decode scan is one pass over a large pool and is bound by how many bytes
+// are outstanding, not by the matrix cores.
+template <int NHB, int KS, bool FP4, int EB>
 __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, int chunk,
                                                            float *__restrict__ scores, int64_t ld) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int b = Q.seq[r];
-  const int n = n_visible(Q.tok[r], K.m, K.count[b]);
-  const int lo = blockIdx.y * chunk;
-  const int hi = min(n, lo + chunk);
-  if (lo >= hi) return;
+  const int hi = n_visible(Q.tok[r], K.m, K.count[b]);
+  constexpr int STEP = 64 * EB;   // entries per super-block
+  if ((int64_t)blockIdx.y * STEP >= hi) return;
   const int H = Q.H, Di = Q.Di;
 
   // query operand and head weights in registers
@@ -95,40 +106,62 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
     for (int i = 0; i < 4; ++i) wt[hb][i] = Q.w[(int64_t)r * H + 16 * hb + 4 * g + i];
   }
 
+  struct Frag {
+    bf16x8 kb[EB][FP4 ? 1 : KS];
+    u32x4 kf[EB];
+    int ks[EB];
+  };
   const int64_t kbase = (int64_t)b * K.stride;
-  for (int e0 = lo + 16 * wv; e0 < hi; e0 += 64) {
-    const int e = min(e0 + c, hi - 1);   // clamp: lanes past the end re-read a valid row
-    const int64_t row = kbase + e;
-    float s = 0.f;
-    if constexpr (FP4) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>((const uint8_t *)K.data + row * (Di / 2) + 16 * g);
-      const i32x8 kb = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const int ks = K.bscale[row * (Di / 32) + g];
+  auto load = [&](int e0, Frag &f) {
 #pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[hb], kb, acc, 4, 4, 0, qs[hb], 0, ks);
+    for (int eb = 0; eb < EB; ++eb) {
+      const int e = min(e0 + 16 * eb + c, hi - 1);   // clamp: lanes past the end re-read a valid row
+      const int64_t row = kbase + e;
+      if constexpr (FP4) {
+        f.kf[eb] = *reinterpret_cast<const u32x4 *>((const uint8_t *)K.data + row * (Di / 2) + 16 * g);
+        f.ks[eb] = K.bscale[row * (Di / 32) + g];
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], fmaxf(acc[i], 0.f), s);
-      }
-    } else {
-      bf16x8 kb[KS];
-#pragma unroll
-      for (int j = 0; j < KS; ++j)
-        kb[j] = *reinterpret_cast<const bf16x8 *>((const uint16_t *)K.data + row * Di + 32 * j + 8 * g);
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < KS; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][j], kb[j], acc, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], fmaxf(acc[i], 0.f), s);
+        for (int j = 0; j < KS; ++j)
+          f.kb[eb][j] = *reinterpret_cast<const bf16x8 *>((const uint16_t *)K.data + row * Di + 32 * j + 8 * g);
       }
     }
-    // sum over the four lane groups (heads 4g..4g+3 of every head block)
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    if (g == 0 && e0 + c < hi) scores[(int64_t)r * ld + e0 + c] = s * scale;
+  };
+  auto comp = [&](int e0, const Frag &f) {
+#pragma unroll
+    for (int eb = 0; eb < EB; ++eb) {
+      float s = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP4) {
+          const i32x8 kb = i32x8{(int)f.kf[eb].x, (int)f.kf[eb].y, (int)f.kf[eb].z, (int)f.kf[eb].w, 0, 0, 0, 0};
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[hb], kb, acc, 4, 4, 0, qs[hb], 0, f.ks[eb]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < KS; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][j], f.kb[eb][j], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], fmaxf(acc[i], 0.f), s);
+      }
+      // sum over the four lane groups (heads 4g..4g+3 of every head block)
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      const int e = e0 + 16 * eb + c;
+      if (g == 0 && e < hi) scores[(int64_t)r * ld + e] = s * scale;
+    }
+  };
+  const int gstride = (int)gridDim.y * STEP;
+  Frag f0, f1;
+  int e0 = (int)blockIdx.y * STEP + 16 * EB * wv;
+  if (e0 < hi) load(e0, f0);
+  for (; e0 < hi; e0 += 2 * gstride) {
+    const int e1 = e0 + gstride;
+    if (e1 < hi) load(e1, f1);
+    comp(e0, f0);
+    if (e1 >= hi) break;
+    if (e1 + gstride < hi) load(e1 + gstride, f0);
+    comp(e1, f1);
   }
 }
 
@@ -273,10 +306,35 @@ __global__ __launch_bounds__(256) void k_index_scores_f32(IdxQ Q, IdxK K, float 
   }
 }
 
-// -------------------------------------------------------------------- block radix select
-// Block exclusive scan of one value per thread (256 threads).  Returns the
-// exclusive prefix; *total receives the block total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh4, uint32_t *total) {
+// -------------------------------------------------------------------- block top-k
+// One workgroup of 256 threads selects the kk largest of up to 256*KPT keys
+// held in registers: thread t holds positions 4*(t + 256*(j/4)) + j%4, so a
+// row of scores loads as coalesced 16-byte vectors.  Keys are order-preserving
+// images of the scores (0 = empty).  Exact and deterministic:
+//   1. the keys are shifted to k - kmin + 1 so their significant bits start
+//      at the top of the block's own range;
+//   2. radix select, 8-bit digits from the top: a 256-bin LDS histogram of the
+//      keys still matching the chosen prefix, a block scan over the bins in
+//      descending order, and the bin holding the want-th largest becomes the
+//      next prefix; it stops once the whole boundary group is taken or every
+//      bit is resolved;
+//   3. equal keys at the boundary are taken lowest position first (a bitmap
+//      of the boundary group and a prefix popcount give each its rank);
+//   4. the selection is a bitmap over positions; its prefix popcount is every
+//      selected key's output slot, so the output comes out in ascending
+//      position order with no sort.
+struct TkLds {
+  uint32_t hist[2][256];
+  uint32_t sh[32];
+  uint32_t bm[512];     // bitmap over positions (256*KPT/32 words)
+  uint32_t wpre[512];   // exclusive prefix popcount of bm per word
+};
+
+__device__ __forceinline__ int tk_pos(int j) { return 4 * ((int)threadIdx.x + 256 * (j >> 2)) + (j & 3); }
+
+// Exclusive scan of one value per thread over the 256 threads (one barrier;
+// sh4 must not be reused before two more barriers).
+__device__ __forceinline__ uint32_t tk_scan(uint32_t v, uint32_t *sh4, uint32_t *total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   uint32_t inc = v;
 #pragma unroll
@@ -289,164 +347,243 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t *sh4, u
   uint32_t base = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (i < wv) base += sh4[i];
+    base += i < wv ? sh4[i] : 0u;
     tot += sh4[i];
   }
-  __syncthreads();
   *total = tot;
   return base + inc - v;
 }
 
-// Block of 256 threads.  keys[0..n) in LDS.  Finds the key value T of the
-// want-th largest element and how many elements equal to T must be taken
-// (the lowest-index ones).  Exact; deterministic.  Three digits of 12, 12 and
-// 8 bits: a 4096-bin first digit spreads scores that share a sign and most of
-// an exponent, which keeps the LDS histogram atomics mostly conflict-free.
-struct SelectResult {
-  uint32_t prefix, mask, take_eq;
-};
-
-constexpr int kHistBins = 4096;
-
-__device__ SelectResult block_radix_select(const uint32_t *keys, int n, int want, uint32_t *hist,
-                                           uint32_t *sh) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  const int shifts[3] = {20, 8, 0};
-  const int widths[3] = {12, 12, 8};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const uint32_t dmask = (1u << widths[pass]) - 1u;
-    const int nb = 1 << widths[pass];
-    for (int i = tid; i < nb; i += 256) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += 256) {
-      const uint32_t k = keys[i];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // thread owns bins [per*tid, per*tid + per); elements in higher bins
-    const int per = nb / 256;
-    uint32_t v = 0;
-    for (int q = 0; q < per; ++q) v += hist[per * tid + q];
-    uint32_t tot;
-    const uint32_t before = block_excl_scan(v, sh + 12, &tot);
-    uint32_t above = tot - before - v;
-    for (int q = per - 1; q >= 0; --q) {
-      const uint32_t cq = hist[per * tid + q];
-      if (above < (uint32_t)want && (uint32_t)want <= above + cq) {
-        sh[0] = prefix | ((uint32_t)(per * tid + q) << shift);
-        sh[1] = (uint32_t)want - above;
-        sh[2] = cq;
-      }
-      above += cq;
-    }
-    __syncthreads();
-    prefix = sh[0];
-    want = (int)sh[1];
-    const uint32_t grp = sh[2];
-    mask |= dmask << shift;
-    __syncthreads();
-    if (grp == (uint32_t)want) break;   // the whole group is taken: no finer digit needed
-  }
-  return SelectResult{prefix, mask, (uint32_t)want};
-}
-
-// Select the top `kk` of keys[0..n) (kk <= n) and write, in ascending position
-// order, out_pos[j] = position and out_key[j] = key for j < kk.
-__device__ void block_topk_compact(const uint32_t *keys, int n, int kk, uint32_t *hist, uint32_t *sh,
-                                   int32_t *out_pos, uint32_t *out_key) {
-  const SelectResult sel = block_radix_select(keys, n, kk, hist, sh);
-  const int tid = threadIdx.x;
-  const int seg = (n + 255) / 256;
-  const int a = min(n, tid * seg), bnd = min(n, a + seg);
-  uint32_t gt = 0, eq = 0;
-  for (int i = a; i < bnd; ++i) {
-    const uint32_t k = keys[i] & sel.mask;
-    gt += k > sel.prefix;
-    eq += k == sel.prefix;
-  }
+// L.bm -> L.wpre (nw words); ends with a barrier.
+__device__ __forceinline__ void tk_word_prefix(TkLds &L, int nw, uint32_t *sh4) {
+  const int per = (nw + 255) / 256, w0 = per * (int)threadIdx.x;
+  uint32_t c = 0;
+  for (int q = 0; q < per; ++q)
+    if (w0 + q < nw) c += __popc(L.bm[w0 + q]);
   uint32_t tot;
-  const uint32_t eq_before = block_excl_scan(eq, sh + 4, &tot);
-  uint32_t eq_take = 0;
-  if (eq_before < sel.take_eq) eq_take = min(eq, sel.take_eq - eq_before);
-  const uint32_t off = block_excl_scan(gt + eq_take, sh + 8, &tot);
-  uint32_t o = off, eq_used = 0;
-  for (int i = a; i < bnd; ++i) {
-    const uint32_t kf = keys[i];
-    const uint32_t k = kf & sel.mask;
-    bool take = k > sel.prefix;
-    if (!take && k == sel.prefix && eq_used < eq_take) { take = true; ++eq_used; }
-    if (take) {
-      out_pos[o] = i;
-      if (out_key) out_key[o] = kf;
-      ++o;
+  uint32_t run = tk_scan(c, sh4, &tot);
+  for (int q = 0; q < per; ++q)
+    if (w0 + q < nw) {
+      L.wpre[w0 + q] = run;
+      run += __popc(L.bm[w0 + q]);
     }
-  }
+  __syncthreads();
 }
 
-// grid (T, n_chunks).  Chunk c covers entries [c*chunk, min(n, (c+1)*chunk)).
-// n_chunks == 1: writes the final idx/score rows.  Otherwise writes per-chunk
-// candidates (ascending entry order, key 0 in unused slots).
+__device__ __forceinline__ uint32_t tk_rank(const TkLds &L, int pos) {
+  const int w = pos >> 5, bit = pos & 31;
+  return L.wpre[w] + __popc(L.bm[w] & ((1u << bit) - 1u));
+}
+
+// Select the kk (>= 1) largest non-empty keys; emit(rank, j, key) for each,
+// ranks 0..kk-1 in ascending position order.  There must be at least kk
+// non-empty keys.
+template <int KPT, class Emit>
+__device__ void tk_select(uint32_t (&k)[KPT], int kk, TkLds &L, Emit emit) {
+  static_assert(KPT % 4 == 0 && KPT <= 64, "keys per thread");
+  constexpr int NW = 8 * KPT;   // bitmap words
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // 1. range of the non-empty keys
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    if (k[j]) lo = min(lo, k[j]);
+    hi = max(hi, k[j]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) {
+    L.sh[4 + wv] = lo;
+    L.sh[8 + wv] = hi;
+  }
+  if (tid == 0) {   // the selection if no bin matched (kk beyond the non-empty keys)
+    L.sh[0] = 0u;
+    L.sh[1] = (uint32_t)kk;
+    L.sh[2] = 0u;
+  }
+  L.hist[0][tid] = 0u;
+  for (int w = tid; w < NW; w += 256) L.bm[w] = 0u;
+  __syncthreads();
+  const uint32_t kmin = min(min(L.sh[4], L.sh[5]), min(L.sh[6], L.sh[7]));
+  const uint32_t kmax = max(max(L.sh[8], L.sh[9]), max(L.sh[10], L.sh[11]));
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) k[j] = k[j] ? k[j] - kmin + 1u : 0u;
+  const uint32_t span = kmax - kmin + 1u;
+  // 2. radix select
+  int hb = 32 - __clz(span);
+  uint32_t prefix = 0u, mask = 0u, want = (uint32_t)kk, grp = 0u;
+  for (int p = 0; hb > 0; ++p) {
+    const int w = hb >= 8 ? 8 : hb, shift = hb - w;
+    const uint32_t dm = (1u << w) - 1u;
+    uint32_t *H = L.hist[p & 1];
+    L.hist[(p + 1) & 1][tid] = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t x = k[j];
+      if (x && (x & mask) == prefix) atomicAdd(&H[(x >> shift) & dm], 1u);
+    }
+    __syncthreads();
+    const int bin = 255 - tid;   // thread order = descending bins
+    const uint32_t v = H[bin];
+    uint32_t tot;
+    const uint32_t above = tk_scan(v, L.sh + 12 + 4 * (p % 3), &tot);
+    if (above < want && want <= above + v) {
+      L.sh[0] = prefix | ((uint32_t)bin << shift);
+      L.sh[1] = want - above;
+      L.sh[2] = v;
+    }
+    __syncthreads();
+    prefix = L.sh[0];
+    want = L.sh[1];
+    grp = L.sh[2];
+    mask |= dm << shift;
+    hb = shift;
+    if (grp == want) break;   // the whole boundary group is taken
+  }
+  // 3. ties at the boundary: lowest positions first
+  uint64_t take_eq = ~0ull;
+  if (grp != want) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t x = k[j];
+      if (x && (x & mask) == prefix) atomicOr(&L.bm[tk_pos(j) >> 5], 1u << (tk_pos(j) & 31));
+    }
+    __syncthreads();
+    tk_word_prefix(L, NW, L.sh + 24);
+    take_eq = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const uint32_t x = k[j];
+      if (x && (x & mask) == prefix && tk_rank(L, tk_pos(j)) < want) take_eq |= 1ull << j;
+    }
+    __syncthreads();
+    for (int w = tid; w < NW; w += 256) L.bm[w] = 0u;
+    __syncthreads();
+  }
+  // 4. selection bitmap -> ranks
+  uint64_t selm = 0ull;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const uint32_t x = k[j];
+    const uint32_t xm = x & mask;
+    if (x && (xm > prefix || (xm == prefix && ((take_eq >> j) & 1ull)))) {
+      selm |= 1ull << j;
+      atomicOr(&L.bm[tk_pos(j) >> 5], 1u << (tk_pos(j) & 31));
+    }
+  }
+  __syncthreads();
+  tk_word_prefix(L, NW, L.sh + 28);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((selm >> j) & 1ull) {
+      const uint32_t rank = tk_rank(L, tk_pos(j));
+      if (rank < (uint32_t)kk) emit((int)rank, j, k[j] + kmin - 1u);
+    }
+}
+
+// grid (T, n_chunks), 256 threads.  Chunk c covers entries [c*chunk, min(n,
+// (c+1)*chunk)), chunk <= 256*KPT.  One chunk: writes the final idx/score rows.
+// Otherwise writes per-chunk candidates (ascending entry order, key 0 and
+// index -1 in unused slots) for k_topk_merge.
+template <int KPT>
 __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
                                                     const int32_t *__restrict__ count, int m,
                                                     const float *__restrict__ scores, int64_t ld, int chunk,
                                                     int topk, int32_t *__restrict__ idx_out,
                                                     float *__restrict__ score_out, uint32_t *__restrict__ cand_key,
                                                     int32_t *__restrict__ cand_idx) {
-  extern __shared__ uint32_t smem[];
-  uint32_t *keys = smem;                       // [chunk]
-  int32_t *pos = (int32_t *)(smem + chunk);    // [topk]
-  uint32_t *kout = smem + chunk + topk;        // [topk]
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t sh[16];
+  __shared__ TkLds L;
   const int r = gridDim.x - 1 - blockIdx.x, cidx = blockIdx.y, nch = gridDim.y;   // long rows first
   const int n = n_visible(tok[r], m, count[seq[r]]);
   const int lo = cidx * chunk;
   const int len = max(0, min(n, lo + chunk) - lo);
   const int kk = min(topk, len);
-  for (int i = threadIdx.x; i < len; i += 256) keys[i] = fkey(scores[(int64_t)r * ld + lo + i]);
-  __syncthreads();
-  if (kk > 0) block_topk_compact(keys, len, kk, hist, sh, pos, kout);
-  __syncthreads();
-  if (nch == 1) {
-    for (int j = threadIdx.x; j < topk; j += 256) {
-      idx_out[(int64_t)r * topk + j] = j < kk ? lo + pos[j] : -1;
-      if (score_out) score_out[(int64_t)r * topk + j] = j < kk ? keyf(kout[j]) : -INFINITY;
+  const bool final_ = nch == 1;
+  int32_t *io = final_ ? idx_out + (int64_t)r * topk : cand_idx + ((int64_t)r * nch + cidx) * topk;
+  float *so = final_ && score_out ? score_out + (int64_t)r * topk : nullptr;
+  uint32_t *ko = final_ ? nullptr : cand_key + ((int64_t)r * nch + cidx) * topk;
+  auto emit = [&](int rank, int pos, uint32_t key) {
+    io[rank] = lo + pos;
+    if (so) so[rank] = keyf(key);
+    if (ko) ko[rank] = key;
+  };
+  if (kk == len) {   // everything visible is taken, in order
+    for (int j = threadIdx.x; j < len; j += 256) {
+      const float v = scores[(int64_t)r * ld + lo + j];
+      emit(j, j, fkey(v));
     }
   } else {
-    const int64_t base = ((int64_t)r * nch + cidx) * topk;
-    for (int j = threadIdx.x; j < topk; j += 256) {
-      cand_key[base + j] = j < kk ? kout[j] : 0u;
-      cand_idx[base + j] = j < kk ? lo + pos[j] : -1;
+    uint32_t k[KPT];
+    const float *src = scores + (int64_t)r * ld + lo;
+    const bool vec = ((((int64_t)r * ld + lo) & 3) == 0) && (((uintptr_t)scores & 15) == 0);
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) {
+      const int p = 4 * ((int)threadIdx.x + 256 * q);
+      if (vec && p + 3 < len) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(src + p);
+        k[4 * q] = fkey(v[0]);
+        k[4 * q + 1] = fkey(v[1]);
+        k[4 * q + 2] = fkey(v[2]);
+        k[4 * q + 3] = fkey(v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k[4 * q + e] = p + e < len ? fkey(src[p + e]) : 0u;
+      }
     }
+    tk_select<KPT>(k, kk, L, [&](int rank, int j, uint32_t key) { emit(rank, tk_pos(j), key); });
+  }
+  for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
+    io[j] = -1;
+    if (so) so[j] = -INFINITY;
+    if (ko) ko[j] = 0u;
   }
 }
 
-// grid (T).  Merges n_chunks*topk candidates (key 0 = empty) into the final row.
+// grid (T), 256 threads.  Merges nc = n_chunks*topk <= 256*KPT candidates
+// (key 0 = empty) into the final row.
+template <int KPT>
 __global__ __launch_bounds__(256) void k_topk_merge(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
                                                     const int32_t *__restrict__ count, int m, int n_chunks,
                                                     int topk, const uint32_t *__restrict__ cand_key,
                                                     const int32_t *__restrict__ cand_idx,
                                                     int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
-  extern __shared__ uint32_t smem[];
+  __shared__ TkLds L;
   const int nc = n_chunks * topk;
-  uint32_t *keys = smem;                    // [nc]
-  int32_t *pos = (int32_t *)(smem + nc);    // [topk]
-  uint32_t *kout = smem + nc + topk;        // [topk]
-  __shared__ uint32_t hist[kHistBins];
-  __shared__ uint32_t sh[16];
   const int r = blockIdx.x;
   const int n = n_visible(tok[r], m, count[seq[r]]);
   const int kk = min(topk, n);
   const int64_t base = (int64_t)r * nc;
-  for (int i = threadIdx.x; i < nc; i += 256) keys[i] = cand_key[base + i];
-  __syncthreads();
-  if (kk > 0) block_topk_compact(keys, nc, kk, hist, sh, pos, kout);
-  __syncthreads();
-  for (int j = threadIdx.x; j < topk; j += 256) {
-    idx_out[(int64_t)r * topk + j] = j < kk ? cand_idx[base + pos[j]] : -1;
-    if (score_out) score_out[(int64_t)r * topk + j] = j < kk ? keyf(kout[j]) : -INFINITY;
+  int32_t *io = idx_out + (int64_t)r * topk;
+  float *so = score_out ? score_out + (int64_t)r * topk : nullptr;
+  if (kk > 0) {
+    uint32_t k[KPT];
+    const uint32_t *src = cand_key + base;
+    const bool vec = (base & 3) == 0 && (((uintptr_t)cand_key & 15) == 0);
+#pragma unroll
+    for (int q = 0; q < KPT / 4; ++q) {
+      const int p = 4 * ((int)threadIdx.x + 256 * q);
+      if (vec && p + 3 < nc) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + p);
+        k[4 * q] = v.x;
+        k[4 * q + 1] = v.y;
+        k[4 * q + 2] = v.z;
+        k[4 * q + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) k[4 * q + e] = p + e < nc ? src[p + e] : 0u;
+      }
+    }
+    tk_select<KPT>(k, kk, L, [&](int rank, int j, uint32_t key) {
+      io[rank] = cand_idx[base + tk_pos(j)];
+      if (so) so[rank] = keyf(key);
+    });
+  }
+  for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
+    io[j] = -1;
+    if (so) so[j] = -INFINITY;
   }
 }
 
@@ -456,22 +593,36 @@ using namespace dsv4;
 
 namespace dsv4host {
 
-// Chunking of the pool for scoring and top-k: the first-stage chunk holds at
-// most 16384 keys (64 KB of LDS); the merge stage holds n_chunks*topk keys.
+// Chunking of the pool for top-k: a first-stage chunk holds up to 16384 keys
+// (64 per thread); with several chunks the merge stage holds n_chunks*topk
+// candidates, also at most 16384.  The smallest chunk that keeps the merge
+// within bounds balances the two stages.
 struct TopkPlan {
-  int chunk, n_chunks;
+  int chunk, n_chunks, kpt1, kpt2;
   size_t scores_bytes, cand_bytes;
 };
 
+static int tk_kpt(int64_t n) {
+  int kpt = 4;
+  while (kpt < 64 && 256LL * kpt < n) kpt *= 2;
+  return kpt;
+}
+
 static TopkPlan plan_topk(int64_t n_rows, int64_t stride, int topk) {
   TopkPlan p;
-  int64_t ch = 4096;
-  while (ch < 16384 && ((stride + ch - 1) / ch) * topk > 16384) ch *= 2;
-  if (stride <= ch) ch = stride > 0 ? stride : 1;
-  p.chunk = (int)ch;
-  p.n_chunks = (int)((stride + ch - 1) / ch);
-  if (p.n_chunks < 1) p.n_chunks = 1;
-  p.scores_bytes = (size_t)n_rows * (size_t)stride * 4;
+  const int64_t st = stride > 0 ? stride : 1;
+  if (st <= 16384) {
+    p.chunk = (int)st;
+    p.n_chunks = 1;
+  } else {
+    int64_t ch = 4096;
+    while (ch < 16384 && ((st + ch - 1) / ch) * topk > 16384) ch *= 2;
+    p.chunk = (int)ch;
+    p.n_chunks = (int)((st + ch - 1) / ch);
+  }
+  p.kpt1 = tk_kpt(p.chunk);
+  p.kpt2 = tk_kpt((int64_t)p.n_chunks * topk);
+  p.scores_bytes = (size_t)n_rows * (size_t)st * 4;
   p.scores_bytes = (p.scores_bytes + 255) & ~(size_t)255;
   p.cand_bytes = p.n_chunks > 1 ? (size_t)n_rows * p.n_chunks * topk * 8 : 0;
   return p;
@@ -484,7 +635,25 @@ size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk) {
 
 int index_topk_supported(int64_t stride, int topk) {
   const TopkPlan p = plan_topk(1, stride, topk);
-  return (int64_t)p.n_chunks * topk <= 16384 + 0 || p.n_chunks == 1;
+  return p.n_chunks == 1 || (int64_t)p.n_chunks * topk <= 16384;
+}
+
+// Workgroups of `kernel` (`block` threads, no dynamic LDS) that the current
+// device holds at once; cached per device and kernel.
+static int resident_wgs(const void *kernel, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, kernel});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int n = per_cu * cus;
+  cache[{dev, kernel}] = n;
+  return n;
 }
 
 int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qscale, int q_dtype, const float *w,
@@ -499,36 +668,26 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
   IdxQ Q{q->seq, q->tok, qv, qscale, w, H, Di};
   IdxK K{kp->data, kp->blk_scale, kp->count, kp->seq_stride, m};
   const int64_t ld = kp->seq_stride;
-  // scoring chunk: 1024 entries per workgroup (16 blocks per wave)
-  const int sc_chunk = 1024;
-  const int sc_chunks = (int)((kp->seq_stride + sc_chunk - 1) / sc_chunk);
-  dim3 sgrid(T, sc_chunks > 0 ? sc_chunks : 1);
-  if (q_dtype == DSV4_F32) {
-    hipLaunchKernelGGL(k_index_scores_f32, sgrid, dim3(256), (size_t)(H * Di + H) * 4, st, Q, K, scale, sc_chunk,
-                       scores, ld);
-  } else if (q_dtype == DSV4_MXFP4) {
+  // scoring kernels with one workgroup per (query row, entry chunk)
+  typedef void (*ScoreK)(IdxQ, IdxK, float, int, float *, int64_t);
+  ScoreK sk = nullptr;
+  int eb = 1;   // entries per wave iteration / 16
+  if (q_dtype == DSV4_MXFP4) {
+    eb = 4;
     switch (H / 16) {
-    case 1: hipLaunchKernelGGL((k_index_scores_mfma<1, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
-    case 2: hipLaunchKernelGGL((k_index_scores_mfma<2, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
-    case 3: hipLaunchKernelGGL((k_index_scores_mfma<3, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
-    default: hipLaunchKernelGGL((k_index_scores_mfma<4, 1, true>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld); break;
+    case 1: sk = k_index_scores_mfma<1, 1, true, 4>; break;
+    case 2: sk = k_index_scores_mfma<2, 1, true, 4>; break;
+    case 3: sk = k_index_scores_mfma<3, 1, true, 4>; break;
+    default: sk = k_index_scores_mfma<4, 1, true, 4>; break;
     }
-  } else if (Di == 128 && T >= 2048) {
-    dim3 g8((T + 7) / 8);
-    switch (H / 16) {
-    case 1: hipLaunchKernelGGL((k_index_scores_q8<1>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    case 2: hipLaunchKernelGGL((k_index_scores_q8<2>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    case 3: hipLaunchKernelGGL((k_index_scores_q8<3>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    default: hipLaunchKernelGGL((k_index_scores_q8<4>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    }
-  } else {
-#define DSV4_IS(NHB, KS) hipLaunchKernelGGL((k_index_scores_mfma<NHB, KS, false>), sgrid, dim3(256), 0, st, Q, K, scale, sc_chunk, scores, ld)
-#define DSV4_IS_H(KS)                  \
-  switch (H / 16) {                    \
-  case 1: DSV4_IS(1, KS); break;       \
-  case 2: DSV4_IS(2, KS); break;       \
-  case 3: DSV4_IS(3, KS); break;       \
-  default: DSV4_IS(4, KS); break;      \
+  } else if (q_dtype != DSV4_F32 && !(Di == 128 && T >= 2048)) {
+    eb = 2;
+#define DSV4_IS_H(KS)                                          \
+  switch (H / 16) {                                            \
+  case 1: sk = k_index_scores_mfma<1, KS, false, 2>; break;    \
+  case 2: sk = k_index_scores_mfma<2, KS, false, 2>; break;    \
+  case 3: sk = k_index_scores_mfma<3, KS, false, 2>; break;    \
+  default: sk = k_index_scores_mfma<4, KS, false, 2>; break;   \
   }
     switch (Di / 32) {
     case 1: DSV4_IS_H(1); break;
@@ -537,18 +696,55 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
     default: DSV4_IS_H(4); break;
     }
 #undef DSV4_IS_H
-#undef DSV4_IS
+  }
+  if (q_dtype == DSV4_F32) {
+    const int sc_chunk = 1024;
+    const int sc_chunks = (int)((kp->seq_stride + sc_chunk - 1) / sc_chunk);
+    hipLaunchKernelGGL(k_index_scores_f32, dim3(T, sc_chunks > 0 ? sc_chunks : 1), dim3(256),
+                       (size_t)(H * Di + H) * 4, st, Q, K, scale, sc_chunk, scores, ld);
+  } else if (sk) {
+    // the chunk is sized so that the whole grid is resident at once: the scan
+    // runs as one wave of workgroups with no partly filled second round
+    const int64_t unit = 64LL * eb;   // entries per super-block
+    const int64_t blocks = (kp->seq_stride + unit - 1) / unit;
+    const int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, resident_wgs((const void *)sk, 256) / T),
+                                              std::max<int64_t>(1, blocks));
+    hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, 0, scores, ld);
+  } else {
+    dim3 g8((T + 7) / 8);
+    switch (H / 16) {
+    case 1: hipLaunchKernelGGL((k_index_scores_q8<1>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 2: hipLaunchKernelGGL((k_index_scores_q8<2>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 3: hipLaunchKernelGGL((k_index_scores_q8<3>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    default: hipLaunchKernelGGL((k_index_scores_q8<4>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    }
   }
   int rc = check_launch("k_index_scores");
   if (rc) return rc;
-  const size_t lds1 = ((size_t)p.chunk + 2 * (size_t)topk) * 4;
-  hipLaunchKernelGGL(k_topk_chunk, dim3(T, p.n_chunks), dim3(256), lds1, st, q->seq, q->tok, kp->count, m, scores, ld,
-                     p.chunk, topk, idx_out, score_out, cand_key, cand_idx);
+#define DSV4_TK1(KPT)                                                                                   \
+  hipLaunchKernelGGL((k_topk_chunk<KPT>), dim3(T, p.n_chunks), dim3(256), 0, st, q->seq, q->tok, kp->count, m, \
+                     scores, ld, p.chunk, topk, idx_out, score_out, cand_key, cand_idx)
+  switch (p.kpt1) {
+  case 4: DSV4_TK1(4); break;
+  case 8: DSV4_TK1(8); break;
+  case 16: DSV4_TK1(16); break;
+  case 32: DSV4_TK1(32); break;
+  default: DSV4_TK1(64); break;
+  }
+#undef DSV4_TK1
   rc = check_launch("k_topk_chunk");
   if (rc || p.n_chunks == 1) return rc;
-  const size_t lds2 = ((size_t)p.n_chunks * topk + 2 * (size_t)topk) * 4;
-  hipLaunchKernelGGL(k_topk_merge, dim3(T), dim3(256), lds2, st, q->seq, q->tok, kp->count, m, p.n_chunks, topk,
-                     cand_key, cand_idx, idx_out, score_out);
+#define DSV4_TK2(KPT)                                                                                   \
+  hipLaunchKernelGGL((k_topk_merge<KPT>), dim3(T), dim3(256), 0, st, q->seq, q->tok, kp->count, m, p.n_chunks, \
+                     topk, cand_key, cand_idx, idx_out, score_out)
+  switch (p.kpt2) {
+  case 4: DSV4_TK2(4); break;
+  case 8: DSV4_TK2(8); break;
+  case 16: DSV4_TK2(16); break;
+  case 32: DSV4_TK2(32); break;
+  default: DSV4_TK2(64); break;
+  }
+#undef DSV4_TK2
   return check_launch("k_topk_merge");
 }
 

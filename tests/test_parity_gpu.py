@@ -170,6 +170,37 @@ def test_index_topk_decode(K, kind, B, L, k):
     say("topk stats", stats)
 
 
+@pytest.mark.parametrize("B,L,k,n_distinct", [
+    (2, [4 * 30000, 4 * 3000 + 3], 512, 3),   # several chunks + merge
+    (1, [4 * 20000], 1024, 1),                # every score equal
+    (3, [4 * 5000, 4 * 700, 9], 256, 2),      # one chunk
+])
+def test_index_topk_ties(K, B, L, k, n_distinct):
+    """Pool rows repeat a few distinct keys in runs of 7, so each row's scores
+    take n_distinct values with thousands of exact ties: the picks must be the
+    oracle's exactly (ties to the lower entry)."""
+    say("index_topk ties", B, L, k, n_distinct)
+    layer = S.decode_layer(77 + B, "csa", B, L, topk=k)
+    kp = layer.kpool
+    rows = kp.data.view(np.uint16).reshape(B, kp.rows_per_seq, -1)
+    pick = (np.arange(kp.rows_per_seq) // 7) % n_distinct
+    rows[:] = rows[:, pick, :]
+    seq = np.arange(B, dtype=np.int32)
+    tok = layer.tok
+    qst = S.bf16_bits(layer.q_idx)
+    ref = O.index_scores(seq, tok, qst, "bf16", layer.w_idx, kp, layer.m, layer.score_scale)
+    nv = O.n_visible(tok, layer.m, kp.count)
+    want = O.topk(ref, nv, k)
+    Q = K.QueryRows(dev(seq), dev(tok), None, B)
+    idx = K.dsv4_index_topk(Q, tensor_of(layer.q_idx, "bf16"), dev(layer.w_idx), upload_rows(kp), layer.m, k,
+                            layer.score_scale)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    for r in range(B):
+        assert np.array_equal(np.sort(idx[r][idx[r] >= 0]), np.sort(want[r][want[r] >= 0])), f"row {r}"
+        assert np.array_equal(idx[r] >= 0, want[r] >= 0), f"row {r}: sentinel layout"
+
+
 # --------------------------------------------------------------------------- attention
 def _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, seed, overlap=True, rows="bf16"):
     """q values rounded to bf16; window rows rotated by the oracle; rows stored
