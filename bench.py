@@ -42,6 +42,25 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(summary):
+    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE runs scaled by a plain copy's counts),
+    or None when the summary is missing or the kernel's sources changed since
+    the counters were taken (sha256 of the listed source files)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        kv = dict(ln.split(": ", 1) for ln in open(path).read().splitlines() if ": " in ln and not ln.startswith(" "))
+        h = hashlib.sha256()
+        for f in kv["source_files"].split():
+            h.update(open(os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f), "rb").read())
+        if h.hexdigest() != kv["source_sha256"].strip():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ----------------------------------------------------------------------------- accounting
 def csa_prefill_counts(S, m, W, k, H, D, Hi, Di):
     t = np.arange(S, dtype=np.int64)
@@ -426,9 +445,10 @@ def main():
         rec["unit"] = "tokens/s"
         flop = wl.counts["attn_flop"]
         ach = flop / (kern_ms / 1e3) / 1e12
+        traffic = measured_traffic("k_attn_f16_csa_prefill_S8192_hbm.txt") if isinstance(wl, CsaPrefill) else None
         rec["roofline"] = {"bound": "mfma", "kernel": "k_attn_f16 (fp16 MFMA, fp32 accumulate)",
                            "achieved": round(ach, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
-                           "frac": round(ach / PEAK_MFMA_F16, 4), "traffic": None,
+                           "frac": round(ach / PEAK_MFMA_F16, 4), "traffic": traffic,
                            "algorithmic": f"{flop / 1e9:.1f} GFLOP per launch ({wl.counts['attn_pairs']} query-row "
                                           f"pairs x 64 heads x 512 x 4)",
                            "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_median": round(kern_med, 4)}

@@ -64,8 +64,10 @@ def assert_close(gpu: np.ndarray, ref: np.ndarray, store: str, what: str = ""):
                              f"max abs err {err.max():.3e}")
 
 
-def check_topk(gpu_idx: np.ndarray, scores: np.ndarray, n_valid: np.ndarray, k: int, what: str = "") -> dict:
+def check_topk(gpu_idx: np.ndarray, scores: np.ndarray, n_valid: np.ndarray, k: int, what: str = "",
+               gap: float = None) -> dict:
     """Gap rule.  Returns counts of exact-set rows and near-tie rows."""
+    GAP_ = GAP if gap is None else gap
     exact = ties = 0
     for r in range(gpu_idx.shape[0]):
         n = int(n_valid[r])
@@ -81,8 +83,8 @@ def check_topk(gpu_idx: np.ndarray, scores: np.ndarray, n_valid: np.ndarray, k: 
         sc = scores[r, :n]
         order = np.lexsort((np.arange(n), -sc))
         vk = sc[order[kk - 1]]
-        assert np.all(sc[picks] >= vk - GAP), f"{what} row {r}: a pick scores below v_k - gap"
-        must = np.nonzero(sc > vk + GAP)[0]
+        assert np.all(sc[picks] >= vk - GAP_), f"{what} row {r}: a pick scores below v_k - gap"
+        must = np.nonzero(sc > vk + GAP_)[0]
         assert np.all(np.isin(must, picks)), f"{what} row {r}: a clear winner is missing"
         ref_set = np.sort(order[:kk])
         if np.array_equal(np.sort(picks), ref_set):
