@@ -166,34 +166,37 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
 }
 
 // -------------------------------------------------------------------- scores, many queries (MFMA)
-// k_index_scores_q8<NHB>: prefill form.  One workgroup scores 8 query rows
-// (2 per wave) against 64-entry key tiles staged once in LDS, so each key is
-// read from L2 once per 8 queries instead of once per query.  Same MFMA
-// mapping as above (heads = M, entries = N, head dim = K); queries of the group
-// that belong to different sequences are handled one sequence at a time.
-template <int NHB>
+// k_index_scores_q8<NHB, QPW>: prefill form.  One workgroup scores 4*QPW query
+// rows (QPW per wave) against 64-entry key tiles staged once in LDS, so each key
+// is read from L2 once per 4*QPW queries.  Same MFMA mapping as above (heads =
+// M, entries = N, head dimension = K); queries of the group that belong to
+// different sequences are handled one sequence at a time.  QPW = 1 keeps the
+// query operand at 64 VGPRs, which leaves room for three waves per SIMD so the
+// ReLU / weighting VALU work of one wave overlaps the MFMAs of another.
+template <int NHB, int QPW>
 __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float scale, int T,
                                                          float *__restrict__ scores, int64_t ld) {
   constexpr int KS = 4;          // head dim 128 = 4 k-steps of 32
   constexpr int DI = 128;
   constexpr int KP = DI + 8;     // LDS row pitch (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][64 * KP];
-  __shared__ int sh_b[8], sh_n[8];
+  constexpr int QG = 4 * QPW;   // queries per workgroup
+  __shared__ int sh_b[QG], sh_n[QG];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int r0 = (gridDim.x - 1 - blockIdx.x) * 8;   // later (longer) rows first
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * QG;   // later (longer) rows first
   const int H = Q.H;
-  if (tid < 8) {
+  if (tid < QG) {
     const int r = r0 + tid;
     sh_b[tid] = r < T ? Q.seq[r] : -1;
     sh_n[tid] = r < T ? n_visible(Q.tok[r], K.m, K.count[Q.seq[r]]) : 0;
   }
   // this wave's two queries: operands and weights in registers
-  bf16x8 qa[2][NHB][KS];
-  float wt[2][NHB][4];
+  bf16x8 qa[QPW][NHB][KS];
+  float wt[QPW][NHB][4];
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int r = min(r0 + 2 * wv + qq, T - 1);
+  for (int qq = 0; qq < QPW; ++qq) {
+    const int r = min(r0 + QPW * wv + qq, T - 1);
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const int h = 16 * hb + c;
@@ -204,22 +207,26 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
       for (int i = 0; i < 4; ++i) wt[qq][hb][i] = Q.w[(int64_t)r * H + 16 * hb + 4 * g + i];
     }
   }
+  // the query loads must be complete before the tile loop: otherwise the
+  // compiler's first-use wait inside the loop (vmcnt counts in order) also
+  // waits for the next tile's key loads on every iteration
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
   __syncthreads();
-  for (int sgi = 0; sgi < 8; ++sgi) {
+  for (int sgi = 0; sgi < QG; ++sgi) {
     const int b = sh_b[sgi];
     if (b < 0) break;
     bool seen = false;
     for (int k = 0; k < sgi; ++k) seen |= sh_b[k] == b;
     if (seen) continue;
     int nmax = 0;
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < QG; ++k)
       if (sh_b[k] == b) nmax = max(nmax, sh_n[k]);
-    int nq[2];
-    bool mine[2];
+    int nq[QPW];
+    bool mine[QPW];
 #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      mine[qq] = sh_b[2 * wv + qq] == b;
-      nq[qq] = mine[qq] ? sh_n[2 * wv + qq] : 0;
+    for (int qq = 0; qq < QPW; ++qq) {
+      mine[qq] = sh_b[QPW * wv + qq] == b;
+      nq[qq] = mine[qq] ? sh_n[QPW * wv + qq] : 0;
     }
     const int ntile = (nmax + 63) / 64;
     const uint16_t *kbase = (const uint16_t *)K.data + (int64_t)b * K.stride * DI;
@@ -248,6 +255,9 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
     for (int tile = 0; tile < ntile; ++tile) {
       const int buf = tile & 1;
       if (tile + 1 < ntile) load(tile + 1, stg);
+      // per-lane partial sums of the tile's 4 entry blocks x 2 queries; the
+      // cross-lane head sums run afterwards, all eight together
+      float sacc[QPW][4];
 #pragma unroll
       for (int eb = 0; eb < 4; ++eb) {
         const int e0 = 64 * tile + 16 * eb;
@@ -256,20 +266,39 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
         for (int j = 0; j < KS; ++j)
           kb[j] = *reinterpret_cast<const bf16x8 *>(&kt[buf][(16 * eb + c) * KP + 32 * j + 8 * g]);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
+        for (int qq = 0; qq < QPW; ++qq) {
+          sacc[qq][eb] = 0.f;
           if (!mine[qq] || e0 >= nq[qq]) continue;   // wave-uniform
-          float sacc = 0.f;
+          // NHB independent accumulation chains, interleaved k-step by k-step
+          f32x4 acc[NHB];
 #pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int hb = 0; hb < NHB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < KS; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qq][hb][j], kb[j], acc, 0, 0, 0);
+          for (int j = 0; j < KS; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sacc = fmaf(wt[qq][hb][i], fmaxf(acc[i], 0.f), sacc);
-          }
-          sacc += __shfl_xor(sacc, 16, 64);
-          sacc += __shfl_xor(sacc, 32, 64);
-          if (g == 0 && e0 + c < nq[qq]) scores[(int64_t)(r0 + 2 * wv + qq) * ld + e0 + c] = sacc * scale;
+            for (int hb = 0; hb < NHB; ++hb)
+              acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[qq][hb][j], kb[j], acc[hb], 0, 0, 0);
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sacc[qq][eb] = fmaf(wt[qq][hb][i], fmaxf(acc[hb][i], 0.f), sacc[qq][eb]);
+        }
+      }
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq)
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) sacc[qq][eb] += __shfl_xor(sacc[qq][eb], 16, 64);
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq)
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) sacc[qq][eb] += __shfl_xor(sacc[qq][eb], 32, 64);
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq) {
+        if (!mine[qq] || g != 0) continue;
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb) {
+          const int e = 64 * tile + 16 * eb + c;
+          if (e < nq[qq]) scores[(int64_t)(r0 + QPW * wv + qq) * ld + e] = sacc[qq][eb] * scale;
         }
       }
       if (tile + 1 < ntile) store(buf ^ 1, stg);
@@ -711,12 +740,13 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
                                               std::max<int64_t>(1, blocks));
     hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, 0, scores, ld);
   } else {
-    dim3 g8((T + 7) / 8);
+    constexpr int QPW = 1;   // queries per wave (4 per workgroup share each key tile)
+    dim3 g8((T + 4 * QPW - 1) / (4 * QPW));
     switch (H / 16) {
-    case 1: hipLaunchKernelGGL((k_index_scores_q8<1>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    case 2: hipLaunchKernelGGL((k_index_scores_q8<2>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    case 3: hipLaunchKernelGGL((k_index_scores_q8<3>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    default: hipLaunchKernelGGL((k_index_scores_q8<4>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 1: hipLaunchKernelGGL((k_index_scores_q8<1, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 2: hipLaunchKernelGGL((k_index_scores_q8<2, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 3: hipLaunchKernelGGL((k_index_scores_q8<3, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    default: hipLaunchKernelGGL((k_index_scores_q8<4, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
     }
   }
   int rc = check_launch("k_index_scores");

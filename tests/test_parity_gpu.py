@@ -117,7 +117,7 @@ def _prefill_indexer_case(store, B, Sx, Hi, Di, m, k, seed):
     ("bf16", 2, 700, 64, 128, 4, 64),
     ("bf16", 1, 300, 16, 64, 4, 8),
     ("bf16", 1, 2050, 64, 128, 4, 512),
-    ("bf16", 3, 701, 64, 128, 4, 64),    # 8-query groups straddle sequences
+    ("bf16", 3, 701, 64, 128, 4, 64),    # 4-query groups straddle sequences
     ("bf16", 2, 1030, 32, 128, 4, 100),
 ])
 def test_index_topk_prefill(K, store, B, Sx, Hi, Di, m, k):
