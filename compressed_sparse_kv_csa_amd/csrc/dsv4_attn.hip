@@ -523,21 +523,47 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
   auto convert = [&](int buf, uint16_t *T) {
     const uint8_t *R = RW + buf * (32 * kF8Row);
     const float *sc = RSC + 32 * buf;
-    for (int u = tid; u < 32 * (kF8Nope / 8); u += NT) {   // 8 E4M3 codes per item
-      const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
-      const u32x2 v = *reinterpret_cast<const u32x2 *>(R + row * kF8Row + 8 * c8);
-      const float s = sc[row];
-      const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, false), a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.x, true);
-      const v2f a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, false), a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.y, true);
-      *reinterpret_cast<u32x4 *>(T + row * KP + 8 * c8) =
-          u32x4{pack_f16x2(a0.x * s, a0.y * s), pack_f16x2(a1.x * s, a1.y * s), pack_f16x2(a2.x * s, a2.y * s),
-                pack_f16x2(a3.x * s, a3.y * s)};
+    constexpr int NI = 32 * (kF8Nope / 8), NU = (NI + NT - 1) / NT;   // items of 8 E4M3 codes
+    constexpr int NR = (32 * 8 + NT - 1) / NT;                         // items of 8 bf16 rope channels
+    u32x2 v[NU];
+    float sv[NU];
+    u32x4 rv[NR];
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {   // every LDS read first
+      const int u = tid + NT * k;
+      if (u < NI) {
+        const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
+        v[k] = *reinterpret_cast<const u32x2 *>(R + row * kF8Row + 8 * c8);
+        sv[k] = sc[row];
+      }
     }
-    for (int u = tid; u < 32 * 8; u += NT) {   // 8 bf16 rope channels per item
-      const int row = u >> 3, c8 = u & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(R + row * kF8Row + kF8Nope + 16 * c8);
-      *reinterpret_cast<u32x4 *>(T + row * KP + kF8Nope + 8 * c8) =
-          u32x4{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int u = tid + NT * k;
+      if (u < 32 * 8) rv[k] = *reinterpret_cast<const u32x4 *>(R + (u >> 3) * kF8Row + kF8Nope + 16 * (u & 7));
+    }
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int u = tid + NT * k;
+      if (u < NI) {
+        const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
+        const float s = sv[k];
+        const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].x, false);
+        const v2f a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].x, true);
+        const v2f a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].y, false);
+        const v2f a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].y, true);
+        *reinterpret_cast<u32x4 *>(T + row * KP + 8 * c8) =
+            u32x4{pack_f16x2(a0.x * s, a0.y * s), pack_f16x2(a1.x * s, a1.y * s), pack_f16x2(a2.x * s, a2.y * s),
+                  pack_f16x2(a3.x * s, a3.y * s)};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      const int u = tid + NT * k;
+      if (u < 32 * 8)
+        *reinterpret_cast<u32x4 *>(T + (u >> 3) * KP + kF8Nope + 8 * (u & 7)) =
+            u32x4{bf16x2_to_f16x2(rv[k].x), bf16x2_to_f16x2(rv[k].y), bf16x2_to_f16x2(rv[k].z),
+                  bf16x2_to_f16x2(rv[k].w)};
     }
   };
 
@@ -715,8 +741,9 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
         if (tid == 0) rflag[(it + 1) & 1] = 0;
         __syncthreads();   // raw tile+1 landed, this tile fully read, flags visible
         if (rflag[it & 1]) { restart = true; break; }
-        if (tile + 1 < tile_hi) convert(odd ? 0 : 1, odd ? T0 : T1);
+        // raw buffer `odd` was decoded last iteration: refill it first, then decode the other
         if (tile + 2 < tile_hi) gather_raw(tile + 2, odd ? 1 : 0);
+        if (tile + 1 < tile_hi) convert(odd ? 0 : 1, odd ? T0 : T1);
         // make the decoded tile visible without waiting for the gather just issued
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();

@@ -472,21 +472,36 @@ __device__ void tk_select(uint32_t (&k)[KPT], int kk, TkLds &L, Emit emit) {
     hb = shift;
     if (grp == want) break;   // the whole boundary group is taken
   }
+  // Positions 4*(tid + 256q) + e (e < 4) of a thread share bitmap word
+  // (tid + 256q) >> 3, bits 4*(tid & 7) + e: one atomic per group of four, and
+  // the rank lookups load each word once.
+  const int sh4 = 4 * (tid & 7);
   // 3. ties at the boundary: lowest positions first
   uint64_t take_eq = ~0ull;
   if (grp != want) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint32_t x = k[j];
-      if (x && (x & mask) == prefix) atomicOr(&L.bm[tk_pos(j) >> 5], 1u << (tk_pos(j) & 31));
+    for (int q = 0; q < KPT / 4; ++q) {
+      uint32_t m4 = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = k[4 * q + e];
+        m4 |= (x && (x & mask) == prefix) ? 1u << e : 0u;
+      }
+      if (m4) atomicOr(&L.bm[(tid + 256 * q) >> 3], m4 << sh4);
     }
     __syncthreads();
     tk_word_prefix(L, NW, L.sh + 24);
     take_eq = 0ull;
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const uint32_t x = k[j];
-      if (x && (x & mask) == prefix && tk_rank(L, tk_pos(j)) < want) take_eq |= 1ull << j;
+    for (int q = 0; q < KPT / 4; ++q) {
+      const int w = (tid + 256 * q) >> 3;
+      const uint32_t base = L.wpre[w], bits = L.bm[w];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = k[4 * q + e];
+        if (x && (x & mask) == prefix && base + __popc(bits & ((1u << (sh4 + e)) - 1u)) < want)
+          take_eq |= 1ull << (4 * q + e);
+      }
     }
     __syncthreads();
     for (int w = tid; w < NW; w += 256) L.bm[w] = 0u;
@@ -495,20 +510,33 @@ __device__ void tk_select(uint32_t (&k)[KPT], int kk, TkLds &L, Emit emit) {
   // 4. selection bitmap -> ranks
   uint64_t selm = 0ull;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const uint32_t x = k[j];
-    const uint32_t xm = x & mask;
-    if (x && (xm > prefix || (xm == prefix && ((take_eq >> j) & 1ull)))) {
-      selm |= 1ull << j;
-      atomicOr(&L.bm[tk_pos(j) >> 5], 1u << (tk_pos(j) & 31));
+  for (int q = 0; q < KPT / 4; ++q) {
+    uint32_t m4 = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 4 * q + e;
+      const uint32_t x = k[j];
+      const uint32_t xm = x & mask;
+      if (x && (xm > prefix || (xm == prefix && ((take_eq >> j) & 1ull)))) {
+        m4 |= 1u << e;
+        selm |= 1ull << j;
+      }
     }
+    if (m4) atomicOr(&L.bm[(tid + 256 * q) >> 3], m4 << sh4);
   }
   __syncthreads();
   tk_word_prefix(L, NW, L.sh + 28);
+  uint32_t wbits[KPT / 4], wbase[KPT / 4];
+#pragma unroll
+  for (int q = 0; q < KPT / 4; ++q) {
+    const int w = (tid + 256 * q) >> 3;
+    wbits[q] = L.bm[w];
+    wbase[q] = L.wpre[w];
+  }
 #pragma unroll
   for (int j = 0; j < KPT; ++j)
     if ((selm >> j) & 1ull) {
-      const uint32_t rank = tk_rank(L, tk_pos(j));
+      const uint32_t rank = wbase[j >> 2] + __popc(wbits[j >> 2] & ((1u << (sh4 + (j & 3))) - 1u));
       if (rank < (uint32_t)kk) emit((int)rank, j, k[j] + kmin - 1u);
     }
 }
