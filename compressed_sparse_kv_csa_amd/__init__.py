@@ -22,8 +22,8 @@ DSV4_F32, DSV4_BF16, DSV4_FP8R, DSV4_MXFP4, DSV4_F16 = 0, 1, 2, 3, 4
 DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, -4
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
-           "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_last_error",
-           "dsv4_version"]
+           "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant",
+           "dsv4_last_error", "dsv4_version"]
 
 
 class Dsv4Error(RuntimeError):
@@ -65,6 +65,7 @@ def lib():
         L.dsv4_attn_workspace.restype = SZ
         L.dsv4_sparse_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, P, I32, P, F, I32, D, P, I32, P, SZ, P]
         L.dsv4_hca_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, I32, P, F, I32, D, P, I32, P, SZ, P]
+        L.dsv4_set_batch_invariant.argtypes = [I32]
         L.dsv4_last_error.restype = ctypes.c_char_p
         L.dsv4_version.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -261,6 +262,12 @@ def dsv4_hca_attn(q: QueryRows, qv: torch.Tensor, window: Optional[RowStore], W:
                                ctypes.byref(pc) if pc is not None else None, m, _ptr(sinks), float(sm_scale),
                                rope_dim, float(rope_theta), _ptr(out), _code(out), _ptr(ws), nbytes, _stream()))
     return out
+
+
+def dsv4_set_batch_invariant(on: bool) -> bool:
+    """Fixed per-query reduction order whatever the batch (see include/dsv4.h).
+    Returns the previous setting."""
+    return bool(lib().dsv4_set_batch_invariant(int(bool(on))))
 
 
 def dsv4_last_error() -> str:

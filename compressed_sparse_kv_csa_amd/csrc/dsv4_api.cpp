@@ -40,6 +40,7 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
                       float *score_out, void *ws, hipStream_t st);
 int attn_nsplit(int T, int64_t max_rows);
 size_t attn_ws(int T, int H, int D, int64_t max_rows);
+int set_batch_invariant(bool on);
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
                 const dsv4_rows *pool, const int32_t *idx, int topk, int m, int csa, const float *sinks,
                 float sm_scale, int rope_dim, double theta, void *out, int out_dtype, void *ws, int64_t max_rows,
@@ -83,6 +84,8 @@ extern "C" {
 const char *dsv4_last_error(void) { return g_err; }
 
 const char *dsv4_version(void) { return "dsv4-gfx950 0.1"; }
+
+int dsv4_set_batch_invariant(int32_t on) { return dsv4host::set_batch_invariant(on != 0); }
 
 int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *pos_bias, int32_t n_seq,
                   int32_t seq_len, int32_t dim, int32_t m, int32_t overlap, int32_t rope_dim, double rope_theta,

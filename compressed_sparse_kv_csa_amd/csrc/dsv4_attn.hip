@@ -32,6 +32,8 @@
 // k_attn_f32: scalar fp32 path for small fp32 shapes.
 #include "dsv4_common.h"
 
+#include <atomic>
+
 namespace dsv4 {
 
 struct RowSrc {
@@ -1002,11 +1004,17 @@ static RowSrc mk_src(const dsv4_rows *rw) {
   return s;
 }
 
+static std::atomic<int> g_batch_invariant{0};
+
+int set_batch_invariant(bool on) { return g_batch_invariant.exchange(on ? 1 : 0); }
+
 // Splits per query (decode): enough workgroups to occupy the chip, but at least
 // four 32-row tiles per split, because every split writes a 64 x 512 fp32
 // partial that the combine kernel reads back.
 int attn_nsplit(int T, int64_t max_rows) {
   const int64_t tiles = (max_rows + 31) / 32;
+  // batch-invariant mode: one workgroup reduces a query's rows in one order
+  if (g_batch_invariant.load(std::memory_order_relaxed)) return 1;
   if (T >= 512 || tiles < 8) return 1;
   int64_t want = (256 + T - 1) / T;
   const int64_t cap = tiles / 4;

@@ -186,6 +186,18 @@ int dsv4_hca_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_
                   double rope_theta, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
                   hipStream_t stream);
 
+/* dsv4_set_batch_invariant -- fixed reduction order across batch compositions
+ * (DeepSeek-V4 review page, "Muon and MoE system": a token's result must be
+ * bitwise the same whatever batch it is computed in).  on = 1: every query row
+ * of the attention calls is reduced by one workgroup in one fixed order (no
+ * split over its rows, whose count would depend on the batch size), so its
+ * output does not depend on the other rows of the call.  The indexer scores,
+ * top-k, compressor and rope are batch-invariant in either mode (one fixed
+ * per-entry order; the choice among scoring kernels does not change it).
+ * Process-wide; affects calls (and dsv4_attn_workspace sizes) made after it.
+ * Returns the previous setting. */
+int dsv4_set_batch_invariant(int32_t on);
+
 /* Thread-local description of the last error (empty string after success). */
 const char *dsv4_last_error(void);
 

@@ -136,3 +136,17 @@ def test_workspace_sizes(K):
     assert L.dsv4_attn_workspace(8192, 64, 512, 640) == 0          # prefill: no split partials
     assert L.dsv4_attn_workspace(8, 64, 512, 8320) > 8 * 64 * 512 * 4
     assert L.dsv4_index_topk_workspace(8, 262144, 1024) >= 8 * 262144 * 4
+
+
+def test_batch_invariant_switch(K):
+    """The mode switch returns the previous setting; in batch-invariant mode a
+    short decode batch needs no split workspace (one workgroup per query)."""
+    L = K.lib()
+    prev = K.dsv4_set_batch_invariant(True)
+    try:
+        assert K.dsv4_set_batch_invariant(True) is True
+        assert L.dsv4_attn_workspace(32, 64, 512, 640) == 0
+        assert K.dsv4_set_batch_invariant(False) is True
+        assert L.dsv4_attn_workspace(32, 64, 512, 640) > 0
+    finally:
+        K.dsv4_set_batch_invariant(prev)
