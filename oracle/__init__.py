@@ -74,6 +74,8 @@ def _L():
         _lib.or_f16_to_f64.restype = D
         _lib.or_e8m0_to_f64.argtypes = [ctypes.c_uint8]
         _lib.or_e8m0_to_f64.restype = D
+        _lib.or_quantize_fp8r.argtypes = [I64, I, I, P, P, P]
+        _lib.or_quantize_mxfp4.argtypes = [I64, I, P, P, P]
         _lib.or_num_threads.restype = I
         _lib.or_set_num_threads.argtypes = [I]
     return _lib
@@ -126,6 +128,33 @@ def decode(rows) -> np.ndarray:
     _L().or_decode(data.ctypes.data, _KIND[rows.kind], B * n, rows.dim, rows.tail,
                    _p(rs), _p(bs), out.ctypes.data)
     return out.reshape(B, n, rows.dim)
+
+
+# ---------------------------------------------------------------- encoders
+def quantize_fp8r(x: np.ndarray, tail: int):
+    """Q1 -- FP8 KV row storage (insight.ai.kr deep dive: FP8 cache, RoPE
+    channels in BF16).  x [..., dim] float32 (values taken as fp32).
+    Returns (rows [..., (dim-tail) + 2*tail] uint8, scales [...] float32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    dim = x.shape[-1]
+    n = x.size // dim
+    rows = np.empty((n, (dim - tail) + 2 * tail), np.uint8)
+    sc = np.empty(n, np.float32)
+    _L().or_quantize_fp8r(n, dim, tail, x.ctypes.data, rows.ctypes.data, sc.ctypes.data)
+    return rows.reshape(*x.shape[:-1], -1), sc.reshape(x.shape[:-1])
+
+
+def quantize_mxfp4(x: np.ndarray):
+    """Q2 -- MXFP4 (MarkTechPost: FP4 on the indexer query/key path).
+    x [..., dim] float32, dim % 32 == 0.  Returns (nibbles [..., dim/2] uint8,
+    E8M0 scales [..., dim/32] uint8)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    dim = x.shape[-1]
+    n = x.size // dim
+    rows = np.empty((n, dim // 2), np.uint8)
+    sc = np.empty((n, dim // 32), np.uint8)
+    _L().or_quantize_mxfp4(n, dim, x.ctypes.data, rows.ctypes.data, sc.ctypes.data)
+    return rows.reshape(*x.shape[:-1], -1), sc.reshape(*x.shape[:-1], -1)
 
 
 # ---------------------------------------------------------------- wrapped steps

@@ -406,5 +406,112 @@ void or_attn(int n_q, const int32_t *q_seq, const int32_t *q_tok, const int64_t 
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Q1/Q2: storage encoders for quantise-on-write (insight.ai.kr deep dive:  */
+/* the KV cache is FP8 with the RoPE channels kept in BF16; MarkTechPost:    */
+/* the indexer's query/key path is MXFP4).  The pages give the formats, not  */
+/* the scale recipe; the readings here: FP8 rows take one fp32 scale         */
+/* s = amax/448 over the E4M3 channels (s = 1 for an all-zero row), codes    */
+/* are the E4M3 value nearest to x/s (ties to the even code, the sign of     */
+/* x/s kept, 448 at most); MXFP4 blocks of 32 take the OCP MX scale          */
+/* 2^(floor(log2 amax) - 2) (2^-127 for an all-zero block, exponent clamped  */
+/* to [-127, 127]), codes are the E2M1 value nearest to x/scale, saturated   */
+/* at 6, ties to the even code, no negative zero.  The scale and x/s are     */
+/* formed in fp32, the precision the GPU kernel decides them in; the nearest */
+/* code is then found by searching every code of the format.                 */
+/* ------------------------------------------------------------------------ */
+static uint8_t nearest_e4m3(float v) {
+  const int neg = signbit(v) ? 1 : 0;
+  double best = INFINITY;
+  int c, code = 0;
+  for (c = 0; c < 127; c++) {   /* magnitudes 0x00..0x7E (0x7F is NaN) */
+    const double d = fabs(fabs((double)v) - or_e4m3_to_f64((uint8_t)c));
+    if (d < best || (d == best && (c & 1) == 0)) {
+      best = d;
+      code = c;
+    }
+  }
+  return (uint8_t)(code | (neg << 7));
+}
+
+static uint8_t nearest_e2m1(double v) {
+  const double a = fabs(v) > 6.0 ? 6.0 : fabs(v);
+  double best = INFINITY;
+  int c, code = 0;
+  for (c = 0; c < 8; c++) {
+    const double d = fabs(a - or_e2m1_to_f64((uint8_t)c));
+    if (d < best || (d == best && (c & 1) == 0)) {
+      best = d;
+      code = c;
+    }
+  }
+  if (code != 0 && v < 0) code |= 8;
+  return (uint8_t)code;
+}
+
+/* x: n rows of dim fp32 values.  rows: n x ((dim - tail) + 2 tail) bytes;
+ * scales: n fp32. */
+void or_quantize_fp8r(int64_t n, int dim, int tail, const float *x, uint8_t *rows, float *scales) {
+  int64_t i;
+  const int64_t rb = (int64_t)(dim - tail) + 2LL * tail;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < n; i++) {
+    const float *xr = x + i * dim;
+    uint8_t *o = rows + i * rb;
+    float amax = 0.f, s;
+    int d;
+    for (d = 0; d < dim - tail; d++)
+      if (fabsf(xr[d]) > amax) amax = fabsf(xr[d]);
+    s = amax > 0.f ? amax / 448.0f : 1.0f;
+    scales[i] = s;
+    for (d = 0; d < dim - tail; d++) o[d] = nearest_e4m3(xr[d] / s);
+    for (d = 0; d < tail; d++) {   /* bf16: the nearer of the two neighbours, ties to even */
+      const double v = (double)xr[dim - tail + d];
+      uint32_t u;
+      uint16_t lo, hi, h;
+      memcpy(&u, &xr[dim - tail + d], 4);
+      lo = (uint16_t)(u >> 16);   /* truncation: same sign, magnitude just below (or equal) */
+      hi = (uint16_t)(lo + 1);
+      {
+        const double dl = fabs(v - or_bf16_to_f64(lo)), dh = fabs(v - or_bf16_to_f64(hi));
+        h = (dl < dh || (dl == dh && (lo & 1) == 0)) ? lo : hi;
+      }
+      memcpy(o + (dim - tail) + 2 * d, &h, 2);
+    }
+  }
+}
+
+/* x: n rows of dim fp32 values (dim a multiple of 32).  rows: n x dim/2 bytes
+ * (low nibble = even element); scales: n x dim/32 E8M0 bytes. */
+void or_quantize_mxfp4(int64_t n, int dim, const float *x, uint8_t *rows, uint8_t *scales) {
+  int64_t i;
+#pragma omp parallel for schedule(static)
+  for (i = 0; i < n; i++) {
+    int blk, d;
+    for (blk = 0; blk < dim / 32; blk++) {
+      const float *xb = x + i * dim + 32 * blk;
+      float amax = 0.f;
+      int e;
+      for (d = 0; d < 32; d++)
+        if (fabsf(xb[d]) > amax) amax = fabsf(xb[d]);
+      if (amax > 0.f) {
+        int k;
+        frexp((double)amax, &k);   /* amax = f 2^k, f in [0.5, 1): floor(log2 amax) = k - 1 */
+        e = k - 1 - 2;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+      } else {
+        e = -127;
+      }
+      scales[i * (dim / 32) + blk] = (uint8_t)(e + 127);
+      for (d = 0; d < 32; d += 2) {
+        const uint8_t lo = nearest_e2m1(ldexp((double)xb[d], -e));
+        const uint8_t hi = nearest_e2m1(ldexp((double)xb[d + 1], -e));
+        rows[i * (dim / 2) + 16 * blk + d / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
 int or_num_threads(void) { return omp_get_max_threads(); }
 void or_set_num_threads(int n) { omp_set_num_threads(n); }
