@@ -23,7 +23,7 @@ DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, 
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
            "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant",
-           "dsv4_last_error", "dsv4_version"]
+           "dsv4_quantize", "dsv4_last_error", "dsv4_version"]
 
 
 class Dsv4Error(RuntimeError):
@@ -66,6 +66,7 @@ def lib():
         L.dsv4_sparse_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, P, I32, P, F, I32, D, P, I32, P, SZ, P]
         L.dsv4_hca_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, I32, P, F, I32, D, P, I32, P, SZ, P]
         L.dsv4_set_batch_invariant.argtypes = [I32]
+        L.dsv4_quantize.argtypes = [P, I32, I64, I32, I32, P, P, P, I32, P]
         L.dsv4_last_error.restype = ctypes.c_char_p
         L.dsv4_version.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -262,6 +263,27 @@ def dsv4_hca_attn(q: QueryRows, qv: torch.Tensor, window: Optional[RowStore], W:
                                ctypes.byref(pc) if pc is not None else None, m, _ptr(sinks), float(sm_scale),
                                rope_dim, float(rope_theta), _ptr(out), _code(out), _ptr(ws), nbytes, _stream()))
     return out
+
+
+def dsv4_quantize(x: torch.Tensor, out_dtype: int, tail: int = 0):
+    """Quantise rows x [..., dim] (float32 / bfloat16 / float16) for storage.
+    DSV4_FP8R -> (rows uint8 [..., (dim-tail) + 2*tail], row scales float32 [...]);
+    DSV4_MXFP4 -> (nibbles uint8 [..., dim/2], E8M0 block scales uint8 [..., dim/32])."""
+    x = x.contiguous()
+    dim = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    n = x.numel() // dim
+    if out_dtype == DSV4_FP8R:
+        rows = torch.empty(lead + ((dim - tail) + 2 * tail,), dtype=torch.uint8, device=x.device)
+        sc = torch.empty(lead, dtype=torch.float32, device=x.device)
+        _check(lib().dsv4_quantize(_ptr(x), _code(x), n, dim, tail, _ptr(rows), _ptr(sc), None, out_dtype,
+                                   _stream()))
+    else:
+        rows = torch.empty(lead + (dim // 2,), dtype=torch.uint8, device=x.device)
+        sc = torch.empty(lead + (dim // 32,), dtype=torch.uint8, device=x.device)
+        _check(lib().dsv4_quantize(_ptr(x), _code(x), n, dim, tail, _ptr(rows), None, _ptr(sc), out_dtype,
+                                   _stream()))
+    return rows, sc
 
 
 def dsv4_set_batch_invariant(on: bool) -> bool:

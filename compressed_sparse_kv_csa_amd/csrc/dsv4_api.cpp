@@ -41,6 +41,8 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
 int attn_nsplit(int T, int64_t max_rows);
 size_t attn_ws(int T, int H, int D, int64_t max_rows);
 int set_batch_invariant(bool on);
+int launch_quantize(const void *x, int x_dtype, int64_t n, int dim, int tail, void *rows, float *row_scale,
+                    uint8_t *blk_scale, int out_dtype, hipStream_t st);
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
                 const dsv4_rows *pool, const int32_t *idx, int topk, int m, int csa, const float *sinks,
                 float sm_scale, int rope_dim, double theta, void *out, int out_dtype, void *ws, int64_t max_rows,
@@ -84,6 +86,26 @@ extern "C" {
 const char *dsv4_last_error(void) { return g_err; }
 
 const char *dsv4_version(void) { return "dsv4-gfx950 0.1"; }
+
+int dsv4_quantize(const void *x, int32_t x_dtype, int64_t n_rows, int32_t dim, int32_t tail, void *rows_out,
+                  float *row_scale_out, uint8_t *blk_scale_out, int32_t out_dtype, hipStream_t stream) {
+  if (n_rows < 0) return fail(DSV4_EINVAL, "quantize: n_rows %lld", (long long)n_rows);
+  if (x_dtype != DSV4_F32 && x_dtype != DSV4_BF16 && x_dtype != DSV4_F16)
+    return fail(DSV4_ENOTSUP, "quantize: input dtype %d", x_dtype);
+  if (dim < 64 || dim > 512 || dim % 64) return fail(DSV4_ENOTSUP, "quantize: dim %d (64..512, multiple of 64)", dim);
+  if (out_dtype == DSV4_FP8R) {
+    if (tail < 0 || tail >= dim || (tail & 1)) return fail(DSV4_EINVAL, "quantize: tail %d", tail);
+    if (n_rows > 0 && (!x || !rows_out || !row_scale_out)) return fail(DSV4_EINVAL, "quantize: NULL x/rows/row_scale");
+  } else if (out_dtype == DSV4_MXFP4) {
+    if (tail != 0) return fail(DSV4_EINVAL, "quantize: MXFP4 takes no bf16 tail (tail %d)", tail);
+    if (n_rows > 0 && (!x || !rows_out || !blk_scale_out)) return fail(DSV4_EINVAL, "quantize: NULL x/rows/blk_scale");
+  } else {
+    return fail(DSV4_ENOTSUP, "quantize: output dtype %d (FP8R or MXFP4)", out_dtype);
+  }
+  const int rc = launch_quantize(x, x_dtype, n_rows, dim, tail, rows_out, row_scale_out, blk_scale_out, out_dtype,
+                                 stream);
+  return rc ? rc : ok();
+}
 
 int dsv4_set_batch_invariant(int32_t on) { return dsv4host::set_batch_invariant(on != 0); }
 

@@ -186,6 +186,26 @@ int dsv4_hca_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_
                   double rope_theta, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
                   hipStream_t stream);
 
+/* dsv4_quantize -- quantise rows for storage (quantise-on-write of the decode
+ * caches).  insight.ai.kr deep dive: the KV cache is FP8 with the RoPE
+ * channels in BF16; MarkTechPost summary: the indexer's query/key path is
+ * MXFP4.  Scale recipes (the pages give only the formats):
+ *   DSV4_FP8R : per row s = amax/448 over channels [0, dim-tail) (1 for an
+ *               all-zero row), code = E4M3 value nearest to x/s (ties to even,
+ *               saturated at 448); channels [dim-tail, dim) as bf16 (round to
+ *               nearest even).  rows_out [n_rows, (dim-tail) + 2*tail] bytes,
+ *               row_scale_out [n_rows] float32.
+ *   DSV4_MXFP4: per 32-channel block scale 2^(floor(log2 amax) - 2) (2^-127 for
+ *               an all-zero block) as E8M0, code = E2M1 value nearest to
+ *               x/scale (ties to even, saturated at 6, no negative zero).
+ *               rows_out [n_rows, dim/2] bytes (low nibble = even channel),
+ *               blk_scale_out [n_rows, dim/32]; tail must be 0.
+ *   x : [n_rows, dim] in x_dtype (DSV4_F32, DSV4_BF16 or DSV4_F16), device.
+ * Supported: dim a multiple of 64, at most 512; 0 <= tail < dim, tail even. */
+int dsv4_quantize(const void *x, int32_t x_dtype, int64_t n_rows, int32_t dim, int32_t tail,
+                  void *rows_out, float *row_scale_out, uint8_t *blk_scale_out, int32_t out_dtype,
+                  hipStream_t stream);
+
 /* dsv4_set_batch_invariant -- fixed reduction order across batch compositions
  * (DeepSeek-V4 review page, "Muon and MoE system": a token's result must be
  * bitwise the same whatever batch it is computed in).  on = 1: every query row

@@ -150,3 +150,15 @@ def test_batch_invariant_switch(K):
         assert L.dsv4_attn_workspace(32, 64, 512, 640) > 0
     finally:
         K.dsv4_set_batch_invariant(prev)
+
+
+def test_quantize_rejects_bad_args(K):
+    L = K.lib()
+    fake = ctypes.c_void_p(0x1000)
+    assert _rc(L.dsv4_quantize(fake, 0, 4, 512, 64, fake, fake, None, K.DSV4_BF16, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_quantize(fake, 0, 4, 500, 64, fake, fake, None, K.DSV4_FP8R, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_quantize(fake, 0, 4, 512, 63, fake, fake, None, K.DSV4_FP8R, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_quantize(fake, 0, 4, 512, 0, fake, None, None, K.DSV4_FP8R, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_quantize(fake, 0, 4, 128, 32, fake, None, fake, K.DSV4_MXFP4, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_quantize(fake, 9, 4, 128, 0, fake, None, fake, K.DSV4_MXFP4, None)) == K.DSV4_ENOTSUP
+    assert _rc(L.dsv4_quantize(None, 0, 0, 128, 0, None, None, None, K.DSV4_MXFP4, None)) == K.DSV4_OK
