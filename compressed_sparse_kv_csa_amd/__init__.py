@@ -23,7 +23,7 @@ DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, 
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
            "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant",
-           "dsv4_quantize", "dsv4_last_error", "dsv4_version"]
+           "dsv4_quantize", "dsv4_cache_append", "dsv4_last_error", "dsv4_version"]
 
 
 class Dsv4Error(RuntimeError):
@@ -40,7 +40,24 @@ class Queries(ctypes.Structure):
 class Rows(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("row_scale", ctypes.c_void_p), ("blk_scale", ctypes.c_void_p),
                 ("dtype", ctypes.c_int32), ("dim", ctypes.c_int32), ("tail", ctypes.c_int32),
-                ("seq_stride", ctypes.c_int64), ("count", ctypes.c_void_p), ("first_tok", ctypes.c_void_p)]
+                ("seq_stride", ctypes.c_int64), ("count", ctypes.c_void_p), ("first_tok", ctypes.c_void_p),
+                ("ring", ctypes.c_int32)]
+
+
+class Stream(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("pos_bias", ctypes.c_void_p),
+                ("buf", ctypes.c_void_p), ("pool", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
+                ("blk_scale", ctypes.c_void_p), ("pool_dtype", ctypes.c_int32), ("tail", ctypes.c_int32),
+                ("pool_cap", ctypes.c_int64), ("count", ctypes.c_void_p)]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("m", ctypes.c_int32), ("overlap", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double), ("pos0", ctypes.c_void_p), ("len", ctypes.c_void_p),
+                ("win", ctypes.c_void_p), ("win_scale", ctypes.c_void_p), ("win_dtype", ctypes.c_int32),
+                ("win_tail", ctypes.c_int32), ("win_cap", ctypes.c_int32), ("win_dim", ctypes.c_int32),
+                ("win_rope_dim", ctypes.c_int32), ("win_count", ctypes.c_void_p), ("win_first", ctypes.c_void_p),
+                ("kv", Stream), ("idx", Stream)]
 
 
 _lib = None
@@ -67,6 +84,7 @@ def lib():
         L.dsv4_hca_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, I32, P, F, I32, D, P, I32, P, SZ, P]
         L.dsv4_set_batch_invariant.argtypes = [I32]
         L.dsv4_quantize.argtypes = [P, I32, I64, I32, I32, P, P, P, I32, P]
+        L.dsv4_cache_append.argtypes = [P, I32, P, P, P, P, P, P, I32, P]
         L.dsv4_last_error.restype = ctypes.c_char_p
         L.dsv4_version.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -142,6 +160,7 @@ class RowStore:
     row_scale: Optional[torch.Tensor] = None  # [B, stride] f32
     blk_scale: Optional[torch.Tensor] = None  # [B, stride, dim/32] u8
     first_tok: Optional[torch.Tensor] = None  # [B] int32
+    ring: bool = False                        # window ring: token j at row j mod stride
 
     @property
     def stride(self) -> int:
@@ -149,7 +168,103 @@ class RowStore:
 
     def c(self) -> Rows:
         return Rows(_ptr(self.data), _ptr(self.row_scale), _ptr(self.blk_scale), self.dtype, self.dim,
-                    self.tail, self.stride, _ptr(self.count), _ptr(self.first_tok))
+                    self.tail, self.stride, _ptr(self.count), _ptr(self.first_tok), 1 if self.ring else 0)
+
+
+def row_bytes(dtype: int, dim: int, tail: int = 0) -> int:
+    """Bytes of one stored row (see the storage types in include/dsv4.h)."""
+    return {DSV4_F32: 4 * dim, DSV4_BF16: 2 * dim, DSV4_F16: 2 * dim,
+            DSV4_FP8R: (dim - tail) + 2 * tail, DSV4_MXFP4: dim // 2}[dtype]
+
+
+class DecodeCache:
+    """Device state of one compressed-attention layer's cache (dsv4_cache in
+    include/dsv4.h): token counts, the window ring of K=V rows and one
+    (HCA) or two (CSA: K=V and indexer keys) compressed streams, each with
+    its buffer of the newest tokens, pool and count.  Tensors are allocated
+    here (torch, device memory); every update runs in dsv4_cache_append."""
+
+    def __init__(self, n_seq: int, m: int, overlap: bool, kv_dim: int, kv_bias: torch.Tensor, pool_cap: int,
+                 win_cap: int, rope_dim: int = 0, rope_theta: float = 10000.0, kv_dtype: int = DSV4_FP8R,
+                 kv_tail: int = 0, win_dtype: Optional[int] = None, idx_dim: int = 0,
+                 idx_bias: Optional[torch.Tensor] = None, idx_dtype: int = DSV4_MXFP4,
+                 pos0: Optional[torch.Tensor] = None, device="cuda"):
+        span = 2 * m if overlap else m
+        self.n_seq, self.m, self.overlap, self.span = n_seq, m, bool(overlap), span
+        self.rope_theta, self.pos0 = float(rope_theta), pos0
+        i32 = dict(dtype=torch.int32, device=device)
+        self.len = torch.zeros(n_seq, **i32)
+        self.win_dtype = kv_dtype if win_dtype is None else win_dtype
+        self.win_tail = kv_tail if self.win_dtype == DSV4_FP8R else 0
+        self.win_cap, self.kv_dim, self.rope_dim = win_cap, kv_dim, rope_dim
+        self.win = torch.zeros(n_seq, max(win_cap, 1), row_bytes(self.win_dtype, kv_dim, self.win_tail),
+                               dtype=torch.uint8, device=device)
+        self.win_scale = (torch.zeros(n_seq, max(win_cap, 1), dtype=torch.float32, device=device)
+                          if self.win_dtype == DSV4_FP8R else None)
+        self.win_count = torch.zeros(n_seq, **i32)
+        self.win_first = torch.zeros(n_seq, **i32)
+        self.kv = self._stream(kv_dim, rope_dim, kv_bias, kv_dtype, kv_tail, pool_cap, device)
+        self.idx = (self._stream(idx_dim, 0, idx_bias, idx_dtype, 0, pool_cap, device)
+                    if idx_dim else None)
+
+    def _stream(self, dim, rope_dim, bias, dtype, tail, cap, device):
+        assert bias is not None and tuple(bias.shape) == (self.span, dim) and bias.dtype == torch.float32
+        st = dict(dim=dim, rope_dim=rope_dim, bias=bias.contiguous(), dtype=dtype, tail=tail,
+                  buf=torch.zeros(self.n_seq, self.span, 2, dim, dtype=torch.float32, device=device),
+                  pool=torch.zeros(self.n_seq, max(cap, 1), row_bytes(dtype, dim, tail), dtype=torch.uint8,
+                                   device=device),
+                  row_scale=(torch.zeros(self.n_seq, max(cap, 1), dtype=torch.float32, device=device)
+                             if dtype == DSV4_FP8R else None),
+                  blk_scale=(torch.zeros(self.n_seq, max(cap, 1), dim // 32, dtype=torch.uint8, device=device)
+                             if dtype == DSV4_MXFP4 else None),
+                  cap=cap, count=torch.zeros(self.n_seq, dtype=torch.int32, device=device))
+        return st
+
+    @staticmethod
+    def _c_stream(st) -> Stream:
+        if st is None:
+            return Stream()
+        return Stream(st["dim"], st["rope_dim"], _ptr(st["bias"]), _ptr(st["buf"]), _ptr(st["pool"]),
+                      _ptr(st["row_scale"]), _ptr(st["blk_scale"]), st["dtype"], st["tail"], st["cap"],
+                      _ptr(st["count"]))
+
+    def c(self) -> Cache:
+        return Cache(self.n_seq, self.m, 1 if self.overlap else 0, self.rope_theta, _ptr(self.pos0),
+                     _ptr(self.len), _ptr(self.win), _ptr(self.win_scale), self.win_dtype, self.win_tail,
+                     self.win_cap, self.kv_dim, self.rope_dim, _ptr(self.win_count), _ptr(self.win_first),
+                     self._c_stream(self.kv), self._c_stream(self.idx))
+
+    def append(self, kv: Optional[torch.Tensor], kv_c: torch.Tensor, kv_z: torch.Tensor,
+               idx_c: Optional[torch.Tensor] = None, idx_z: Optional[torch.Tensor] = None,
+               n_new: Optional[torch.Tensor] = None, stream=None) -> None:
+        """dsv4_cache_append: inputs [B, n, dim], all float32 or all bfloat16;
+        n_new [B] int32 (tokens taken per sequence, <= n) or None."""
+        B, n, _ = kv_c.shape
+        assert B == self.n_seq
+        ins = [t for t in (kv, kv_c, kv_z, idx_c, idx_z) if t is not None]
+        code = _code(kv_c)
+        for t in ins:
+            assert t.dtype == kv_c.dtype and t.shape[:2] == (B, n), "inputs: one dtype, shape [B, n, dim]"
+        cs = self.c()
+        _check(lib().dsv4_cache_append(ctypes.byref(cs), n, _ptr(n_new), _ptr(kv), _ptr(kv_c), _ptr(kv_z),
+                                       _ptr(idx_c), _ptr(idx_z), code, _stream(stream)))
+
+    def window(self) -> RowStore:
+        """The window ring as attention calls read it."""
+        return RowStore(self.win, self.win_dtype, self.kv_dim, self.win_count, tail=self.win_tail,
+                        row_scale=self.win_scale, first_tok=self.win_first, ring=True)
+
+    @staticmethod
+    def _pool(st) -> RowStore:
+        return RowStore(st["pool"], st["dtype"], st["dim"], st["count"], tail=st["tail"],
+                        row_scale=st["row_scale"], blk_scale=st["blk_scale"])
+
+    def kv_pool(self) -> RowStore:
+        return self._pool(self.kv)
+
+    def idx_pool(self) -> RowStore:
+        assert self.idx is not None, "this cache has no indexer stream"
+        return self._pool(self.idx)
 
 
 # ------------------------------------------------------------------ entry points

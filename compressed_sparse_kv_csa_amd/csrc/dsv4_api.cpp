@@ -41,12 +41,47 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
 int attn_nsplit(int T, int64_t max_rows);
 size_t attn_ws(int T, int H, int D, int64_t max_rows);
 int set_batch_invariant(bool on);
+int launch_cache_append(const dsv4_cache *C, int n, const int32_t *n_new, const void *kv, const void *kv_c,
+                        const void *kv_z, const void *idx_c, const void *idx_z, int in_dtype, hipStream_t st);
 int launch_quantize(const void *x, int x_dtype, int64_t n, int dim, int tail, void *rows, float *row_scale,
                     uint8_t *blk_scale, int out_dtype, hipStream_t st);
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
                 const dsv4_rows *pool, const int32_t *idx, int topk, int m, int csa, const float *sinks,
                 float sm_scale, int rope_dim, double theta, void *out, int out_dtype, void *ws, int64_t max_rows,
                 hipStream_t st);
+
+// a stored-row format of the cache writer: dtype, dim and tail
+static int check_store(const char *what, int dtype, int dim, int tail, const void *rsc, const void *bsc, bool mx_ok) {
+  if (dim < 64 || dim > 512 || dim % 64) return fail(DSV4_ENOTSUP, "%s: dim %d (64..512, multiple of 64)", what, dim);
+  switch (dtype) {
+  case DSV4_F32:
+  case DSV4_BF16:
+  case DSV4_F16:
+    if (tail != 0) return fail(DSV4_EINVAL, "%s: tail %d without FP8R", what, tail);
+    return DSV4_OK;
+  case DSV4_FP8R:
+    if (!rsc) return fail(DSV4_EINVAL, "%s: FP8R rows need row scales", what);
+    if (tail < 0 || tail >= dim || tail % 8) return fail(DSV4_ENOTSUP, "%s: FP8R tail %d (multiple of 8, < dim)", what, tail);
+    return DSV4_OK;
+  case DSV4_MXFP4:
+    if (!mx_ok) return fail(DSV4_ENOTSUP, "%s: MXFP4 is a pool format only", what);
+    if (!bsc) return fail(DSV4_EINVAL, "%s: MXFP4 rows need block scales", what);
+    if (tail != 0) return fail(DSV4_EINVAL, "%s: MXFP4 takes no tail", what);
+    return DSV4_OK;
+  }
+  return fail(DSV4_EINVAL, "%s: unknown dtype %d", what, dtype);
+}
+
+static int check_stream(const char *what, const dsv4_stream *s, const void *c, const void *z) {
+  int rc = check_store(what, s->pool_dtype, s->dim, s->tail, s->row_scale, s->blk_scale, true);
+  if (rc) return rc;
+  if (!s->pos_bias || !s->buf || !s->pool || !s->count || s->pool_cap < 0)
+    return fail(DSV4_EINVAL, "%s: NULL pos_bias/buf/pool/count or negative pool_cap", what);
+  if (s->rope_dim < 0 || (s->rope_dim & 1) || s->rope_dim > 64)
+    return fail(DSV4_EINVAL, "%s: rope_dim %d (even, <= 64)", what, s->rope_dim);
+  if (!c || !z) return fail(DSV4_EINVAL, "%s: NULL inputs c/z", what);
+  return DSV4_OK;
+}
 
 static int ok() {
   g_err[0] = 0;
@@ -65,6 +100,8 @@ static int check_rows(const dsv4_rows *r, const char *what, int dim) {
   if ((!r->data && r->seq_stride > 0) || !r->count) return fail(DSV4_EINVAL, "%s: data/count is NULL", what);
   if (r->dim != dim) return fail(DSV4_EINVAL, "%s: dim %d, expected %d", what, r->dim, dim);
   if (r->seq_stride < 0) return fail(DSV4_EINVAL, "%s: negative seq_stride", what);
+  if (r->ring && (!r->first_tok || r->seq_stride < 1))
+    return fail(DSV4_EINVAL, "%s: the ring layout is for windows (first_tok set, seq_stride >= 1)", what);
   if (r->dtype == DSV4_FP8R) {
     if (!r->row_scale && r->seq_stride > 0) return fail(DSV4_EINVAL, "%s: FP8R rows need row_scale", what);
     if (r->tail < 0 || r->tail > dim || (r->tail % 8) != 0 || ((dim - r->tail) % 8) != 0)
@@ -104,6 +141,36 @@ int dsv4_quantize(const void *x, int32_t x_dtype, int64_t n_rows, int32_t dim, i
   }
   const int rc = launch_quantize(x, x_dtype, n_rows, dim, tail, rows_out, row_scale_out, blk_scale_out, out_dtype,
                                  stream);
+  return rc ? rc : ok();
+}
+
+int dsv4_cache_append(const dsv4_cache *C, int32_t n, const int32_t *n_new, const void *kv, const void *kv_c,
+                      const void *kv_z, const void *idx_c, const void *idx_z, int32_t in_dtype, hipStream_t stream) {
+  if (!C) return fail(DSV4_EINVAL, "cache_append: NULL cache");
+  if (C->n_seq < 1 || C->n_seq > 65535 || n < 0)
+    return fail(DSV4_EINVAL, "cache_append: n_seq %d (1..65535), n %d", C->n_seq, n);
+  if (C->m < 1 || C->m > 1024) return fail(DSV4_ENOTSUP, "cache_append: m %d (1..1024)", C->m);
+  if (!C->len) return fail(DSV4_EINVAL, "cache_append: NULL len");
+  if (in_dtype != DSV4_F32 && in_dtype != DSV4_BF16) return fail(DSV4_ENOTSUP, "cache_append: input dtype %d", in_dtype);
+  int rc = check_stream("cache_append: kv stream", &C->kv, kv_c, kv_z);
+  if (rc) return rc;
+  if (C->idx.dim != 0 && (rc = check_stream("cache_append: idx stream", &C->idx, idx_c, idx_z))) return rc;
+  if (C->win_cap < 0) return fail(DSV4_EINVAL, "cache_append: win_cap %d", C->win_cap);
+  if (C->win_cap > 0) {
+    if ((rc = check_store("cache_append: window", C->win_dtype, C->win_dim, C->win_tail, C->win_scale, nullptr, false)))
+      return rc;
+    if (C->win_dim != C->kv.dim) return fail(DSV4_EINVAL, "cache_append: win_dim %d != kv dim %d", C->win_dim, C->kv.dim);
+    if (!C->win || !C->win_count || !C->win_first || !kv)
+      return fail(DSV4_EINVAL, "cache_append: NULL window rows/count/first or kv input");
+    if (C->win_rope_dim < 0 || (C->win_rope_dim & 1) || C->win_rope_dim > 64)
+      return fail(DSV4_EINVAL, "cache_append: win_rope_dim %d (even, <= 64)", C->win_rope_dim);
+  }
+  const bool rot = C->kv.rope_dim > 0 || C->idx.rope_dim > 0 || (C->win_cap > 0 && C->win_rope_dim > 0);
+  if (rot && !(C->rope_theta > 0)) return fail(DSV4_EINVAL, "cache_append: rope_theta must be > 0");
+  const int64_t items = (C->win_cap > 0 ? (int64_t)(n < C->win_cap ? n : C->win_cap) : 0) +
+                        (C->idx.dim ? 2 : 1) * (((int64_t)n + C->m - 1) / C->m);
+  if (items > 0x7fffffff) return fail(DSV4_ENOTSUP, "cache_append: n %d too large for one append", n);
+  rc = launch_cache_append(C, n, n_new, kv, kv_c, kv_z, idx_c, idx_z, in_dtype, stream);
   return rc ? rc : ok();
 }
 
@@ -157,6 +224,7 @@ int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_i
   if (!q_idx || !w || !idx_out) return fail(DSV4_EINVAL, "index_topk: NULL tensor pointer");
   if (m < 1 || topk < 1 || topk > 2048) return fail(DSV4_EINVAL, "index_topk: m %d topk %d (1..2048)", m, topk);
   if ((rc = check_rows(k_pool, "index_topk: k_pool", head_dim))) return rc;
+  if (k_pool->ring) return fail(DSV4_EINVAL, "index_topk: k_pool cannot be a ring");
   if (k_pool->dtype != q_dtype) return fail(DSV4_ENOTSUP, "index_topk: key dtype %d != query dtype %d", k_pool->dtype, q_dtype);
   if (!(score_scale > 0)) return fail(DSV4_EINVAL, "index_topk: score_scale must be > 0");
   if (q_dtype == DSV4_F32) {
@@ -200,6 +268,7 @@ static int attn_common(const char *who, const dsv4_queries *q, const void *qv, i
   if (W > 0 && (rc = check_rows(window, "window", dim))) return rc;
   if (W > 0 && !window->first_tok) return fail(DSV4_EINVAL, "%s: window rows need first_tok", who);
   if (pool_needed && (rc = check_rows(pool, "pool", dim))) return rc;
+  if (pool_needed && pool->ring) return fail(DSV4_EINVAL, "%s: a pool cannot be a ring", who);
   if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
     return fail(DSV4_EINVAL, "%s: rope_dim %d (even, <= min(dim, 64))", who, rope_dim);
   if (rope_dim > 0 && !(rope_theta > 0)) return fail(DSV4_EINVAL, "%s: rope_theta must be > 0", who);
@@ -219,7 +288,6 @@ static int attn_common(const char *who, const dsv4_queries *q, const void *qv, i
     const bool ok_p = !pool_needed || pdt == DSV4_BF16 || pdt == DSV4_FP8R || pdt == DSV4_F16;
     if (!ok_w || !ok_p) return fail(DSV4_ENOTSUP, "%s: bf16 queries need F16, BF16 or FP8R rows", who);
     if (W > 0 && pool_needed && wdt != pdt) return fail(DSV4_ENOTSUP, "%s: window and pool dtypes differ", who);
-    if ((W == 0 && !pool_needed) && false) return DSV4_OK;
   } else {
     return fail(DSV4_ENOTSUP, "%s: query dtype %d", who, q_dtype);
   }

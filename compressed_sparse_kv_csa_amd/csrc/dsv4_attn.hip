@@ -44,6 +44,7 @@ struct RowSrc {
   int64_t stride;
   int64_t rbytes;
   int dtype, tail;
+  int ring;   // windows: token j at row j mod stride
 };
 
 struct AttnArgs {
@@ -91,7 +92,9 @@ __device__ __forceinline__ RowPlan row_plan(const AttnArgs &A, int r) {
     lo = lo < 0 ? 0 : lo;
     int hi = P.t;
     hi = hi > ft + wc - 1 ? ft + wc - 1 : hi;
-    P.wlo = lo - ft;   // storage row of the first window token
+    // storage row of the first window token; the rows of the later ones
+    // follow it, wrapping at the stride (only a ring ever wraps)
+    P.wlo = A.win.ring ? (int)(lo % A.win.stride) : lo - ft;
     P.nwin = hi >= lo ? hi - lo + 1 : 0;
   }
   P.nsel = 0;
@@ -141,10 +144,16 @@ __device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cn
   return total;
 }
 
+// storage row (within its sequence) of window row i of a query
+__device__ __forceinline__ int win_slot(const AttnArgs &A, const RowPlan &P, int i) {
+  const int s = P.wlo + i;
+  return s >= A.win.stride ? s - (int)A.win.stride : s;
+}
+
 __device__ __forceinline__ const uint8_t *row_ptr(const AttnArgs &A, const RowPlan &P, const int *sel, int i,
                                                   float *scale) {
   if (i < P.nwin) {
-    const int64_t g = (int64_t)P.b * A.win.stride + P.wlo + i;
+    const int64_t g = (int64_t)P.b * A.win.stride + win_slot(A, P, i);
     *scale = A.win.rscale ? A.win.rscale[g] : 1.f;
     return A.win.data + g * A.win.rbytes;
   }
@@ -453,18 +462,18 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
   const int nwin = P.nwin, csa = A.csa;
   // row addressing in scalars: window rows first, then pool rows
   const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * RB : nullptr;
-  const uint8_t *wbase = A.win.data ? A.win.data + ((int64_t)P.b * A.win.stride + P.wlo) * RB : pbase;
+  const uint8_t *wbase = A.win.data ? A.win.data + (int64_t)P.b * A.win.stride * RB : pbase;
   const float *psc = FP8 && A.pool.data ? A.pool.rscale + (int64_t)P.b * A.pool.stride : nullptr;
-  const float *wsc = FP8 && A.win.data ? A.win.rscale + (int64_t)P.b * A.win.stride + P.wlo : psc;
+  const float *wsc = FP8 && A.win.data ? A.win.rscale + (int64_t)P.b * A.win.stride : psc;
 
-  // Row ids: window index (>= 0) or -1 - pool entry.  Positions past the end of
+  // Row ids: window storage row (>= 0) or -1 - pool entry.  Positions past the end of
   // the list are clamped to its last row, so every gathered tile row holds
   // finite stored values (their probabilities are zero) and no buffer needs
   // clearing.  nrows is provisional (window + HCA rows) until CSA compaction.
   int nrows = nwin + P.nsel;
   auto row_id = [&](int i) -> int {
     i = min(i, nrows - 1);
-    return i < nwin ? i : -1 - (csa ? sel[i - nwin] : i - nwin);
+    return i < nwin ? win_slot(A, P, i) : -1 - (csa ? sel[i - nwin] : i - nwin);
   };
   constexpr int RPW = (32 + NW - 1) / NW;   // tile rows per wave (wave w: rows w, w+NW, ...)
   auto tile_ids = [&](int tile) -> int {    // lane k < RPW: id of row wv + NW*k of the tile
@@ -994,6 +1003,7 @@ static RowSrc mk_src(const dsv4_rows *rw) {
   s.stride = rw->seq_stride;
   s.dtype = rw->dtype;
   s.tail = rw->tail;
+  s.ring = rw->ring ? 1 : 0;
   switch (rw->dtype) {
   case DSV4_F32: s.rbytes = 4LL * rw->dim; break;
   case DSV4_BF16: s.rbytes = 2LL * rw->dim; break;

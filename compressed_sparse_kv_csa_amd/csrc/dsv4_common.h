@@ -68,10 +68,81 @@ __device__ __forceinline__ void rope_cs(double pos, int pair, int rope_dim, doub
   rope_cs_f(pos, pow(theta, -2.0 * (double)pair / (double)rope_dim), sign, c, s);
 }
 
+// Rotate one interleaved rope pair by the angle whose (cos, sin) is (cs, sn).
+// Written with explicit fmaf so that every kernel that rotates (the rope
+// kernel, the compressor epilogue, the cache writer) rounds identically.
+__device__ __forceinline__ void rope_rotate(float &x0, float &x1, float cs, float sn) {
+  const float a = fmaf(x0, cs, -(x1 * sn)), b = fmaf(x0, sn, x1 * cs);
+  x0 = a;
+  x1 = b;
+}
+
+// One token of the compressor's per-channel online softmax: gate g (z + bias)
+// and candidate c; the pooled value is acc / den once the window is done.
+// Shared by the batch compressor and the streaming cache writer so that both
+// produce the same bits for an entry.
+struct PoolAcc {
+  float mx, den, acc;
+};
+__device__ __forceinline__ PoolAcc pool_init() { return PoolAcc{-INFINITY, 0.f, 0.f}; }
+__device__ __forceinline__ void pool_step(PoolAcc &a, float g, float c) {
+  if (g > a.mx) {
+    const float r = __expf(a.mx - g);
+    a.den *= r;
+    a.acc *= r;
+    a.mx = g;
+  }
+  const float e = __expf(g - a.mx);
+  a.den += e;
+  a.acc = fmaf(e, c, a.acc);
+}
+
+// ---- storage encoders (quantise-on-write) ----
+// E4M3 code of v, round to nearest even, saturating at 448 (the code 0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sgn = (__float_as_uint(v) >> 31) << 7;
+  const float a = fabsf(v);
+  if (!(a < 464.f)) return sgn | 0x7Eu;          // at or past the 448 | NaN midpoint: 448
+  if (a < 0.015625f) return sgn | (uint32_t)rintf(a * 512.f);   // subnormal steps of 2^-9 (8 = 2^-6)
+  int ex = (int)(__float_as_uint(a) >> 23) - 127;              // floor(log2 a), a normal
+  const float q = rintf((ldexpf(a, -ex) - 1.f) * 8.f);          // 3 mantissa bits, ties to even
+  int mq = (int)q;
+  if (mq == 8) {
+    mq = 0;
+    ++ex;
+  }
+  if (ex > 8 || (ex == 8 && mq == 7)) return sgn | 0x7Eu;
+  return sgn | ((uint32_t)(ex + 7) << 3) | (uint32_t)mq;
+}
+
+// E2M1 code of v for a block scale 2^e (nearest, ties to even, saturating at
+// 6, no negative zero).
+__device__ __forceinline__ uint32_t e2m1_encode(float v, int e) {
+  const float a = fabsf(ldexpf(v, -e));
+  // thresholds between grid points 0 .5 1 1.5 2 3 4 6; '>' at a midpoint below
+  // an odd code, '>=' below an even one
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.f);
+  return c ? (c | ((__float_as_uint(v) >> 31) << 3)) : 0u;
+}
+
+// FP8R row scale from the row's largest |x| over the E4M3 channels.
+__device__ __forceinline__ float fp8r_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
+
+// MXFP4 block exponent from the block's largest |x|: floor(log2 amax) - 2,
+// clamped to the E8M0 range (-127 for an all-zero block).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  int k2;
+  frexpf(amax, &k2);   // amax = f 2^k2, f in [0.5, 1)
+  return min(127, max(-127, k2 - 3));
+}
+
 __device__ __forceinline__ int64_t row_bytes(int dtype, int dim, int tail) {
   switch (dtype) {
   case DSV4_F32: return 4LL * dim;
   case DSV4_BF16: return 2LL * dim;
+  case DSV4_F16: return 2LL * dim;
   case DSV4_FP8R: return (int64_t)(dim - tail) + 2LL * tail;
   case DSV4_MXFP4: return dim / 2;
   }

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, co
   const int width = overlap ? 2 * m : m;
   const int jlo = t0 < 0 ? -t0 : 0;
   const int64_t rowbase = (int64_t)b * S;
-  float mx0 = -INFINITY, mx1 = -INFINITY, den0 = 0.f, den1 = 0.f, acc0 = 0.f, acc1 = 0.f;
+  PoolAcc a0 = pool_init(), a1 = pool_init();
   for (int j = jlo; j < width; ++j) {
     const int t = t0 + j;
     if (t >= S) break;
@@ -77,23 +77,17 @@ __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, co
     const float2 zz = Pair<TI>::load(z, e);
     const float2 cc = Pair<TI>::load(c, e);
     const float2 bb = reinterpret_cast<const float2 *>(bias)[(int64_t)j * half + pr];
-    const float g0 = zz.x + bb.x, g1 = zz.y + bb.y;
-    // online softmax per channel
-    if (g0 > mx0) { const float r = __expf(mx0 - g0); den0 *= r; acc0 *= r; mx0 = g0; }
-    if (g1 > mx1) { const float r = __expf(mx1 - g1); den1 *= r; acc1 *= r; mx1 = g1; }
-    const float e0 = __expf(g0 - mx0), e1 = __expf(g1 - mx1);
-    den0 += e0; acc0 = fmaf(e0, cc.x, acc0);
-    den1 += e1; acc1 = fmaf(e1, cc.y, acc1);
+    pool_step(a0, zz.x + bb.x, cc.x);   // online softmax per channel
+    pool_step(a1, zz.y + bb.y, cc.y);
   }
-  float o0 = acc0 / den0, o1 = acc1 / den1;
+  float o0 = a0.acc / a0.den, o1 = a1.acc / a1.den;
   const int d0 = 2 * pr;
   if (rope_dim > 0 && d0 >= dim - rope_dim) {
     const int pair = (d0 - (dim - rope_dim)) >> 1;
     const double P = (double)((pos0 ? pos0[b] : 0) + (int64_t)s * m);
     float cs, sn;
     rope_cs(P, pair, rope_dim, theta, 1.f, &cs, &sn);
-    const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
-    o0 = r0; o1 = r1;
+    rope_rotate(o0, o1, cs, sn);
   }
   Pair<TO>::store(pool, ((int64_t)b * N + s) * half + pr, o0, o1);
 }
@@ -113,8 +107,7 @@ __global__ __launch_bounds__(256) void k_rope(const void *x, void *y, int64_t n_
   if (d0 >= dim - rope_dim) {
     float cs, sn;
     rope_cs((double)pos[r], (d0 - (dim - rope_dim)) >> 1, rope_dim, theta, sign, &cs, &sn);
-    const float a = v.x * cs - v.y * sn, bq = v.x * sn + v.y * cs;
-    v.x = a; v.y = bq;
+    rope_rotate(v.x, v.y, cs, sn);
   }
   Pair<TO>::store(y, e, v.x, v.y);
 }

@@ -19,34 +19,6 @@
 
 namespace dsv4 {
 
-// E4M3 code of v (|v| <= ~448 expected), round to nearest even, saturating.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sgn = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
-  if (!(a < 464.f)) return sgn | 0x7Eu;          // at or past the 448 | NaN midpoint: 448
-  if (a < 0.015625f) return sgn | (uint32_t)rintf(a * 512.f);   // subnormal steps of 2^-9 (8 = 2^-6)
-  int ex = (int)(__float_as_uint(a) >> 23) - 127;              // floor(log2 a), a normal
-  const float q = rintf((ldexpf(a, -ex) - 1.f) * 8.f);          // 3 mantissa bits, ties to even
-  int mq = (int)q;
-  if (mq == 8) {
-    mq = 0;
-    ++ex;
-  }
-  if (ex > 8 || (ex == 8 && mq == 7)) return sgn | 0x7Eu;
-  return sgn | ((uint32_t)(ex + 7) << 3) | (uint32_t)mq;
-}
-
-// E2M1 code of v for a block scale 2^e (nearest, ties to even, saturating at
-// 6, no negative zero).
-__device__ __forceinline__ uint32_t e2m1_encode(float v, int e) {
-  const float a = fabsf(ldexpf(v, -e));
-  // thresholds between grid points 0 .5 1 1.5 2 3 4 6; '>' at a midpoint below
-  // an odd code, '>=' below an even one
-  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-                     (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.f);
-  return c ? (c | ((__float_as_uint(v) >> 31) << 3)) : 0u;
-}
-
 template <int XD>
 __device__ __forceinline__ float load_x(const void *x, int64_t i) {
   if constexpr (XD == DSV4_F32) return reinterpret_cast<const float *>(x)[i];
@@ -74,7 +46,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *x, int64_t n, int 
       if (k < E && E * lane + k < nq) am = fmaxf(am, fabsf(v[k]));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    const float s = am > 0.f ? am / 448.f : 1.f;
+    const float s = fp8r_scale(am);
     if (lane == 0) row_scale[r] = s;
     uint8_t *o = rows + r * (int64_t)(nq + 2 * tail);
 #pragma unroll
@@ -96,12 +68,7 @@ __global__ __launch_bounds__(256) void k_quantize(const void *x, int64_t n, int 
     for (int k = 0; k < EMAX; ++k)
       if (k < E) am = fmaxf(am, fabsf(v[k]));
     for (int o = 1; o < 32 / E; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
-    int e = -127;
-    if (am > 0.f) {
-      int k2;
-      frexpf(am, &k2);   // am = f 2^k2, f in [0.5, 1)
-      e = min(127, max(-127, k2 - 3));
-    }
+    const int e = mx_exponent(am);
     if ((E * lane) % 32 == 0) blk_scale[r * (dim / 32) + (E * lane) / 32] = (uint8_t)(e + 127);
     uint8_t *o = rows + r * (int64_t)(dim / 2);
     if (E == 1) {   // a lane holds one channel: pair it with its odd neighbour

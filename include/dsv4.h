@@ -77,8 +77,11 @@ typedef struct {
 
 /* Per-sequence stored rows: a compressed pool or a sliding window.
  * Row i of sequence b lives at data + (b*seq_stride + i) * row_bytes(dtype).
- * count[b] rows are valid.  For a window, row i holds token first_tok[b] + i;
- * for a pool, first_tok is NULL and row s is compressed entry s. */
+ * count[b] rows are valid.  For a window, the valid rows hold the tokens
+ * [first_tok[b], first_tok[b] + count[b]): token j is row j - first_tok[b]
+ * (ring = 0), or row j mod seq_stride (ring = 1: the sliding-window ring that
+ * dsv4_cache_append maintains).  For a pool, first_tok is NULL, ring is 0 and
+ * row s is compressed entry s. */
 typedef struct {
   const void *data;
   const float *row_scale;    /* DSV4_FP8R: [B*seq_stride]; else NULL */
@@ -89,6 +92,7 @@ typedef struct {
   int64_t seq_stride;        /* rows reserved per sequence (>= every count[b]) */
   const int32_t *count;      /* [B] */
   const int32_t *first_tok;  /* [B] (windows) or NULL (pools) */
+  int32_t ring;              /* windows: 1 = ring layout (see above); pools: 0 */
 } dsv4_rows;
 
 /* dsv4_compress -- softmax-gated pooling with a learned position bias.
@@ -217,6 +221,78 @@ int dsv4_quantize(const void *x, int32_t x_dtype, int64_t n_rows, int32_t dim, i
  * Process-wide; affects calls (and dsv4_attn_workspace sizes) made after it.
  * Returns the previous setting. */
 int dsv4_set_batch_invariant(int32_t on);
+
+/* ---- decode caches: streaming maintenance ----
+ * HF DeepSeek-V4 page, "Cache layers": every compressed-attention layer carries
+ * its compressor (and indexer) state from one forward call to the next -- a
+ * sliding window of K=V rows plus, per compressed stream, a buffer of the
+ * newest tokens, the pool and its count, with overlap state for CSA; the HCA
+ * cache has one stream, the CSA cache a second one for the indexer keys at
+ * index_head_dim.  insight.ai.kr deep dive: the KV cache is stored as FP8 with
+ * the rope channels in BF16; MarkTechPost summary: MXFP4 indexer keys.
+ *
+ * One compressed stream.  The buffer keeps the candidates c and gates z of the
+ * newest `span` tokens (span = 2m with overlap, else m): token t at slot
+ * t mod span, as float32 [B, span, 2, dim] (c then z).  An entry is pooled,
+ * rotated (rope_dim > 0) and quantised into the pool when its window closes. */
+typedef struct {
+  int32_t dim;               /* channels: multiple of 64, 64..512 */
+  int32_t rope_dim;          /* trailing channels rotated at the entry position (0: none) */
+  const float *pos_bias;     /* [span, dim] float32 */
+  float *buf;                /* [B, span, 2, dim] float32 state */
+  void *pool;                /* [B, pool_cap] rows of pool_dtype */
+  float *row_scale;          /* DSV4_FP8R: [B, pool_cap]; else NULL */
+  uint8_t *blk_scale;        /* DSV4_MXFP4: [B, pool_cap, dim/32]; else NULL */
+  int32_t pool_dtype;        /* DSV4_F32, DSV4_BF16, DSV4_F16, DSV4_FP8R or DSV4_MXFP4 */
+  int32_t tail;              /* DSV4_FP8R: bf16 channels at the end; else 0 */
+  int64_t pool_cap;          /* pool rows reserved per sequence */
+  int32_t *count;            /* [B] pooled entries (state; = len/m after every call) */
+} dsv4_stream;
+
+/* A layer's cache: per-sequence token count, the window ring and one or two
+ * compressed streams.  All pointers are device memory owned by the caller,
+ * zero-initialised (len, counts) before the first append. */
+typedef struct {
+  int32_t n_seq;             /* B >= 1 */
+  int32_t m;                 /* compression stride (CSA 4, HCA 128) */
+  int32_t overlap;           /* 1: windows of 2m with stride m (CSA); 0: windows of m (HCA) */
+  double rope_theta;         /* one theta for every rotation of the layer */
+  const int64_t *pos0;       /* [B] or NULL */
+  int32_t *len;              /* [B] tokens appended so far (state) */
+  /* window ring of K=V rows, rotated at their positions; win_cap = 0: none */
+  void *win;                 /* [B, win_cap] rows of win_dtype (DSV4_F32/BF16/F16/FP8R) */
+  float *win_scale;          /* DSV4_FP8R: [B, win_cap] */
+  int32_t win_dtype, win_tail, win_cap;
+  int32_t win_dim;           /* K=V channels (the kv stream's dim) */
+  int32_t win_rope_dim;      /* trailing channels rotated at the token's position */
+  int32_t *win_count;        /* [B] state: min(len, win_cap) */
+  int32_t *win_first;        /* [B] state: len - win_count */
+  dsv4_stream kv;            /* the K=V compressed stream */
+  dsv4_stream idx;           /* indexer keys (CSA); idx.dim = 0: absent (HCA) */
+} dsv4_cache;
+
+/* dsv4_cache_append -- append up to n tokens to every sequence of a cache.
+ * Sequence b takes n_new[b] (<= n; n_new NULL: n) tokens, L_b = len[b] first:
+ * token L_b + i comes from row i of the inputs.  The newest win_cap of them
+ * are rotated at pos0[b] + token and quantised into the window ring; every
+ * entry whose window closes (s with (s+1)m <= L_b + n_new[b]) is pooled from
+ * the buffer and the inputs as dsv4_compress does, rotated at pos0[b] + s*m
+ * (kv stream) and quantised as dsv4_quantize does; the newest span tokens go
+ * to the buffers; len, count, win_count and win_first advance.  Prefill into an
+ * empty cache and one decode step are the same call (n = S, or n = 1).
+ *   kv            : [B, n, win_dim]       (may be NULL when win_cap = 0)
+ *   kv_c, kv_z    : [B, n, kv.dim]
+ *   idx_c, idx_z  : [B, n, idx.dim]        (NULL when idx.dim = 0)
+ *   in_dtype      : DSV4_F32 or DSV4_BF16 for every input
+ *   n_new         : [B] int32 device, or NULL
+ * The caller keeps pool_cap >= (len + n_new)/m; entries past pool_cap are not
+ * written (count stops at pool_cap).  With DSV4_FP8R the window and pool rows
+ * are 576-byte rows for dim 512 / tail 64.  The window ring is read back by
+ * the attention calls as a dsv4_rows window with ring = 1, seq_stride =
+ * win_cap, count = win_count, first_tok = win_first. */
+int dsv4_cache_append(const dsv4_cache *cache, int32_t n, const int32_t *n_new, const void *kv,
+                      const void *kv_c, const void *kv_z, const void *idx_c, const void *idx_z,
+                      int32_t in_dtype, hipStream_t stream);
 
 /* Thread-local description of the last error (empty string after success). */
 const char *dsv4_last_error(void);

@@ -162,3 +162,69 @@ def test_quantize_rejects_bad_args(K):
     assert _rc(L.dsv4_quantize(fake, 0, 4, 128, 32, fake, None, fake, K.DSV4_MXFP4, None)) == K.DSV4_EINVAL
     assert _rc(L.dsv4_quantize(fake, 9, 4, 128, 0, fake, None, fake, K.DSV4_MXFP4, None)) == K.DSV4_ENOTSUP
     assert _rc(L.dsv4_quantize(None, 0, 0, 128, 0, None, None, None, K.DSV4_MXFP4, None)) == K.DSV4_OK
+
+
+def _cache(K, **over):
+    """A well-formed CSA cache descriptor on fake device addresses (never
+    dereferenced: every case below fails validation or appends 0 tokens)."""
+    f = 0x1000
+    st = dict(dim=512, rope_dim=64, pos_bias=f, buf=f, pool=f, row_scale=f, blk_scale=None,
+              pool_dtype=K.DSV4_FP8R, tail=64, pool_cap=64, count=f)
+    ix = dict(dim=128, rope_dim=0, pos_bias=f, buf=f, pool=f, row_scale=None, blk_scale=f,
+              pool_dtype=K.DSV4_MXFP4, tail=0, pool_cap=64, count=f)
+    st.update(over.pop("kv", {}))
+    ix.update(over.pop("idx", {}))
+    c = dict(n_seq=2, m=4, overlap=1, rope_theta=1.6e5, pos0=None, len=f, win=f, win_scale=f,
+             win_dtype=K.DSV4_FP8R, win_tail=64, win_cap=128, win_dim=512, win_rope_dim=64, win_count=f,
+             win_first=f)
+    c.update(over)
+    return K.Cache(kv=K.Stream(**st), idx=K.Stream(**ix), **c)
+
+
+def test_cache_append_rejects_bad_args(K):
+    L = K.lib()
+    f = ctypes.c_void_p(0x1000)
+
+    def call(cache, n=1, kv=f, idx=f, dt=K.DSV4_BF16):
+        return _rc(L.dsv4_cache_append(ctypes.byref(cache), n, None, kv, f, f, idx, idx, dt, None))
+
+    assert _rc(L.dsv4_cache_append(None, 1, None, f, f, f, f, f, K.DSV4_BF16, None)) == K.DSV4_EINVAL
+    assert call(_cache(K), n=0) == K.DSV4_OK                      # nothing to append: nothing launched
+    assert call(_cache(K), n=-1) == K.DSV4_EINVAL
+    assert call(_cache(K, n_seq=0)) == K.DSV4_EINVAL
+    assert call(_cache(K, m=0)) == K.DSV4_ENOTSUP
+    assert call(_cache(K, len=None)) == K.DSV4_EINVAL
+    assert call(_cache(K), dt=K.DSV4_FP8R) == K.DSV4_ENOTSUP     # inputs are f32 or bf16
+    assert call(_cache(K, kv=dict(dim=500))) == K.DSV4_ENOTSUP
+    assert call(_cache(K, kv=dict(row_scale=None))) == K.DSV4_EINVAL
+    assert call(_cache(K, kv=dict(tail=60))) == K.DSV4_ENOTSUP
+    assert call(_cache(K, kv=dict(buf=None))) == K.DSV4_EINVAL
+    assert call(_cache(K, kv=dict(rope_dim=66))) == K.DSV4_EINVAL
+    assert call(_cache(K, idx=dict(blk_scale=None))) == K.DSV4_EINVAL
+    assert call(_cache(K, idx=dict(tail=8))) == K.DSV4_EINVAL
+    assert call(_cache(K), idx=None) == K.DSV4_EINVAL             # the idx stream needs its inputs
+    assert call(_cache(K, win_dtype=K.DSV4_MXFP4, win_tail=0)) == K.DSV4_ENOTSUP
+    assert call(_cache(K, win_dim=256)) == K.DSV4_EINVAL
+    assert call(_cache(K), kv=None) == K.DSV4_EINVAL
+    assert call(_cache(K, win_cap=-1)) == K.DSV4_EINVAL
+    assert call(_cache(K, rope_theta=0.0)) == K.DSV4_EINVAL
+    assert "rope_theta" in K.dsv4_last_error()
+
+
+def test_ring_windows_only(K):
+    """The ring layout is a window layout: a pool (no first_tok) cannot be one."""
+    L = K.lib()
+    f = ctypes.c_void_p(0x1000)
+    q = K.Queries(1, 1, 0x1000, 0x1000, None)
+    pool = K.Rows(0x1000, None, None, K.DSV4_BF16, 512, 0, 16, 0x1000, None, 1)
+    rc = _rc(L.dsv4_sparse_attn(ctypes.byref(q), f, K.DSV4_BF16, 64, 512, None, 0, ctypes.byref(pool), f, 8,
+                                None, 0.04, 64, 1e4, f, K.DSV4_BF16, f, 1 << 30, None))
+    assert rc == K.DSV4_EINVAL and "ring" in K.dsv4_last_error()
+    kp = K.Rows(0x1000, None, None, K.DSV4_BF16, 128, 0, 16, 0x1000, None, 1)
+    rc = _rc(L.dsv4_index_topk(ctypes.byref(q), f, None, K.DSV4_BF16, f, 64, 128, ctypes.byref(kp), 4, 8, 1.0,
+                               f, None, f, 1 << 30, None))
+    assert rc == K.DSV4_EINVAL and "ring" in K.dsv4_last_error()
+    win = K.Rows(0x1000, None, None, K.DSV4_BF16, 512, 0, 0, 0x1000, 0x1000, 1)   # ring of stride 0
+    rc = _rc(L.dsv4_sparse_attn(ctypes.byref(q), f, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128, None, None, 0,
+                                None, 0.04, 64, 1e4, f, K.DSV4_BF16, f, 1 << 30, None))
+    assert rc == K.DSV4_EINVAL
