@@ -243,8 +243,8 @@ int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_i
     return fail(DSV4_ENOTSUP, "index_topk: query dtype %d", q_dtype);
   }
   if (!index_topk_supported(k_pool->seq_stride, topk))
-    return fail(DSV4_ENOTSUP, "index_topk: pool stride %lld with topk %d exceeds the two-stage select",
-                (long long)k_pool->seq_stride, topk);
+    return fail(DSV4_ENOTSUP, "index_topk: pool stride %lld (at most 65535 chunks of 4096 entries)",
+                (long long)k_pool->seq_stride);
   const size_t need = index_topk_ws(q->n_rows, k_pool->seq_stride, topk);
   if (q->n_rows > 0 && (!ws || ws_bytes < need))
     return fail(DSV4_EWORKSPACE, "index_topk: workspace %zu bytes, need %zu", ws_bytes, need);

@@ -18,10 +18,14 @@
 //       Keys are read once, straight from HBM into MFMA registers; the ReLU,
 //       the head weights and the head sum run on the accumulators.
 //   k_index_scores_f32  scalar fp32 path (small fp32 shapes).
-//   k_topk_chunk / k_topk_merge  exact radix select in LDS over an
-//       order-preserving key (digits of up to 12 bits, counted from the top of
-//       the keys' own range), ties to the lower index, stable compaction so
-//       indices come out ascending.
+//   k_topk_chunk  rows of up to 16384 visible entries: exact radix select
+//       on register-resident order-preserving keys (8-bit digits counted from
+//       the top of the keys' own range), ties to the lower index, stable
+//       compaction so indices come out ascending.
+//   k_rt_hist / k_rt_count / k_rt_emit  longer rows: the exact kk-th largest
+//       key from three global histogram passes (11 + 11 + 10 bits) over every
+//       chunk of the row, then per-chunk counts and an ordered emission; the
+//       same picks, spread over (row, chunk) workgroups.
 #include "dsv4_common.h"
 
 #include <algorithm>
@@ -74,11 +78,14 @@ __device__ __forceinline__ float keyf(uint32_t k) {
 // decode scan is one pass over a large pool and is bound by how many bytes
 // are outstanding, not by the matrix cores.
 template <int NHB, int KS, bool FP4, int EB>
-__global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, int chunk,
-                                                           float *__restrict__ scores, int64_t ld) {
+__global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, uint32_t *hzero,
+                                                           int hwords, float *__restrict__ scores, int64_t ld) {
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
+  // clear this row's top-k histograms (when the radix passes follow)
+  if (hzero && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < hwords; i += 256) hzero[(int64_t)r * hwords + i] = 0u;
   const int b = Q.seq[r];
   const int hi = n_visible(Q.tok[r], K.m, K.count[b]);
   constexpr int STEP = 64 * EB;   // entries per super-block
@@ -541,45 +548,33 @@ __device__ void tk_select(uint32_t (&k)[KPT], int kk, TkLds &L, Emit emit) {
     }
 }
 
-// grid (T, n_chunks), 256 threads.  Chunk c covers entries [c*chunk, min(n,
-// (c+1)*chunk)), chunk <= 256*KPT.  One chunk: writes the final idx/score rows.
-// Otherwise writes per-chunk candidates (ascending entry order, key 0 and
-// index -1 in unused slots) for k_topk_merge.
+// grid (T), 256 threads: rows of at most 256*KPT visible entries, selected in
+// registers; writes the final idx/score rows.
 template <int KPT>
 __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
                                                     const int32_t *__restrict__ count, int m,
-                                                    const float *__restrict__ scores, int64_t ld, int chunk,
-                                                    int topk, int32_t *__restrict__ idx_out,
-                                                    float *__restrict__ score_out, uint32_t *__restrict__ cand_key,
-                                                    int32_t *__restrict__ cand_idx) {
+                                                    const float *__restrict__ scores, int64_t ld, int topk,
+                                                    int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
   __shared__ TkLds L;
-  const int r = gridDim.x - 1 - blockIdx.x, cidx = blockIdx.y, nch = gridDim.y;   // long rows first
+  const int r = gridDim.x - 1 - blockIdx.x;   // long rows first
   const int n = n_visible(tok[r], m, count[seq[r]]);
-  const int lo = cidx * chunk;
-  const int len = max(0, min(n, lo + chunk) - lo);
-  const int kk = min(topk, len);
-  const bool final_ = nch == 1;
-  int32_t *io = final_ ? idx_out + (int64_t)r * topk : cand_idx + ((int64_t)r * nch + cidx) * topk;
-  float *so = final_ && score_out ? score_out + (int64_t)r * topk : nullptr;
-  uint32_t *ko = final_ ? nullptr : cand_key + ((int64_t)r * nch + cidx) * topk;
+  const int kk = min(topk, n);
+  int32_t *io = idx_out + (int64_t)r * topk;
+  float *so = score_out ? score_out + (int64_t)r * topk : nullptr;
   auto emit = [&](int rank, int pos, uint32_t key) {
-    io[rank] = lo + pos;
+    io[rank] = pos;
     if (so) so[rank] = keyf(key);
-    if (ko) ko[rank] = key;
   };
-  if (kk == len) {   // everything visible is taken, in order
-    for (int j = threadIdx.x; j < len; j += 256) {
-      const float v = scores[(int64_t)r * ld + lo + j];
-      emit(j, j, fkey(v));
-    }
+  if (kk == n) {   // everything visible is taken, in order
+    for (int j = threadIdx.x; j < n; j += 256) emit(j, j, fkey(scores[(int64_t)r * ld + j]));
   } else {
     uint32_t k[KPT];
-    const float *src = scores + (int64_t)r * ld + lo;
-    const bool vec = ((((int64_t)r * ld + lo) & 3) == 0) && (((uintptr_t)scores & 15) == 0);
+    const float *src = scores + (int64_t)r * ld;
+    const bool vec = ((((int64_t)r * ld) & 3) == 0) && (((uintptr_t)scores & 15) == 0);
 #pragma unroll
     for (int q = 0; q < KPT / 4; ++q) {
       const int p = 4 * ((int)threadIdx.x + 256 * q);
-      if (vec && p + 3 < len) {
+      if (vec && p + 3 < n) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(src + p);
         k[4 * q] = fkey(v[0]);
         k[4 * q + 1] = fkey(v[1]);
@@ -587,7 +582,7 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ 
         k[4 * q + 3] = fkey(v[3]);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) k[4 * q + e] = p + e < len ? fkey(src[p + e]) : 0u;
+        for (int e = 0; e < 4; ++e) k[4 * q + e] = p + e < n ? fkey(src[p + e]) : 0u;
       }
     }
     tk_select<KPT>(k, kk, L, [&](int rank, int j, uint32_t key) { emit(rank, tk_pos(j), key); });
@@ -595,52 +590,262 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ 
   for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
     io[j] = -1;
     if (so) so[j] = -INFINITY;
-    if (ko) ko[j] = 0u;
   }
 }
 
-// grid (T), 256 threads.  Merges nc = n_chunks*topk <= 256*KPT candidates
-// (key 0 = empty) into the final row.
-template <int KPT>
-__global__ __launch_bounds__(256) void k_topk_merge(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
-                                                    const int32_t *__restrict__ count, int m, int n_chunks,
-                                                    int topk, const uint32_t *__restrict__ cand_key,
-                                                    const int32_t *__restrict__ cand_idx,
-                                                    int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
-  __shared__ TkLds L;
-  const int nc = n_chunks * topk;
-  const int r = blockIdx.x;
+// -------------------------------------------------------------------- long rows: radix threshold
+// Rows longer than one workgroup's 16384 register-resident keys (decode over
+// long pools) are selected by finding the exact kk-th largest key t* of the
+// row with three histogram passes over all of the row's chunks (11, 11 and 10
+// key bits, global atomic histograms), then counting, per chunk of 4096 keys,
+// the keys above t* and equal to t*, and emitting: every key above t*, and the
+// lowest-position keys equal to t* up to kk.  Every pass runs one workgroup
+// per (row, chunk), so a few long rows still spread over the whole GPU; the
+// picks come out in ascending position order (per-chunk prefix counts), with
+// the same result as the register-resident select.
+constexpr int kRtChunk = 4096;   // keys per workgroup: 16 per thread
+constexpr int kRtBins = 2048;
+
+struct RtHist {                   // per row
+  uint32_t h[3][kRtBins];
+  uint32_t st[2][4];              // prefix, above, want after levels 1 and 2
+};
+
+__device__ __forceinline__ int rt_pos(int j) { return 4 * ((int)threadIdx.x + 256 * (j >> 2)) + (j & 3); }
+
+// keys of chunk c of row r (0 = no entry)
+__device__ __forceinline__ void rt_load(const float *scores, int64_t ld, int r, int lo, int n, uint32_t (&k)[16]) {
+  const float *src = scores + (int64_t)r * ld + lo;
+  const bool vec = ((((int64_t)r * ld + lo) & 3) == 0) && (((uintptr_t)scores & 15) == 0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int p = 4 * ((int)threadIdx.x + 256 * q);
+    if (vec && lo + p + 3 < n) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(src + p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k[4 * q + e] = fkey(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) k[4 * q + e] = lo + p + e < n ? fkey(src[p + e]) : 0u;
+    }
+  }
+}
+
+// Bin of histogram `h` (nb bins) holding the want-th largest key: returns the
+// bin and, in *above, the count of keys in higher bins.  Block-wide; uses sh
+// (at least 8 words) and ends with a barrier.
+__device__ __forceinline__ int rt_find(const uint32_t *h, int nb, uint32_t want, uint32_t *above, uint32_t *sh) {
+  const int per = nb / 256;                      // bins per thread, highest bins to thread 0
+  const int top = nb - 1 - per * (int)threadIdx.x;
+  uint32_t c[8], tot_t = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    c[i] = i < per ? h[top - i] : 0u;
+    tot_t += c[i];
+  }
+  uint32_t total;
+  const uint32_t before = tk_scan(tot_t, sh, &total);   // keys in bins above this thread's
+  if (threadIdx.x == 0) {
+    sh[4] = 0;
+    sh[5] = 0;
+  }
+  __syncthreads();
+  if (before < want && want <= before + tot_t) {
+    uint32_t run = before;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < per && run < want && want <= run + c[i]) {
+        sh[4] = (uint32_t)(top - i);
+        sh[5] = run;
+      }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+  const int bin = (int)sh[4];
+  *above = sh[5];
+  __syncthreads();
+  return bin;
+}
+
+// Threshold state after some histogram levels: key prefix, count of keys
+// above it and the number still wanted inside it.
+struct RtThr {
+  uint32_t prefix, above, want;
+};
+// One more level: the bin of histogram h (nb bins of `bits` bits) that holds
+// the want-th largest key under the prefix.
+__device__ __forceinline__ RtThr rt_next(const uint32_t *h, int nb, int bits, RtThr t, uint32_t *sh) {
+  uint32_t ab;
+  const int bin = rt_find(h, nb, t.want, &ab, sh);
+  return RtThr{(t.prefix << bits) | (uint32_t)bin, t.above + ab, t.want - ab};
+}
+
+// grid (3*kRtBins*T/256), 256 threads: clear the histograms
+__global__ __launch_bounds__(256) void k_rt_zero(uint32_t *h, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) h[i] = 0u;
+}
+
+// grid (T, n_chunks), 256 threads: histogram level L (0, 1, 2) of the keys
+// that match the prefix fixed by the levels before it
+template <int L>
+__global__ __launch_bounds__(256) void k_rt_hist(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                 const int32_t *__restrict__ count, int m, const float *__restrict__ scores,
+                                                 int64_t ld, int topk, RtHist *__restrict__ hist) {
+  __shared__ uint32_t lh[kRtBins];
+  __shared__ uint32_t sh[8];
+  const int r = blockIdx.x, lo = blockIdx.y * kRtChunk;
   const int n = n_visible(tok[r], m, count[seq[r]]);
   const int kk = min(topk, n);
-  const int64_t base = (int64_t)r * nc;
+  if (kk == n || lo >= n) return;   // every entry taken, or nothing here
+  RtHist &H = hist[r];
+  // the prefix fixed by the levels before this one: level 1 scans level 0's
+  // histogram; level 2 starts from the state level 1's chunk 0 recorded
+  RtThr t{0u, 0u, (uint32_t)kk};
+  if constexpr (L == 1) t = rt_next(H.h[0], kRtBins, 11, t, sh);
+  if constexpr (L == 2) t = rt_next(H.h[1], kRtBins, 11, RtThr{H.st[0][0], H.st[0][1], H.st[0][2]}, sh);
+  if (L > 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    H.st[L - 1][0] = t.prefix;
+    H.st[L - 1][1] = t.above;
+    H.st[L - 1][2] = t.want;
+  }
+  for (int i = threadIdx.x; i < kRtBins; i += 256) lh[i] = 0u;
+  uint32_t k[16];
+  rt_load(scores, ld, r, lo, n, k);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t key = k[j];
+    if (key == 0u) continue;
+    if constexpr (L == 0) atomicAdd(&lh[key >> 21], 1u);
+    else if constexpr (L == 1) {
+      if ((key >> 21) == t.prefix) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
+    } else {
+      if ((key >> 10) == t.prefix) atomicAdd(&lh[key & 1023u], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < (L == 2 ? 1024 : kRtBins); i += 256)
+    if (lh[i]) atomicAdd(&H.h[L][i], lh[i]);
+}
+
+// grid (T, n_chunks), 256 threads: keys above t* and equal to t* per chunk;
+// chunk 0 also records (t*, keys wanted at t*)
+__global__ __launch_bounds__(256) void k_rt_count(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                  const int32_t *__restrict__ count, int m,
+                                                  const float *__restrict__ scores, int64_t ld, int topk,
+                                                  const RtHist *__restrict__ hist, uint32_t *__restrict__ cnt,
+                                                  uint32_t *__restrict__ thr) {
+  __shared__ uint32_t sh[8];
+  const int r = blockIdx.x, c = blockIdx.y, nch = gridDim.y, lo = c * kRtChunk;
+  const int n = n_visible(tok[r], m, count[seq[r]]);
+  const int kk = min(topk, n);
+  uint32_t gt = 0, eq = 0;
+  if (kk < n && lo < n) {
+    const RtHist &H = hist[r];
+    const RtThr t = rt_next(H.h[2], 1024, 10, RtThr{H.st[1][0], H.st[1][1], H.st[1][2]}, sh);
+    uint32_t k[16];
+    rt_load(scores, ld, r, lo, n, k);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      gt += k[j] > t.prefix ? 1u : 0u;
+      eq += k[j] == t.prefix ? 1u : 0u;
+    }
+    uint32_t tot;
+    tk_scan(gt, sh, &tot);
+    gt = tot;
+    __syncthreads();
+    tk_scan(eq, sh, &tot);
+    eq = tot;
+    if (c == 0 && threadIdx.x == 0) {
+      thr[2 * r] = t.prefix;
+      thr[2 * r + 1] = t.want;
+    }
+  }
+  if (threadIdx.x == 0) {
+    cnt[2 * ((int64_t)r * nch + c)] = gt;
+    cnt[2 * ((int64_t)r * nch + c) + 1] = eq;
+  }
+}
+
+// grid (T, n_chunks), 256 threads: write the picks in ascending position order
+__global__ __launch_bounds__(256) void k_rt_emit(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                 const int32_t *__restrict__ count, int m,
+                                                 const float *__restrict__ scores, int64_t ld, int topk,
+                                                 const uint32_t *__restrict__ cnt, const uint32_t *__restrict__ thr,
+                                                 int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
+  __shared__ uint32_t sh[8];
+  const int r = blockIdx.x, c = blockIdx.y, nch = gridDim.y, lo = c * kRtChunk;
+  const int n = n_visible(tok[r], m, count[seq[r]]);
+  const int kk = min(topk, n);
   int32_t *io = idx_out + (int64_t)r * topk;
   float *so = score_out ? score_out + (int64_t)r * topk : nullptr;
-  if (kk > 0) {
-    uint32_t k[KPT];
-    const uint32_t *src = cand_key + base;
-    const bool vec = (base & 3) == 0 && (((uintptr_t)cand_key & 15) == 0);
-#pragma unroll
-    for (int q = 0; q < KPT / 4; ++q) {
-      const int p = 4 * ((int)threadIdx.x + 256 * q);
-      if (vec && p + 3 < nc) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(src + p);
-        k[4 * q] = v.x;
-        k[4 * q + 1] = v.y;
-        k[4 * q + 2] = v.z;
-        k[4 * q + 3] = v.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) k[4 * q + e] = p + e < nc ? src[p + e] : 0u;
-      }
+  if (c == 0)
+    for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
+      io[j] = -1;
+      if (so) so[j] = -INFINITY;
     }
-    tk_select<KPT>(k, kk, L, [&](int rank, int j, uint32_t key) {
-      io[rank] = cand_idx[base + tk_pos(j)];
-      if (so) so[rank] = keyf(key);
-    });
+  if (lo >= n) return;
+  if (kk == n) {   // every visible entry is taken, in order
+    for (int j = threadIdx.x; j < min(kRtChunk, n - lo); j += 256) {
+      io[lo + j] = lo + j;
+      if (so) so[lo + j] = scores[(int64_t)r * ld + lo + j];
+    }
+    return;
   }
-  for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
-    io[j] = -1;
-    if (so) so[j] = -INFINITY;
+  const uint32_t tstar = thr[2 * r], want = thr[2 * r + 1];
+  // keys above t* (G) and equal to t* (E) in the chunks before this one; the
+  // equal keys are taken in position order up to `want`, so the picks before
+  // this chunk are G + min(E, want)
+  uint32_t gsum = 0, esum = 0;
+  for (int cc = threadIdx.x; cc < c; cc += 256) {
+    gsum += cnt[2 * ((int64_t)r * nch + cc)];
+    esum += cnt[2 * ((int64_t)r * nch + cc) + 1];
+  }
+  uint32_t G, E;
+  tk_scan(gsum, sh, &G);
+  __syncthreads();
+  tk_scan(esum, sh, &E);
+  __syncthreads();
+  const uint32_t sel_before = G + min(E, want);
+  const uint32_t quota = E >= want ? 0u : want - E;   // keys equal to t* this chunk may take
+  uint32_t k[16];
+  rt_load(scores, ld, r, lo, n, k);
+  uint32_t eq_run = 0, sel_run = sel_before;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {   // position order: q, then thread, then e
+    uint32_t ne = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ne += k[4 * q + e] == tstar ? 1u : 0u;
+    uint32_t tot;
+    uint32_t er = eq_run + tk_scan(ne, sh, &tot);
+    eq_run += tot;
+    __syncthreads();
+    bool pick[4];
+    uint32_t ns = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = k[4 * q + e];
+      bool p = key > tstar;
+      if (key == tstar) {
+        p = er < quota;
+        ++er;
+      }
+      pick[e] = p;
+      ns += p ? 1u : 0u;
+    }
+    uint32_t slot = sel_run + tk_scan(ns, sh, &tot);
+    sel_run += tot;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (!pick[e]) continue;
+      const int pos = lo + 4 * ((int)threadIdx.x + 256 * q) + e;
+      io[slot] = pos;
+      if (so) so[slot] = keyf(k[4 * q + e]);
+      ++slot;
+    }
   }
 }
 
@@ -650,13 +855,14 @@ using namespace dsv4;
 
 namespace dsv4host {
 
-// Chunking of the pool for top-k: a first-stage chunk holds up to 16384 keys
-// (64 per thread); with several chunks the merge stage holds n_chunks*topk
-// candidates, also at most 16384.  The smallest chunk that keeps the merge
-// within bounds balances the two stages.
+// Top-k plan: rows of at most 16384 entries are selected by one workgroup
+// each (k_topk_chunk, KPT keys per thread); longer rows by the radix-threshold
+// passes over chunks of kRtChunk entries.  Workspace: the score rows, then
+// (long rows) the histograms, the per-chunk counts and the thresholds.
 struct TopkPlan {
-  int chunk, n_chunks, kpt1, kpt2;
-  size_t scores_bytes, cand_bytes;
+  bool radix;
+  int kpt, n_chunks;
+  size_t scores_bytes, hist_bytes, cnt_bytes, thr_bytes;
 };
 
 static int tk_kpt(int64_t n) {
@@ -665,34 +871,32 @@ static int tk_kpt(int64_t n) {
   return kpt;
 }
 
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 static TopkPlan plan_topk(int64_t n_rows, int64_t stride, int topk) {
-  TopkPlan p;
+  TopkPlan p{};
   const int64_t st = stride > 0 ? stride : 1;
-  if (st <= 16384) {
-    p.chunk = (int)st;
-    p.n_chunks = 1;
-  } else {
-    int64_t ch = 4096;
-    while (ch < 16384 && ((st + ch - 1) / ch) * topk > 16384) ch *= 2;
-    p.chunk = (int)ch;
-    p.n_chunks = (int)((st + ch - 1) / ch);
+  p.radix = st > 16384;
+  p.kpt = tk_kpt(st);
+  p.n_chunks = p.radix ? (int)((st + kRtChunk - 1) / kRtChunk) : 1;
+  p.scores_bytes = align256((size_t)n_rows * (size_t)st * 4);
+  if (p.radix) {
+    p.hist_bytes = align256((size_t)n_rows * sizeof(RtHist));
+    p.cnt_bytes = align256((size_t)n_rows * p.n_chunks * 8);
+    p.thr_bytes = align256((size_t)n_rows * 8);
   }
-  p.kpt1 = tk_kpt(p.chunk);
-  p.kpt2 = tk_kpt((int64_t)p.n_chunks * topk);
-  p.scores_bytes = (size_t)n_rows * (size_t)st * 4;
-  p.scores_bytes = (p.scores_bytes + 255) & ~(size_t)255;
-  p.cand_bytes = p.n_chunks > 1 ? (size_t)n_rows * p.n_chunks * topk * 8 : 0;
+  (void)topk;
   return p;
 }
 
 size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk) {
   const TopkPlan p = plan_topk(n_rows, stride, topk);
-  return p.scores_bytes + p.cand_bytes + 256;
+  return p.scores_bytes + p.hist_bytes + p.cnt_bytes + p.thr_bytes + 256;
 }
 
 int index_topk_supported(int64_t stride, int topk) {
-  const TopkPlan p = plan_topk(1, stride, topk);
-  return p.n_chunks == 1 || (int64_t)p.n_chunks * topk <= 16384;
+  // grid.y of the radix passes holds the chunks of a row
+  return (stride + kRtChunk - 1) / kRtChunk <= 65535 && topk >= 1;
 }
 
 // Workgroups of `kernel` (`block` threads, no dynamic LDS) that the current
@@ -720,13 +924,14 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
   if (T == 0) return DSV4_OK;
   const TopkPlan p = plan_topk(T, kp->seq_stride, topk);
   float *scores = (float *)ws;
-  uint32_t *cand_key = (uint32_t *)((char *)ws + p.scores_bytes);
-  int32_t *cand_idx = (int32_t *)(cand_key + (size_t)T * p.n_chunks * topk);
+  RtHist *hist = p.radix ? (RtHist *)((char *)ws + p.scores_bytes) : nullptr;
+  const int hwords = (int)(sizeof(RtHist) / 4);
+  bool hist_clear = false;   // the scoring kernel clears the histograms
   IdxQ Q{q->seq, q->tok, qv, qscale, w, H, Di};
   IdxK K{kp->data, kp->blk_scale, kp->count, kp->seq_stride, m};
   const int64_t ld = kp->seq_stride;
   // scoring kernels with one workgroup per (query row, entry chunk)
-  typedef void (*ScoreK)(IdxQ, IdxK, float, int, float *, int64_t);
+  typedef void (*ScoreK)(IdxQ, IdxK, float, uint32_t *, int, float *, int64_t);
   ScoreK sk = nullptr;
   int eb = 1;   // entries per wave iteration / 16
   if (q_dtype == DSV4_MXFP4) {
@@ -766,7 +971,9 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
     const int64_t blocks = (kp->seq_stride + unit - 1) / unit;
     const int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, resident_wgs((const void *)sk, 256) / T),
                                               std::max<int64_t>(1, blocks));
-    hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, 0, scores, ld);
+    hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, (uint32_t *)hist, hwords,
+                       scores, ld);
+    hist_clear = hist != nullptr;
   } else {
     constexpr int QPW = 1;   // queries per wave (4 per workgroup share each key tile)
     dim3 g8((T + 4 * QPW - 1) / (4 * QPW));
@@ -779,31 +986,35 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
   }
   int rc = check_launch("k_index_scores");
   if (rc) return rc;
-#define DSV4_TK1(KPT)                                                                                   \
-  hipLaunchKernelGGL((k_topk_chunk<KPT>), dim3(T, p.n_chunks), dim3(256), 0, st, q->seq, q->tok, kp->count, m, \
-                     scores, ld, p.chunk, topk, idx_out, score_out, cand_key, cand_idx)
-  switch (p.kpt1) {
-  case 4: DSV4_TK1(4); break;
-  case 8: DSV4_TK1(8); break;
-  case 16: DSV4_TK1(16); break;
-  case 32: DSV4_TK1(32); break;
-  default: DSV4_TK1(64); break;
-  }
+  if (!p.radix) {
+#define DSV4_TK1(KPT)                                                                                          \
+  hipLaunchKernelGGL((k_topk_chunk<KPT>), dim3(T), dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, \
+                     topk, idx_out, score_out)
+    switch (p.kpt) {
+    case 4: DSV4_TK1(4); break;
+    case 8: DSV4_TK1(8); break;
+    case 16: DSV4_TK1(16); break;
+    case 32: DSV4_TK1(32); break;
+    default: DSV4_TK1(64); break;
+    }
 #undef DSV4_TK1
-  rc = check_launch("k_topk_chunk");
-  if (rc || p.n_chunks == 1) return rc;
-#define DSV4_TK2(KPT)                                                                                   \
-  hipLaunchKernelGGL((k_topk_merge<KPT>), dim3(T), dim3(256), 0, st, q->seq, q->tok, kp->count, m, p.n_chunks, \
-                     topk, cand_key, cand_idx, idx_out, score_out)
-  switch (p.kpt2) {
-  case 4: DSV4_TK2(4); break;
-  case 8: DSV4_TK2(8); break;
-  case 16: DSV4_TK2(16); break;
-  case 32: DSV4_TK2(32); break;
-  default: DSV4_TK2(64); break;
+    return check_launch("k_topk_chunk");
   }
-#undef DSV4_TK2
-  return check_launch("k_topk_merge");
+  uint32_t *cnt = (uint32_t *)((char *)hist + p.hist_bytes);
+  uint32_t *thr = (uint32_t *)((char *)cnt + p.cnt_bytes);
+  if (!hist_clear) {
+    const int64_t hw = (int64_t)T * hwords;
+    hipLaunchKernelGGL(k_rt_zero, dim3((unsigned)((hw + 255) / 256)), dim3(256), 0, st, (uint32_t *)hist, hw);
+  }
+  const dim3 g((unsigned)T, (unsigned)p.n_chunks);
+  hipLaunchKernelGGL(k_rt_hist<0>, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist);
+  hipLaunchKernelGGL(k_rt_hist<1>, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist);
+  hipLaunchKernelGGL(k_rt_hist<2>, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist);
+  hipLaunchKernelGGL(k_rt_count, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist, cnt,
+                     thr);
+  hipLaunchKernelGGL(k_rt_emit, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, cnt, thr,
+                     idx_out, score_out);
+  return check_launch("k_rt_emit");
 }
 
 }  // namespace dsv4host

@@ -143,7 +143,7 @@ int dsv4_rope(const void *x, int32_t x_dtype, void *y, int32_t y_dtype, int64_t 
  *   score_out   : [T, topk] float32 scores of the picks (or -inf), may be NULL
  *   ws          : scratch of at least dsv4_index_topk_workspace(...) bytes
  * Supported: head_dim 128 (bf16: multiple of 32), n_heads multiple of 16 and
- * <= 64, 1 <= topk <= 2048, m >= 1. */
+ * <= 64, 1 <= topk <= 2048, m >= 1, pool_seq_stride <= 65535 * 4096. */
 size_t dsv4_index_topk_workspace(int32_t n_rows, int64_t pool_seq_stride, int32_t topk);
 int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale,
                     int32_t q_dtype, const float *w, int32_t n_heads, int32_t head_dim,

@@ -100,7 +100,7 @@ def test_index_topk_rejects_bad_args(K):
     assert _rc(L.dsv4_index_topk(*args(qdt=K.DSV4_MXFP4, kp=_rows(K, K.DSV4_MXFP4, 128)))) == K.DSV4_EINVAL
     bad_q = K.Queries(4, 0, fake.value, fake.value, None)
     assert _rc(L.dsv4_index_topk(*args(q=bad_q))) == K.DSV4_EINVAL
-    huge = _rows(K, K.DSV4_BF16, 128, seq_stride=1 << 22)
+    huge = _rows(K, K.DSV4_BF16, 128, seq_stride=1 << 29)   # more than 65535 chunks of 4096 entries
     assert _rc(L.dsv4_index_topk(*args(kp=huge, k=2048, ws=fake, wsb=1 << 62))) == K.DSV4_ENOTSUP
 
 

@@ -147,6 +147,10 @@ def test_index_topk_prefill(K, store, B, Sx, Hi, Di, m, k):
     ("mxfp4", 2, [70000, 5003], 1024),
     ("bf16", 2, [20000, 9], 2048),
     ("mxfp4", 1, [4 * 16384 + 7], 1),
+    # rows longer than one workgroup's select: the radix-threshold passes over
+    # 4096-entry chunks, next to rows that take every entry or have none
+    ("bf16", 3, [4 * 20000, 4 * 300, 3], 2048),
+    ("bf16", 1, [4 * 200000], 2048),
 ])
 def test_index_topk_decode(K, kind, B, L, k):
     say("index_topk decode", kind, B, L, k)
@@ -166,14 +170,18 @@ def test_index_topk_decode(K, kind, B, L, k):
     idx = K.dsv4_index_topk(Q, qdev, dev(layer.w_idx), upload_rows(kp), layer.m, k, layer.score_scale,
                             q_idx_scale=qscd)
     torch.cuda.synchronize()
-    stats = check_topk(idx.cpu().numpy(), ref, nv, k, "decode")
+    idx = idx.cpu().numpy()
+    stats = check_topk(idx, ref, nv, k, "decode")
     say("topk stats", stats)
+    for r in range(B):   # picks in ascending entry order
+        p = idx[r][idx[r] >= 0]
+        assert np.all(np.diff(p) > 0), f"row {r}: picks not in ascending order"
 
 
 @pytest.mark.parametrize("B,L,k,n_distinct", [
-    (2, [4 * 30000, 4 * 3000 + 3], 512, 3),   # several chunks + merge
+    (2, [4 * 30000, 4 * 3000 + 3], 512, 3),   # radix-threshold passes over several chunks
     (1, [4 * 20000], 1024, 1),                # every score equal
-    (3, [4 * 5000, 4 * 700, 9], 256, 2),      # one chunk
+    (3, [4 * 5000, 4 * 700, 9], 256, 2),      # one workgroup per row
 ])
 def test_index_topk_ties(K, B, L, k, n_distinct):
     """Pool rows repeat a few distinct keys in runs of 7, so each row's scores
@@ -199,6 +207,8 @@ def test_index_topk_ties(K, B, L, k, n_distinct):
     for r in range(B):
         assert np.array_equal(np.sort(idx[r][idx[r] >= 0]), np.sort(want[r][want[r] >= 0])), f"row {r}"
         assert np.array_equal(idx[r] >= 0, want[r] >= 0), f"row {r}: sentinel layout"
+        p = idx[r][idx[r] >= 0]
+        assert np.all(np.diff(p) > 0), f"row {r}: picks not in ascending order"
 
 
 # --------------------------------------------------------------------------- attention
