@@ -110,22 +110,38 @@ __device__ __forceinline__ RowPlan row_plan(const AttnArgs &A, int r) {
 // preserving order.  Block-wide; every index load is issued before the one
 // barrier; returns the count (sel[] is visible after the caller's next
 // barrier).  sh_cnt holds kMaxSel/64 ints.
+// The index entries of query row r a workgroup of NT threads compacts:
+// thread t holds entries t, t + NT, ... (issued early, used by compact_idx).
 template <int NT>
-__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cnt) {
+struct IdxPre {
+  int v[kMaxSel / NT];
+};
+template <int NT>
+__device__ __forceinline__ IdxPre<NT> load_idx(const AttnArgs &A, int r) {
+  constexpr int PER = kMaxSel / NT;
+  IdxPre<NT> p;
+  const int nq = (A.topk + NT - 1) / NT;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = q * NT + (int)threadIdx.x;
+    p.v[q] = (q < nq && i < A.topk) ? A.idx[(int64_t)r * A.topk + i] : -1;
+  }
+  return p;
+}
+
+// Compact the valid entries of idx[r, :] (>= 0 and < count) into sel[],
+// preserving order.  Block-wide, one barrier; returns the count (sel[] is
+// visible after the caller's next barrier).  sh_cnt holds kMaxSel/64 ints.
+template <int NT>
+__device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int b, int *sel, int *sh_cnt) {
   constexpr int NWV = NT / 64, PER = kMaxSel / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int cnt = A.pool.count[b];
   const int nq = (A.topk + NT - 1) / NT;
-  int v[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int i = q * NT + tid;
-    v[q] = (q < nq && i < A.topk) ? A.idx[(int64_t)r * A.topk + i] : -1;
-  }
   unsigned long long bal[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
-    bal[q] = __ballot(v[q] >= 0 && v[q] < cnt);
+    bal[q] = __ballot(pre.v[q] >= 0 && pre.v[q] < cnt);
     if (lane == 0 && q < nq) sh_cnt[q * NWV + wv] = __popcll(bal[q]);
   }
   __syncthreads();
@@ -139,9 +155,13 @@ __device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cn
       off += w < wv ? cw : 0;
       total += cw;
     }
-    if ((bal[q] >> lane) & 1ull) sel[off + __popcll(bal[q] & ((1ull << lane) - 1ull))] = v[q];
+    if ((bal[q] >> lane) & 1ull) sel[off + __popcll(bal[q] & ((1ull << lane) - 1ull))] = pre.v[q];
   }
   return total;
+}
+template <int NT>
+__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cnt) {
+  return compact_idx<NT>(A, load_idx<NT>(A, r), b, sel, sh_cnt);
 }
 
 // storage row (within its sequence) of window row i of a query
@@ -413,11 +433,27 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
 // fp16 rows (prefill: the compressor and the rope kernel emit fp16) land in
 // the tile as they are, one 1 KB row per wave instruction.  FP8 rows (decode
 // caches: 448 E4M3 bytes x row scale, then 64 bf16 rope channels, 576 B) land
-// as raw bytes, with their scales, in a second double buffer; one block-wide
-// pass then decodes the raw tile into the fp16 tile (every E4M3 value times its
-// fp32 scale, rounded once to fp16), so decoding is paid once per row per
+// as raw bytes, with their scales, in a raw buffer whose gather for tile i+1
+// is spread over the QK^T steps of tile i; one block-wide pass then decodes
+// the raw tile into the fp16 tile (scaled E4M3 -> fp16 conversion by the
+// scale's power of two, exact, then one fp16 multiply by its significand;
+// bf16 rope channels converted), so decoding is paid once per row per
 // workgroup instead of once per wave and MFMA operand.
 //
+// Waits written out, not left to the compiler's tracking of LDS DMA:
+// vm_wait_all: this wave's vector memory operations (DMAs included) are done.
+// lds_barrier: LDS writes visible to the workgroup, outstanding DMAs kept in
+// flight; the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }   // vmcnt(0)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -431,14 +467,14 @@ constexpr int kF8Nope = 448, kF8Row = kF8Nope + 2 * 64;
 constexpr int kF8Chunks = 32 * kF8Row / 1024;   // 1 KB DMA instructions per 32-row raw tile
 
 template <int NHB, int NW, bool FP8>
-__global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs A) {
+__global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
   constexpr int RB = FP8 ? kF8Row : 2 * D;   // stored row bytes
   static_assert(!FP8 || 32 * kF8Row % 1024 == 0, "raw tile must be whole DMA instructions");
   __shared__ __attribute__((aligned(16))) uint16_t T0[32 * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t T1[32 * KP];
-  __shared__ __attribute__((aligned(16))) uint8_t RW[FP8 ? 2 * 32 * kF8Row : 16];
-  __shared__ float RSC[FP8 ? 2 * 32 : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t T1[FP8 ? 8 : 32 * KP];   // FP8 rows: one fp16 tile
+  __shared__ __attribute__((aligned(16))) uint8_t RW[FP8 ? 32 * kF8Row : 16];
+  __shared__ float RSC[FP8 ? 32 : 1];
   __shared__ int sel[kMaxSel];
   __shared__ float rc[32], rs[32];
   __shared__ int sh_cnt[kMaxSel / 64];
@@ -457,6 +493,9 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
 #pragma unroll
     for (int j = 0; j < NJ; ++j) qb[hb][j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
   }
+  // the index entries next: their latency hides behind the row plan
+  IdxPre<NT> ipre;
+  if (A.csa && A.topk > 0) ipre = load_idx<NT>(A, r);
   RowPlan P = row_plan(A, r);
   const int R = A.rope_dim;
   const int nwin = P.nwin, csa = A.csa;
@@ -496,7 +535,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
   const bool early = !FP8 && A.nsplit == 1 && (csa ? nwin >= 32 : nrows > 0);
   if (early) gather(0, T0);
   if (csa && A.topk > 0) {
-    P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_cnt);
+    P.nsel = compact_idx<NT>(A, ipre, P.b, sel, sh_cnt);
     nrows = nwin + P.nsel;
   }
   const int ntiles = (nrows + 31) / 32;
@@ -512,69 +551,88 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
   // chunks w, w+NW, ...); lane l of chunk q copies bytes [1024q + 16l, +16) of
   // the tile, i.e. part of row (1024q + 16l) / 576.  The last wave also copies
   // the 32 row scales.
-  auto gather_raw = [&](int tile, int buf) {
-    const int rid = lane < 32 ? row_id(32 * tile + lane) : 0x7fffffff;
-    uint8_t *R = RW + buf * (32 * kF8Row);
+  // lane l of chunk k (k-th chunk of this wave, q = wv + NW*k) copies bytes
+  // [1024q + 16l, +16) of the tile, part of row (1024q + 16l) / 576; the row
+  // ids are read from LDS up front, then each DMA is one instruction
+  constexpr int CPW = (kF8Chunks + NW - 1) / NW;   // chunks per wave
+  auto raw_ids = [&](int tile, int (&rk)[CPW], int &rid) {
 #pragma unroll
-    for (int q = wv; q < kF8Chunks; q += NW) {
-      const int o = 1024 * q + 16 * lane;
-      const int row = o / kF8Row;
-      const int rk = __shfl(rid, row, 64);
-      if (rk != 0x7fffffff) {
-        const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB;
-        __builtin_amdgcn_global_load_lds(rp + (o - row * kF8Row), (lds_void *)(R + 1024 * q), 16, 0, 0);
-      }
+    for (int k = 0; k < CPW; ++k) {
+      const int q = wv + NW * k;
+      rk[k] = q < kF8Chunks ? row_id(32 * tile + (1024 * q + 16 * lane) / kF8Row) : 0x7fffffff;
     }
-    if (wv == NW - 1 && rid != 0x7fffffff) {
-      const float *sp = rid >= 0 ? wsc + rid : psc + (-1 - rid);
-      __builtin_amdgcn_global_load_lds(sp, (lds_void *)(RSC + 32 * buf), 4, 0, 0);
+    rid = (wv == NW - 1 && lane < 32) ? row_id(32 * tile + lane) : 0x7fffffff;
+  };
+  auto raw_chunk = [&](int k, int rkk, uint8_t *R) {
+    const int q = wv + NW * k;
+    if (q < kF8Chunks && rkk != 0x7fffffff) {
+      const int o = 1024 * q + 16 * lane, row = o / kF8Row;
+      const uint8_t *rp = rkk >= 0 ? wbase + (int64_t)rkk * RB : pbase + (int64_t)(-1 - rkk) * RB;
+      __builtin_amdgcn_global_load_lds(rp + (o - row * kF8Row), (lds_void *)(R + 1024 * q), 16, 0, 0);
     }
   };
+  auto raw_scale = [&](int rid, float *Sc) {
+    if (rid != 0x7fffffff) {
+      const float *sp = rid >= 0 ? wsc + rid : psc + (-1 - rid);
+      __builtin_amdgcn_global_load_lds(sp, (lds_void *)Sc, 4, 0, 0);
+    }
+  };
+  auto gather_raw = [&](int tile, uint8_t *R, float *Sc) {
+    int rk[CPW], rid;
+    raw_ids(tile, rk, rid);
+#pragma unroll
+    for (int k = 0; k < CPW; ++k) raw_chunk(k, rk[k], R);
+    raw_scale(rid, Sc);
+  };
   // FP8: decode raw tile buf into the fp16 tile T
-  auto convert = [&](int buf, uint16_t *T) {
-    const uint8_t *R = RW + buf * (32 * kF8Row);
-    const float *sc = RSC + 32 * buf;
+  auto convert = [&](const uint8_t *R, const float *sc, uint16_t *T) {
     constexpr int NI = 32 * (kF8Nope / 8), NU = (NI + NT - 1) / NT;   // items of 8 E4M3 codes
     constexpr int NR = (32 * 8 + NT - 1) / NT;                         // items of 8 bf16 rope channels
-    u32x2 v[NU];
-    float sv[NU];
-    u32x4 rv[NR];
+    constexpr int KB = 4;                                              // items read ahead per batch
 #pragma unroll
-    for (int k = 0; k < NU; ++k) {   // every LDS read first
-      const int u = tid + NT * k;
-      if (u < NI) {
-        const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
-        v[k] = *reinterpret_cast<const u32x2 *>(R + row * kF8Row + 8 * c8);
-        sv[k] = sc[row];
+    for (int k0 = 0; k0 < NU; k0 += KB) {
+      u32x2 v[KB];
+      float sv[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {   // the batch's LDS reads first
+        const int u = tid + NT * (k0 + k);
+        if (k0 + k < NU && u < NI) {
+          const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
+          v[k] = *reinterpret_cast<const u32x2 *>(R + row * kF8Row + 8 * c8);
+          sv[k] = sc[row];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int u = tid + NT * (k0 + k);
+        if (k0 + k < NU && u < NI) {
+          const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
+          // s = m 2^e: the conversion applies 2^e exactly (E4M3 values are
+          // exact in fp16), one fp16 multiply applies m in [1, 2)
+          const float s = sv[k];
+          const _Float16 m = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+          const h2 mm = h2{m, m};
+          const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].x, s, false) * mm;
+          const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].x, s, true) * mm;
+          const h2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].y, s, false) * mm;
+          const h2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].y, s, true) * mm;
+          uint32_t w[4];
+          __builtin_memcpy(&w[0], &a0, 4);
+          __builtin_memcpy(&w[1], &a1, 4);
+          __builtin_memcpy(&w[2], &a2, 4);
+          __builtin_memcpy(&w[3], &a3, 4);
+          *reinterpret_cast<u32x4 *>(T + row * KP + 8 * c8) = u32x4{w[0], w[1], w[2], w[3]};
+        }
       }
     }
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
       const int u = tid + NT * k;
-      if (u < 32 * 8) rv[k] = *reinterpret_cast<const u32x4 *>(R + (u >> 3) * kF8Row + kF8Nope + 16 * (u & 7));
-    }
-#pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int u = tid + NT * k;
-      if (u < NI) {
-        const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
-        const float s = sv[k];
-        const v2f a0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].x, false);
-        const v2f a1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].x, true);
-        const v2f a2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].y, false);
-        const v2f a3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[k].y, true);
-        *reinterpret_cast<u32x4 *>(T + row * KP + 8 * c8) =
-            u32x4{pack_f16x2(a0.x * s, a0.y * s), pack_f16x2(a1.x * s, a1.y * s), pack_f16x2(a2.x * s, a2.y * s),
-                  pack_f16x2(a3.x * s, a3.y * s)};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int u = tid + NT * k;
-      if (u < 32 * 8)
+      if (u < 32 * 8) {
+        const u32x4 rv = *reinterpret_cast<const u32x4 *>(R + (u >> 3) * kF8Row + kF8Nope + 16 * (u & 7));
         *reinterpret_cast<u32x4 *>(T + (u >> 3) * KP + kF8Nope + 8 * (u & 7)) =
-            u32x4{bf16x2_to_f16x2(rv[k].x), bf16x2_to_f16x2(rv[k].y), bf16x2_to_f16x2(rv[k].z),
-                  bf16x2_to_f16x2(rv[k].w)};
+            u32x4{bf16x2_to_f16x2(rv.x), bf16x2_to_f16x2(rv.y), bf16x2_to_f16x2(rv.z), bf16x2_to_f16x2(rv.w)};
+      }
     }
   };
 
@@ -622,8 +680,18 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
   // Tn/idn: the next tile's buffer and row ids (Tn == nullptr: nothing to
   // gather); its DMAs are spread over the k-steps of S^T so that their issue
   // (the texture path moves 64 B per clock per CU) overlaps the matrix cores
-  auto compute = [&](const uint16_t *T, int tile, uint16_t *Tn, int idn) -> bool {
+  auto compute = [&](const uint16_t *__restrict__ T, int tile, uint16_t *__restrict__ Tn, int idn,
+                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile) -> bool {
     const int base = 32 * tile;
+    // FP8 rows: the next raw tile's gather is issued during this tile's
+    // matrix work (its buffer is disjoint from T), one DMA per few k-steps
+    int grk[FP8 ? CPW : 1], grid_ = 0x7fffffff;
+    if constexpr (FP8) {
+      if (Rn) {
+        raw_ids(ntile, grk, grid_);
+        raw_scale(grid_, Sn);
+      }
+    }
     f32x4 s[NHB][2];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) { s[hb][0] = f32x4{0.f, 0.f, 0.f, 0.f}; s[hb][1] = s[hb][0]; }
@@ -654,6 +722,12 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
         if (Tn) {
 #pragma unroll
           for (int k = (j * RPW) / NJ; k < ((j + 1) * RPW) / NJ; ++k) dma_row(idn, k, Tn);
+        }
+        if constexpr (FP8) {
+          if (Rn) {
+#pragma unroll
+            for (int k = (j * CPW) / NJ; k < ((j + 1) * CPW) / NJ; ++k) raw_chunk(k, grk[k], Rn);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -727,37 +801,38 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 8 / NW) void k_attn_f16(AttnArgs
     int it = 0;
     if constexpr (!FP8) {
       if (tile_lo < tile_hi && !(early && pass == 0)) gather(tile_lo, T0);
-      __syncthreads();   // the first tile landed (the barrier waits for outstanding memory)
+      vm_wait_all();     // this wave's rows of the first tile landed ...
+      __syncthreads();   // ... and every wave's
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool odd = it & 1;
         const bool more = tile + 1 < tile_hi;
-        const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_ids(tile + 1) : 0);
+        const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_ids(tile + 1) : 0,
+                                  nullptr, nullptr, 0);
         if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
         if (tid == 0) rflag[(it + 1) & 1] = 0;
-        __syncthreads();   // next tile landed, this one fully read, flags visible
+        vm_wait_all();     // this wave's rows of the next tile landed ...
+        __syncthreads();   // ... and every wave's; this one fully read, flags visible
         if (rflag[it & 1]) { restart = true; break; }
       }
     } else {
-      // raw tile i+1 is in flight while tile i is on the matrix cores; the
-      // decode of raw i+1 into the other fp16 tile sits between two barriers
-      if (tile_lo < tile_hi) gather_raw(tile_lo, 0);
-      __syncthreads();   // raw tile landed (the barrier waits for outstanding memory)
-      if (tile_lo < tile_hi) convert(0, T0);
-      if (tile_lo + 1 < tile_hi) gather_raw(tile_lo + 1, 1);
-      __syncthreads();
+      // one raw buffer and one fp16 tile (two workgroups share a CU, so one's
+      // waits overlap the other's matrix work): raw tile i+1 is gathered
+      // during compute(i), then decoded into the tile compute(i) just read
+      if (tile_lo < tile_hi) gather_raw(tile_lo, RW, RSC);
+      vm_wait_all();     // this wave's part of the raw tile landed ...
+      __syncthreads();   // ... and every wave's
+      if (tile_lo < tile_hi) convert(RW, RSC, T0);
+      lds_barrier();
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
-        const bool odd = it & 1;
-        const bool over = compute(odd ? T1 : T0, tile, nullptr, 0);
+        const bool more = tile + 1 < tile_hi;
+        const bool over = compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1);
         if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
         if (tid == 0) rflag[(it + 1) & 1] = 0;
-        __syncthreads();   // raw tile+1 landed, this tile fully read, flags visible
+        vm_wait_all();     // this wave's part of raw tile+1 landed ...
+        __syncthreads();   // ... and every wave's; the tile fully read, flags visible
         if (rflag[it & 1]) { restart = true; break; }
-        // raw buffer `odd` was decoded last iteration: refill it first, then decode the other
-        if (tile + 2 < tile_hi) gather_raw(tile + 2, odd ? 1 : 0);
-        if (tile + 1 < tile_hi) convert(odd ? 0 : 1, odd ? T0 : T1);
-        // make the decoded tile visible without waiting for the gather just issued
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
+        if (more) convert(RW, RSC, T0);
+        lds_barrier();
       }
     }
     if (!restart) break;
