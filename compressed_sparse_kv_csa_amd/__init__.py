@@ -23,7 +23,7 @@ DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, 
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
            "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant",
-           "dsv4_quantize", "dsv4_cache_append", "dsv4_last_error", "dsv4_version"]
+           "dsv4_quantize", "dsv4_cache_append", "dsv4_linear", "dsv4_last_error", "dsv4_version"]
 
 
 class Dsv4Error(RuntimeError):
@@ -85,6 +85,7 @@ def lib():
         L.dsv4_set_batch_invariant.argtypes = [I32]
         L.dsv4_quantize.argtypes = [P, I32, I64, I32, I32, P, P, P, I32, P]
         L.dsv4_cache_append.argtypes = [P, I32, P, P, P, P, P, P, I32, P]
+        L.dsv4_linear.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, I32, I32, I64, I64, I64, P]
         L.dsv4_last_error.restype = ctypes.c_char_p
         L.dsv4_version.restype = ctypes.c_char_p
         for name in EXPORTS:
@@ -105,6 +106,15 @@ def _ptr(t: Optional[torch.Tensor]):
         raise ValueError("dsv4 tensors must live in device memory")
     if not t.is_contiguous():
         raise ValueError("dsv4 tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _ptr_rows(t: torch.Tensor):
+    """Pointer of a 2-D tensor whose rows may be strided (unit column stride)."""
+    if not t.is_cuda:
+        raise ValueError("dsv4 tensors must live in device memory")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with contiguous rows")
     return t.data_ptr()
 
 
@@ -378,6 +388,28 @@ def dsv4_hca_attn(q: QueryRows, qv: torch.Tensor, window: Optional[RowStore], W:
                                ctypes.byref(pc) if pc is not None else None, m, _ptr(sinks), float(sm_scale),
                                rope_dim, float(rope_theta), _ptr(out), _code(out), _ptr(ws), nbytes, _stream()))
     return out
+
+
+def dsv4_linear(x: torch.Tensor, w: torch.Tensor, out_dtype: Optional[torch.dtype] = None,
+                groups: int = 1, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y = X W^T (bf16 in, fp32 accumulate).  groups = 1: x [M, K], w [N, K] ->
+    y [M, N].  groups = G: x [M, G*K] (group g = columns g*K .. g*K+K-1),
+    w [G, N, K] -> y [M, G*N]."""
+    assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16, "bf16 operands"
+    M = x.shape[0]
+    if groups == 1:
+        N, K = w.shape
+        assert x.shape[-1] == K
+        gx = gw = gy = 0
+    else:
+        G, N, K = w.shape
+        assert G == groups and x.shape[-1] == G * K
+        gx, gw, gy = K, N * K, N
+    y = out if out is not None else torch.empty(M, groups * N, dtype=out_dtype or torch.bfloat16, device=x.device)
+    assert y.shape == (M, groups * N)
+    _check(lib().dsv4_linear(_ptr_rows(x), x.stride(0), _ptr(w), K, _ptr_rows(y), y.stride(0), _code(y), M, N, K,
+                             groups, gx, gw, gy, _stream(stream)))
+    return y
 
 
 def dsv4_quantize(x: torch.Tensor, out_dtype: int, tail: int = 0):

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdsv4.so")
-SOURCES = ["dsv4_api.cpp", "dsv4_compress.hip", "dsv4_indexer.hip", "dsv4_attn.hip", "dsv4_quant.hip", "dsv4_cache.hip"]
+SOURCES = ["dsv4_api.cpp", "dsv4_compress.hip", "dsv4_indexer.hip", "dsv4_attn.hip", "dsv4_quant.hip", "dsv4_cache.hip", "dsv4_linear.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -43,6 +43,8 @@ size_t attn_ws(int T, int H, int D, int64_t max_rows);
 int set_batch_invariant(bool on);
 int launch_cache_append(const dsv4_cache *C, int n, const int32_t *n_new, const void *kv, const void *kv_c,
                         const void *kv_z, const void *idx_c, const void *idx_z, int in_dtype, hipStream_t st);
+int launch_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, void *y, int64_t ldy, int y_dtype, int M,
+                  int N, int K, int groups, int64_t gx, int64_t gw, int64_t gy, hipStream_t st);
 int launch_quantize(const void *x, int x_dtype, int64_t n, int dim, int tail, void *rows, float *row_scale,
                     uint8_t *blk_scale, int out_dtype, hipStream_t st);
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
@@ -171,6 +173,26 @@ int dsv4_cache_append(const dsv4_cache *C, int32_t n, const int32_t *n_new, cons
                         (C->idx.dim ? 2 : 1) * (((int64_t)n + C->m - 1) / C->m);
   if (items > 0x7fffffff) return fail(DSV4_ENOTSUP, "cache_append: n %d too large for one append", n);
   rc = launch_cache_append(C, n, n_new, kv, kv_c, kv_z, idx_c, idx_z, in_dtype, stream);
+  return rc ? rc : ok();
+}
+
+int dsv4_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, void *y, int64_t ldy, int32_t y_dtype,
+                int32_t M, int32_t N, int32_t K, int32_t groups, int64_t x_group_stride, int64_t w_group_stride,
+                int64_t y_group_stride, hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0 || groups < 0) return fail(DSV4_EINVAL, "linear: M %d N %d K %d groups %d", M, N, K, groups);
+  if (M == 0 || N == 0 || groups == 0) return ok();
+  if (!x || !w || !y) return fail(DSV4_EINVAL, "linear: NULL x/w/y");
+  if (K == 0 || K % 64) return fail(DSV4_ENOTSUP, "linear: K %d (a positive multiple of 64)", K);
+  if (y_dtype != DSV4_F32 && y_dtype != DSV4_BF16 && y_dtype != DSV4_F16)
+    return fail(DSV4_ENOTSUP, "linear: output dtype %d (F32, BF16 or F16)", y_dtype);
+  if (ldx < K || ldw < K || ldy < N || ldx % 8 || ldw % 8)
+    return fail(DSV4_EINVAL, "linear: row strides x %lld w %lld (>= K, multiples of 8) y %lld (>= N)", (long long)ldx,
+                (long long)ldw, (long long)ldy);
+  if ((x_group_stride | w_group_stride) % 8 || (((uintptr_t)x | (uintptr_t)w) & 15))
+    return fail(DSV4_EINVAL, "linear: x and w must be 16-byte aligned with group strides that keep them so");
+  if (M > 65535 * 128 || groups > 65535) return fail(DSV4_ENOTSUP, "linear: M %d / groups %d too large", M, groups);
+  const int rc = launch_linear(x, ldx, w, ldw, y, ldy, y_dtype, M, N, K, groups, x_group_stride, w_group_stride,
+                               y_group_stride, stream);
   return rc ? rc : ok();
 }
 

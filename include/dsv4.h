@@ -294,6 +294,25 @@ int dsv4_cache_append(const dsv4_cache *cache, int32_t n, const int32_t *n_new, 
                       const void *kv_c, const void *kv_z, const void *idx_c, const void *idx_z,
                       int32_t in_dtype, hipStream_t stream);
 
+/* dsv4_linear -- the projections around the attention core: Y = X W^T.
+ * HF DeepSeek-V4 page, "Hybrid attention": kv_proj makes the single K=V head,
+ * and the output goes through the grouped low-rank projection (o_groups head
+ * groups, each to o_lora_rank by its own weight, then o_b_proj to
+ * hidden_size); llm-atlas config: hidden_size 4096, q_lora_rank 1024,
+ * o_groups 8, o_lora_rank 1024.  For g < groups, m < M, n < N:
+ *   y[g*y_group_stride + m*ldy + n] =
+ *       sum_{k<K} x[g*x_group_stride + m*ldx + k] * w[g*w_group_stride + n*ldw + k]
+ * accumulated in fp32.  x and w are bfloat16 (row-major, K contiguous: weights
+ * stored [out, in]); y is y_dtype (DSV4_F32, DSV4_BF16 or DSV4_F16).  Strides
+ * are in elements.  K must be a multiple of 64; x, w 16-byte aligned with row
+ * and group strides that are multiples of 8.  groups = 1 with zero group
+ * strides is one plain product; the grouped output projection is groups = 8
+ * with x the attention output viewed as [T, 8, 4096] (x_group_stride 4096,
+ * ldx 32768). */
+int dsv4_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, void *y, int64_t ldy, int32_t y_dtype,
+                int32_t M, int32_t N, int32_t K, int32_t groups, int64_t x_group_stride,
+                int64_t w_group_stride, int64_t y_group_stride, hipStream_t stream);
+
 /* Thread-local description of the last error (empty string after success). */
 const char *dsv4_last_error(void);
 

@@ -290,3 +290,29 @@ def attn(q_seq, q_tok, pos0, q, q_kind: str, win, W: int, pool, mode: str, idx=N
                  _p(idx) if mode == "csa" else None, k, m, _p(sk), float(sm_scale),
                  rope_dim, float(theta), out.ctypes.data)
     return out
+
+
+# ---------------------------------------------------------------- projections
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """P1 -- one projection y = x W^T, fp64 (weights stored [out, in]).
+
+    HF DeepSeek-V4 page, "Hybrid attention": kv_proj makes the single K=V head
+    (and the other projections around the core are plain linear maps of the
+    hidden states).  x: [..., K] (any float, taken exactly), w: [N, K].
+    Returns fp64 [..., N]."""
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def grouped_linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """P2 -- grouped projection, fp64.
+
+    HF DeepSeek-V4 page, "Hybrid attention", grouped low-rank output
+    projection: the heads are split into o_groups groups and each group's
+    concatenated head outputs go through its own [o_lora_rank, group width]
+    weight.  x: [M, G*K] (group g = columns gK .. gK+K-1), w: [G, N, K].
+    Returns fp64 [M, G*N] (group g's outputs at columns gN .. gN+N-1)."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    G, N, K = w.shape
+    assert x.shape[-1] == G * K
+    return np.concatenate([x[:, g * K:(g + 1) * K] @ w[g].T for g in range(G)], axis=-1)

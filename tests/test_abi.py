@@ -228,3 +228,21 @@ def test_ring_windows_only(K):
     rc = _rc(L.dsv4_sparse_attn(ctypes.byref(q), f, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128, None, None, 0,
                                 None, 0.04, 64, 1e4, f, K.DSV4_BF16, f, 1 << 30, None))
     assert rc == K.DSV4_EINVAL
+
+
+def test_linear_rejects_bad_args(K):
+    L = K.lib()
+    f = ctypes.c_void_p(0x1000)
+
+    def call(M=4, N=4, Kd=64, ldx=64, ldw=64, ldy=4, dt=0, groups=1, gx=0, gw=0, gy=0, x=f):
+        return _rc(L.dsv4_linear(x, ldx, f, ldw, f, ldy, dt, M, N, Kd, groups, gx, gw, gy, None))
+
+    assert call(M=0) == K.DSV4_OK                     # empty product: nothing launched
+    assert call(M=-1) == K.DSV4_EINVAL
+    assert call(x=None) == K.DSV4_EINVAL
+    assert call(Kd=96, ldx=96, ldw=96) == K.DSV4_ENOTSUP   # K not a multiple of 64
+    assert call(dt=K.DSV4_FP8R) == K.DSV4_ENOTSUP
+    assert call(ldx=32) == K.DSV4_EINVAL              # row stride below K
+    assert call(ldy=2) == K.DSV4_EINVAL
+    assert call(ldx=68) == K.DSV4_EINVAL              # rows not 16-byte aligned
+    assert call(groups=2, gx=4) == K.DSV4_EINVAL
