@@ -332,8 +332,66 @@ class MixedDecode:
                         ws=self.ws_hca, out=self.hout)
 
 
+class CsaBlock(CsaPrefill):
+    """The Flash CSA attention block from hidden states (batch 1, seq 8192):
+    the projections (low-rank q 4096 -> 1024 -> 64 x 512, kv, compressor and
+    indexer projections from x) as dsv4_linear products, the CSA core as in
+    CsaPrefill, then the grouped low-rank output projection (8 groups of
+    8 heads x 512 -> 1024 each) and o_b (8192 -> 4096).  x ~ N(0, 1), weights
+    ~ N(0, 0.02^2) (the config's initializer range), all bf16."""
+    name = "flash_csa_block_S8192"
+
+    def __init__(self, torch, K, S_, seed=1006, S=8192, hidden=4096, q_lora=1024, o_groups=8, o_lora=1024, **kw):
+        super().__init__(torch, K, S_, S=S, **kw)
+        bf = torch.bfloat16
+        H, D, Hi, Di = self.H, self.D, self.Hi, self.Di
+        dr = lambda name, shape, s: S_.draw_torch(seed, name, shape, s, bf)
+        self.hidden, self.o_groups, self.o_lora = hidden, o_groups, o_lora
+        self.x = dr("x", (S, hidden), 1.0)
+        ws = 0.02
+        self.Wqa = dr("W_qa", (q_lora, hidden), ws)
+        self.Wqb = dr("W_qb", (H * D, q_lora), ws)
+        self.Wkv = dr("W_kv", (D, hidden), ws)
+        self.Wc = dr("W_c", (D, hidden), ws)
+        self.Wz = dr("W_z", (D, hidden), ws)
+        self.WqI = dr("W_qI", (Hi * Di, hidden), ws)
+        self.Ww = dr("W_w", (Hi, hidden), ws)
+        self.WcI = dr("W_cI", (Di, hidden), ws)
+        self.WzI = dr("W_zI", (Di, hidden), ws)
+        self.Woa = dr("W_oa", (o_groups, o_lora, H * D // o_groups), ws)
+        self.Wob = dr("W_ob", (hidden, o_groups * o_lora), ws)
+        dev = self.x.device
+        self.qa = torch.empty(S, q_lora, dtype=bf, device=dev)
+        self.oa = torch.empty(S, o_groups * o_lora, dtype=bf, device=dev)
+        self.y = torch.empty(S, hidden, dtype=bf, device=dev)
+        Hg = H * D // o_groups
+        self.gemm_flop = 2 * S * (hidden * (q_lora + 3 * D + Hi * Di + Hi + 2 * Di) + q_lora * H * D
+                                  + o_groups * o_lora * Hg + o_groups * o_lora * hidden)
+        self.qb_flop = 2 * S * q_lora * H * D
+
+    def step(self, ev=None):
+        K, S = self.K, self.S
+        lin = K.dsv4_linear
+        lin(self.x, self.Wqa, out=self.qa)
+        if ev is not None:
+            ev[0].record()
+        lin(self.qa, self.Wqb, out=self.q.view(S, -1))
+        if ev is not None:
+            ev[1].record()
+        lin(self.x, self.Wkv, out=self.kv)
+        lin(self.x, self.Wc, out=self.c.view(S, -1))
+        lin(self.x, self.Wz, out=self.z.view(S, -1))
+        lin(self.x, self.WqI, out=self.q_idx.view(S, -1))
+        lin(self.x, self.Ww, out=self.w)
+        lin(self.x, self.WcI, out=self.c_idx.view(S, -1))
+        lin(self.x, self.WzI, out=self.z_idx.view(S, -1))
+        super().step()
+        lin(self.out.view(S, -1), self.Woa, groups=self.o_groups, out=self.oa)
+        lin(self.oa, self.Wob, out=self.y)
+
+
 WORKLOADS = {"csa_prefill": CsaPrefill, "hca_prefill": HcaPrefill, "csa_decode": CsaDecode,
-             "mixed_decode": MixedDecode}
+             "mixed_decode": MixedDecode, "csa_block": CsaBlock}
 
 
 def time_steps(torch, wl, steps, warmup):
@@ -503,7 +561,19 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded, device-drawn N(0,1.28^2) activations)",
            "timing": timing, "ms_per_step_eager": round(ms_eager, 4)}
-    if isinstance(wl, (CsaPrefill, HcaPrefill)):
+    if isinstance(wl, CsaBlock):
+        rec["value"] = round(wl.tokens() / (ms / 1e3), 1)
+        rec["unit"] = "tokens/s"
+        ach = wl.qb_flop / (kern_ms / 1e3) / 1e12
+        rec["roofline"] = {"bound": "mfma", "kernel": "k_linear (q_b projection, bf16 MFMA, fp32 accumulate)",
+                           "achieved": round(ach, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
+                           "frac": round(ach / PEAK_MFMA_F16, 4), "traffic": None,
+                           "algorithmic": f"{wl.qb_flop / 1e9:.1f} GFLOP per launch (8192 x 32768 x 1024 x 2)",
+                           "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_median": round(kern_med, 4)}
+        rec["config"] = {"workload": wl.name, "seq_len": wl.S, "hidden": wl.hidden, "heads": wl.H,
+                         "head_dim": wl.D, "o_groups": wl.o_groups, "o_lora_rank": wl.o_lora,
+                         "projection_gflop": round(wl.gemm_flop / 1e9, 1)}
+    elif isinstance(wl, (CsaPrefill, HcaPrefill)):
         rec["value"] = round(wl.tokens() / (ms / 1e3), 1)
         rec["unit"] = "tokens/s"
         flop = wl.counts["attn_flop"]
@@ -543,7 +613,7 @@ def main():
         legs = {}
         del wl
         torch.cuda.empty_cache()
-        for name in ("hca_prefill", "csa_decode", "mixed_decode"):
+        for name in ("hca_prefill", "csa_decode", "mixed_decode", "csa_block"):
             log("leg", name)
             lw = WORKLOADS[name](torch, K, S_)
             torch.cuda.synchronize()
@@ -551,7 +621,15 @@ def main():
             if not args.no_graph:
                 gms = time_steps_graph(torch, lw, args.leg_steps, 2)
                 lms = gms if gms is not None else lms
-            if isinstance(lw, HcaPrefill):
+            if isinstance(lw, CsaBlock):
+                ach = lw.qb_flop / (lk / 1e3) / 1e12
+                tot = (lw.gemm_flop + lw.counts["attn_flop"] + lw.counts.get("index_flop", 0)) / (lms / 1e3) / 1e12
+                legs[name] = {"workload": lw.name, "tokens_per_s": round(lw.tokens() / (lms / 1e3), 1),
+                              "ms_per_step": round(lms, 3), "block_tflops": round(tot, 1),
+                              "projection_gflop": round(lw.gemm_flop / 1e9, 1),
+                              "q_b_gemm_ms": round(lk, 3), "q_b_gemm_tflops": round(ach, 1),
+                              "q_b_gemm_frac_mfma_peak": round(ach / PEAK_MFMA_F16, 4)}
+            elif isinstance(lw, HcaPrefill):
                 ach = lw.counts["attn_flop"] / (lk / 1e3) / 1e12
                 legs[name] = {"workload": lw.name, "tokens_per_s": round(lw.tokens() / (lms / 1e3), 1),
                               "ms_per_step": round(lms, 3), "attn_kernel_ms": round(lk, 3),
