@@ -37,7 +37,9 @@ def _tol_close(got, ref, K_, what):
 
 @pytest.mark.parametrize("M,N,Kd,out", [(1, 16, 64, torch.float32), (300, 200, 192, torch.float32),
                                         (129, 513, 256, torch.bfloat16), (128, 128, 4096, torch.float32),
-                                        (37, 11072, 128, torch.float16), (700, 64, 1024, torch.float32)])
+                                        (37, 11072, 128, torch.float16), (700, 64, 1024, torch.float32),
+                                        # 256 x 256 tiles with ragged edges in both dimensions
+                                        (1300, 1100, 128, torch.float32), (1030, 2049, 256, torch.bfloat16)])
 def test_linear(K, M, N, Kd, out):
     say("linear", M, N, Kd, out)
     rng = np.random.default_rng(M * 7 + N)
