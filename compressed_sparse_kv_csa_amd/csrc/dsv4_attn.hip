@@ -26,8 +26,9 @@
 // q~ and P four times smaller than bf16 would, which matters when a query has
 // only a few rows and every logit error moves the output directly.  FP8 rows
 // (E4M3 x row scale, bf16 rope channels) are decoded to fp16 while staging.
-// Several splits per query (decode) write unnormalised partials that
-// k_attn_combine merges with the sink.
+// Several splits per query (decode) each write their output normalised by
+// their own sum (fp16: a convex combination of rows stays in the rows' range)
+// with their (max, sum) in fp32; k_attn_combine merges them with the sink.
 //
 // k_attn_f32: scalar fp32 path for small fp32 shapes.
 #include "dsv4_common.h"
@@ -65,8 +66,8 @@ struct AttnArgs {
   void *out;
   int out_dtype;
   int nsplit;
-  float *part_o;      // [T*nsplit*H, D]
-  float *part_ml;     // [T*nsplit*H, 2]
+  uint16_t *part_o;   // [T*nsplit*H, D] fp16: each split's output normalised by its own sum
+  float *part_ml;     // [T*nsplit*H, 2]: the split's reference maximum (log2 units) and sum
 };
 
 constexpr int kMaxSel = 2048;
@@ -377,10 +378,14 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
 
   if (A.nsplit > 1) {
     const int64_t pr = ((int64_t)r * A.nsplit + split) * A.H + h;
-    float *po = A.part_o + pr * D;
+    uint16_t *po = A.part_o + pr * D;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;   // normalised: within the rows' range, fp16-safe
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * g) = acc_o[db];
+    for (int db = 0; db < NDB; ++db) {
+      const f32x4 a = acc_o[db];
+      *reinterpret_cast<u32x2 *>(po + 16 * db + 4 * g) =
+          u32x2{pack_f16x2(a[0] * inv, a[1] * inv), pack_f16x2(a[2] * inv, a[3] * inv)};
+    }
     if (g == 0) {
       A.part_ml[2 * pr] = m_run;
       A.part_ml[2 * pr + 1] = l_run;
@@ -852,9 +857,14 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     const float mr = m_ref[hb];
     if (A.nsplit > 1) {
       const int64_t pr = ((int64_t)r * A.nsplit + split) * A.H + h;
-      float *po = A.part_o + pr * D;
+      uint16_t *po = A.part_o + pr * D;
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;   // normalised: within the rows' range, fp16-safe
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) *reinterpret_cast<f32x4 *>(po + 16 * db + 4 * g) = acc_o[hb][db];
+      for (int db = 0; db < NDB; ++db) {
+        const f32x4 a = acc_o[hb][db];
+        *reinterpret_cast<u32x2 *>(po + 16 * db + 4 * g) =
+            u32x2{pack_f16x2(a[0] * inv, a[1] * inv), pack_f16x2(a[2] * inv, a[3] * inv)};
+      }
       if (g == 0) {
         A.part_ml[2 * pr] = mr;
         A.part_ml[2 * pr + 1] = lr;
@@ -915,11 +925,15 @@ __global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
     const int64_t q = ((int64_t)r * A.nsplit + s) * A.H + h;
     const float ms = A.part_ml[2 * q];
     if (ms == -INFINITY) continue;   // split without rows
-    const float f = exp2f(ms - M);
-    den += A.part_ml[2 * q + 1] * f;
-    const float2 v = reinterpret_cast<const float2 *>(A.part_o + q * D)[pr];
-    o0 = fmaf(v.x, f, o0);
-    o1 = fmaf(v.y, f, o1);
+    const float f = A.part_ml[2 * q + 1] * exp2f(ms - M);   // the split's weight: its sum at the common max
+    den += f;
+    const uint32_t u = reinterpret_cast<const uint32_t *>(A.part_o + q * D)[pr];
+    _Float16 h0, h1;
+    const uint16_t lo = (uint16_t)(u & 0xFFFFu), hi = (uint16_t)(u >> 16);
+    __builtin_memcpy(&h0, &lo, 2);
+    __builtin_memcpy(&h1, &hi, 2);
+    o0 = fmaf((float)h0, f, o0);
+    o1 = fmaf((float)h1, f, o1);
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   o0 *= inv;
@@ -1111,7 +1125,7 @@ int attn_nsplit(int T, int64_t max_rows) {
 size_t attn_ws(int T, int H, int D, int64_t max_rows) {
   const int ns = attn_nsplit(T, max_rows);
   if (ns <= 1) return 0;
-  return (size_t)T * ns * H * ((size_t)D + 2) * 4 + 256;
+  return (size_t)T * ns * H * ((size_t)D * 2 + 8) + 256;   // fp16 outputs, fp32 (max, sum)
 }
 
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
@@ -1151,8 +1165,8 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   const int ns = attn_nsplit(T, max_rows);
   A.nsplit = ns;
   if (ns > 1) {
-    A.part_o = (float *)ws;
-    A.part_ml = A.part_o + (size_t)T * ns * H * D;
+    A.part_o = (uint16_t *)ws;
+    A.part_ml = (float *)(A.part_o + (size_t)T * ns * H * D);
   }
   const bool fp8 = (W > 0 && win->dtype == DSV4_FP8R) || (pool && pool->dtype == DSV4_FP8R);
   const bool f16 = (W > 0 ? win->dtype == DSV4_F16 : true) && (pool ? pool->dtype == DSV4_F16 : true) &&
