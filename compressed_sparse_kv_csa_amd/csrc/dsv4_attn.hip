@@ -427,13 +427,25 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
 }
 
 // ---------------------------------------------------------------- fp16 / FP8 rows, DMA-staged
-// k_attn_f16<NHB, NW, FP8>: the fast path.  NW waves, each owning 16*NHB heads
-// (64 heads: 4 waves x 16 heads; the accumulators of 16 heads x 512 dims stay
-// in VGPRs).  Rows are gathered straight from global memory into LDS with
+// k_attn_f16<NHB, NW, FP8>: the fast path.  NW waves; for S^T each wave owns
+// 16*NHB heads.  Rows are gathered straight from global memory into LDS with
 // global_load_lds_dwordx4 (no VGPR staging), double-buffered: the gather of
 // tile i+1 is in flight while tile i is on the matrix cores.  The PV operand
 // V^T comes from the same row-major fp16 tile through ds_read_b64_tr_b16 (a
 // 16x4 transpose inside each 16-lane group), so no transposed copy is written.
+//
+// fp16 rows with 16, 32 or 64 heads split PV by output channel instead of by
+// head: after S^T and the softmax, every wave writes its 16-head P^T fragment
+// to LDS, and after one barrier wave w accumulates O^T for all heads over
+// channels [w D/NW, (w+1) D/NW).  Each V^T fragment read from LDS then feeds
+// NW matrix products, and the tile's V^T is read once per workgroup instead of
+// once per wave (the transposing reads run at about half the rate of plain
+// 16-byte reads).  The accumulators stay 128 VGPRs per wave either way.  The
+// next tile's eight 1 KB row DMAs per wave are issued right before that
+// barrier, where a wave waits for the others' scores anyway; a lane holds one
+// row address so that each DMA is two lane reads and scalar LDS addressing.
+// bf16 outputs are staged in the idle tile buffers, heads as rows, so that
+// every global store writes a whole 1 KB head row.
 //
 // fp16 rows (prefill: the compressor and the rope kernel emit fp16) land in
 // the tile as they are, one 1 KB row per wave instruction.  FP8 rows (decode
@@ -475,6 +487,13 @@ template <int NHB, int NW, bool FP8>
 __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
   constexpr int RB = FP8 ? kF8Row : 2 * D;   // stored row bytes
+  // Dimension-split PV (fp16 rows, one 16-head block per wave, NW | 32): every
+  // wave publishes its P^T fragment in LDS and accumulates O^T for all heads
+  // over its own D/NW output channels, so each V^T fragment read from LDS feeds
+  // NW products instead of one (the tile's V^T is read once per workgroup, not
+  // once per wave).  AH: head blocks and DB: 16-channel blocks a wave accumulates.
+  constexpr bool DSPV = !FP8 && NHB == 1 && (NW == 1 || NW == 2 || NW == 4);
+  constexpr int AH = DSPV ? NW : NHB, DB = DSPV ? NDB / NW : NDB;
   static_assert(!FP8 || 32 * kF8Row % 1024 == 0, "raw tile must be whole DMA instructions");
   __shared__ __attribute__((aligned(16))) uint16_t T0[32 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t T1[FP8 ? 8 : 32 * KP];   // FP8 rows: one fp16 tile
@@ -482,8 +501,10 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   __shared__ float RSC[FP8 ? 32 : 1];
   __shared__ int sel[kMaxSel];
   __shared__ float rc[32], rs[32];
+  __shared__ float sk[64];   // the heads' sinks (log2 units), loaded with the setup
   __shared__ int sh_cnt[kMaxSel / 64];
   __shared__ int rflag[2];
+  __shared__ __attribute__((aligned(16))) uint16_t PB[DSPV ? NW * 64 * 8 : 8];   // P^T fragments, wave-major
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -520,20 +541,24 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     return i < nwin ? win_slot(A, P, i) : -1 - (csa ? sel[i - nwin] : i - nwin);
   };
   constexpr int RPW = (32 + NW - 1) / NW;   // tile rows per wave (wave w: rows w, w+NW, ...)
-  auto tile_ids = [&](int tile) -> int {    // lane k < RPW: id of row wv + NW*k of the tile
-    return (lane < RPW && wv + NW * lane < 32) ? row_id(32 * tile + wv + NW * lane) : 0x7fffffff;
+  // lane k < RPW: global address of row wv + NW*k of the tile (0: no such row),
+  // so that one DMA takes two lane reads and scalar LDS addressing
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  auto tile_addr = [&](int tile) -> uint64_t {
+    if (!(lane < RPW && wv + NW * lane < 32)) return 0;
+    const int rk = row_id(32 * tile + wv + NW * lane);
+    return (uint64_t)(rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB);
   };
-  auto dma_row = [&](int ids, int k, uint16_t *T) {   // row wv + NW*k of a tile, one 1 KB DMA
-    const int rk = __builtin_amdgcn_readlane(ids, k);
-    if (rk != 0x7fffffff) {
-      const uint8_t *rp = rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB;
-      __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wv + NW * k) * KP), 16, 0, 0);
-    }
+  auto dma_row = [&](uint64_t ad, int k, uint16_t *T) {   // row wv + NW*k of a tile, one 1 KB DMA
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)ad, k);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(ad >> 32), k);
+    const uint8_t *rp = (const uint8_t *)(((uint64_t)hi << 32) | lo);
+    if (rp) __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wvs + NW * k) * KP), 16, 0, 0);
   };
   auto gather = [&](int tile, uint16_t *T) {
-    const int ids = tile_ids(tile);
+    const uint64_t ad = tile_addr(tile);
 #pragma unroll
-    for (int k = 0; k < RPW; ++k) dma_row(ids, k, T);
+    for (int k = 0; k < RPW; ++k) dma_row(ad, k, T);
   };
   // the first tile can be in flight during the compaction when its rows are
   // known without it: window rows (CSA prefill: the newest 32 tokens) or HCA rows
@@ -549,6 +574,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   const int tile_hi = min(ntiles, tile_lo + tps);
 
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
+  if (tid < A.H) sk[tid] = A.sinks ? A.sinks[tid] * kLog2e : -INFINITY;
   if (tid < 2) rflag[tid] = 0;
   __syncthreads();
 
@@ -675,7 +701,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     }
   }
 
-  f32x4 acc_o[NHB][NDB];
+  f32x4 acc_o[AH][DB];
   float m_ref[NHB], m_seen[NHB], l_run[NHB];
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) { m_ref[hb] = -INFINITY; m_seen[hb] = -INFINITY; }
@@ -685,8 +711,8 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // Tn/idn: the next tile's buffer and row ids (Tn == nullptr: nothing to
   // gather); its DMAs are spread over the k-steps of S^T so that their issue
   // (the texture path moves 64 B per clock per CU) overlaps the matrix cores
-  auto compute = [&](const uint16_t *__restrict__ T, int tile, uint16_t *__restrict__ Tn, int idn,
-                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile) -> bool {
+  auto compute = [&](const uint16_t *__restrict__ T, int tile, uint16_t *__restrict__ Tn, uint64_t idn,
+                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile, int fl) -> bool {
     const int base = 32 * tile;
     // FP8 rows: the next raw tile's gather is issued during this tile's
     // matrix work (its buffer is disjoint from T), one DMA per few k-steps
@@ -724,7 +750,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
           s[hb][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[hb][j], s[hb][0], 0, 0, 0);
           s[hb][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[hb][j], s[hb][1], 0, 0, 0);
         }
-        if (Tn) {
+        if (!DSPV && Tn) {
 #pragma unroll
           for (int k = (j * RPW) / NJ; k < ((j + 1) * RPW) / NJ; ++k) dma_row(idn, k, Tn);
         }
@@ -759,13 +785,60 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[4 * mb + i] = exp2f(s[hb][mb][i] - m_ref[hb]);
+          p[4 * mb + i] = __builtin_amdgcn_exp2f(s[hb][mb][i] - m_ref[hb]);
           psum += p[4 * mb + i];
         }
       l_run[hb] += psum;
       const u32x4 pw = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
                              pack_f16x2(p[6], p[7])};
       __builtin_memcpy(&pb[hb], &pw, 16);
+    }
+    if constexpr (DSPV) {
+      // every wave's P^T fragment to LDS (PB was last read before the previous
+      // tile's closing barrier), then O^T[this wave's channels, all heads]
+      *reinterpret_cast<f16x8 *>(PB + (wv * 64 + lane) * 8) = pb[0];
+      if (__ballot(over) && lane == 0) rflag[fl] = 1;   // raised before the barrier: nothing live across PV
+      // the running sum and maximum settled here, so no probability stays live across PV
+      asm volatile("" : "+v"(l_run[0]), "+v"(m_seen[0]));
+      // the next tile's gather: issued where the wave would wait for the others'
+      // scores anyway (its buffer was released by the previous tile's closing barrier)
+      if (Tn) {
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) dma_row(idn, k, Tn);
+      }
+      lds_barrier();   // P^T of every wave visible; the next tile's DMAs stay in flight
+      // head blocks in groups of HG (P^T fragments live: HG; V^T read NW/HG times)
+      constexpr int HG = NW;
+      const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * DB * wv;
+      const uint16_t *v1p = v0p + 16 * KP;
+#pragma unroll
+      for (int w0 = 0; w0 < NW; w0 += HG) {
+        f16x8 pw[HG];
+#pragma unroll
+        for (int w = 0; w < HG; ++w) pw[w] = *reinterpret_cast<const f16x8 *>(PB + ((w0 + w) * 64 + lane) * 8);
+        constexpr int VD = 2;
+        v4i16 vlo[VD], vhi[VD];
+#pragma unroll
+        for (int db = 0; db < VD; ++db) {
+          vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * db));
+          vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * db));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          f16x8 a;
+          __builtin_memcpy(&a, &vlo[db % VD], 8);
+          __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &vhi[db % VD], 8);
+          if (db + VD < DB) {
+            vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * (db + VD)));
+            vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * (db + VD)));
+          }
+#pragma unroll
+          for (int w = 0; w < HG; ++w)
+            acc_o[w0 + w][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pw[w], acc_o[w0 + w][db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      return false;
     }
     // O^T += V^T P^T; V^T fragments by transposing reads of the row-major tile,
     // pipelined VD 16-dim blocks deep
@@ -789,7 +862,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       }
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        acc_o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[hb], acc_o[hb][db], 0, 0, 0);
+        if constexpr (!DSPV) acc_o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[hb], acc_o[hb][db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     return over;
@@ -797,11 +870,11 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 
   for (int pass = 0;; ++pass) {
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-      l_run[hb] = 0.f;
+    for (int hb = 0; hb < NHB; ++hb) l_run[hb] = 0.f;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int ah = 0; ah < AH; ++ah)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[ah][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool restart = false;
     int it = 0;
     if constexpr (!FP8) {
@@ -811,8 +884,8 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool odd = it & 1;
         const bool more = tile + 1 < tile_hi;
-        const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_ids(tile + 1) : 0,
-                                  nullptr, nullptr, 0);
+        const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_addr(tile + 1) : 0,
+                                  nullptr, nullptr, 0, it & 1);
         if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
         if (tid == 0) rflag[(it + 1) & 1] = 0;
         vm_wait_all();     // this wave's rows of the next tile landed ...
@@ -830,7 +903,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       lds_barrier();
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool more = tile + 1 < tile_hi;
-        const bool over = compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1);
+        const bool over = compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1, it & 1);
         if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
         if (tid == 0) rflag[(it + 1) & 1] = 0;
         vm_wait_all();     // this wave's part of raw tile+1 landed ...
@@ -848,24 +921,46 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     __syncthreads();
   }
 
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const int h = h0 + 16 * hb + c;
-    float lr = l_run[hb];
+  // DSPV: the head-owning waves' (reference, sum) pairs through LDS
+  float *shml = reinterpret_cast<float *>(PB);
+  if constexpr (DSPV) {
+    float lr = l_run[0];
     lr += __shfl_xor(lr, 16, 64);
     lr += __shfl_xor(lr, 32, 64);
-    const float mr = m_ref[hb];
+    if (g == 0) {
+      shml[2 * (16 * wv + c)] = m_ref[0];
+      shml[2 * (16 * wv + c) + 1] = lr;
+    }
+    __syncthreads();
+  }
+  // bf16 outputs of the dimension-split path are staged in the (now idle) tile
+  // buffers, heads as rows, so that every global store writes one whole 1 KB row
+  const bool stage = DSPV && A.nsplit == 1 && A.out_dtype != DSV4_F32;
+#pragma unroll
+  for (int hb = 0; hb < AH; ++hb) {
+    const int h = DSPV ? 16 * hb + c : h0 + 16 * hb + c;
+    float lr, mr;
+    if constexpr (DSPV) {
+      mr = shml[2 * h];
+      lr = shml[2 * h + 1];
+    } else {
+      lr = l_run[hb];
+      lr += __shfl_xor(lr, 16, 64);
+      lr += __shfl_xor(lr, 32, 64);
+      mr = m_ref[hb];
+    }
+    const int dlo = DSPV ? 16 * DB * wv : 0;   // this wave's first output channel
     if (A.nsplit > 1) {
       const int64_t pr = ((int64_t)r * A.nsplit + split) * A.H + h;
       uint16_t *po = A.part_o + pr * D;
       const float inv = lr > 0.f ? 1.f / lr : 0.f;   // normalised: within the rows' range, fp16-safe
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const f32x4 a = acc_o[hb][db];
-        *reinterpret_cast<u32x2 *>(po + 16 * db + 4 * g) =
+        *reinterpret_cast<u32x2 *>(po + dlo + 16 * db + 4 * g) =
             u32x2{pack_f16x2(a[0] * inv, a[1] * inv), pack_f16x2(a[2] * inv, a[3] * inv)};
       }
-      if (g == 0) {
+      if (g == 0 && (!DSPV || hb == wv)) {
         A.part_ml[2 * pr] = mr;
         A.part_ml[2 * pr + 1] = lr;
       }
@@ -873,16 +968,16 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     }
     float f = 1.f, den = lr;
     if (A.sinks) {
-      const float sg = A.sinks[h] * kLog2e;
+      const float sg = sk[h];
       const float M = fmaxf(mr, sg);
       f = exp2f(mr - M);
       den = lr * f + exp2f(sg - M);
     }
     const float inv = den > 0.f ? f / den : 0.f;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int db = 0; db < DB; ++db) {
       float o[4];
-      const int d0 = 16 * db + 4 * g;
+      const int d0 = dlo + 16 * db + 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
       if (d0 >= D - R) {
@@ -896,11 +991,24 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         }
       }
       const int64_t oe = ((int64_t)r * A.H + h) * D + d0;
-      if (A.out_dtype == DSV4_F32) {
+      if (stage) {
+        *reinterpret_cast<u32x2 *>((h < 32 ? T0 : T1) + (h & 31) * KP + d0) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      } else if (A.out_dtype == DSV4_F32) {
         *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
       } else {
         *reinterpret_cast<u32x2 *>((uint16_t *)A.out + oe) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       }
+    }
+  }
+  if (stage) {
+    __syncthreads();
+    // wave w writes the rows of heads 16w .. 16w+15: lane l carries channels 8l .. 8l+7
+#pragma unroll 4
+    for (int k = 0; k < 16; ++k) {
+      const int h = 16 * wv + k;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>((h < 32 ? T0 : T1) + (h & 31) * KP + 8 * lane);
+      *reinterpret_cast<u32x4 *>((uint16_t *)A.out + ((int64_t)r * A.H + h) * D + 8 * lane) = v;
     }
   }
 }

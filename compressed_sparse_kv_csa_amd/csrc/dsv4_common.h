@@ -20,15 +20,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---- bfloat16 <-> float (bit patterns kept in uint16_t) ----
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// round to nearest even; inputs are finite
+// round to nearest even (gfx950 converts in hardware: v_cvt_pk_bf16_f32)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_hw;
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // two floats -> packed IEEE fp16 pair (round to nearest even)
