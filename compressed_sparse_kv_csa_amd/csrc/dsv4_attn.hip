@@ -492,7 +492,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // over its own D/NW output channels, so each V^T fragment read from LDS feeds
   // NW products instead of one (the tile's V^T is read once per workgroup, not
   // once per wave).  AH: head blocks and DB: 16-channel blocks a wave accumulates.
-  constexpr bool DSPV = !FP8 && NHB == 1 && (NW == 1 || NW == 2 || NW == 4);
+  constexpr bool DSPV = NHB == 1 && (NW == 1 || NW == 2 || NW == 4);
   constexpr int AH = DSPV ? NW : NHB, DB = DSPV ? NDB / NW : NDB;
   static_assert(!FP8 || 32 * kF8Row % 1024 == 0, "raw tile must be whole DMA instructions");
   __shared__ __attribute__((aligned(16))) uint16_t T0[32 * KP];
@@ -721,6 +721,12 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       if (Rn) {
         raw_ids(ntile, grk, grid_);
         raw_scale(grid_, Sn);
+        // dimension-split path: the whole raw tile at once, so that its
+        // latency has the full tile to hide behind
+        if constexpr (DSPV) {
+#pragma unroll
+          for (int k = 0; k < CPW; ++k) raw_chunk(k, grk[k], Rn);
+        }
       }
     }
     f32x4 s[NHB][2];
@@ -754,7 +760,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 #pragma unroll
           for (int k = (j * RPW) / NJ; k < ((j + 1) * RPW) / NJ; ++k) dma_row(idn, k, Tn);
         }
-        if constexpr (FP8) {
+        if constexpr (FP8 && !DSPV) {
           if (Rn) {
 #pragma unroll
             for (int k = (j * CPW) / NJ; k < ((j + 1) * CPW) / NJ; ++k) raw_chunk(k, grk[k], Rn);
@@ -802,7 +808,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       asm volatile("" : "+v"(l_run[0]), "+v"(m_seen[0]));
       // the next tile's gather: issued where the wave would wait for the others'
       // scores anyway (its buffer was released by the previous tile's closing barrier)
-      if (Tn) {
+      if (!FP8 && Tn) {
 #pragma unroll
         for (int k = 0; k < RPW; ++k) dma_row(idn, k, Tn);
       }
@@ -935,7 +941,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   }
   // bf16 outputs of the dimension-split path are staged in the (now idle) tile
   // buffers, heads as rows, so that every global store writes one whole 1 KB row
-  const bool stage = DSPV && A.nsplit == 1 && A.out_dtype != DSV4_F32;
+  const bool stage = DSPV && !FP8 && A.nsplit == 1 && A.out_dtype != DSV4_F32;
 #pragma unroll
   for (int hb = 0; hb < AH; ++hb) {
     const int h = DSPV ? 16 * hb + c : h0 + 16 * hb + c;
