@@ -1020,34 +1020,53 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 }
 
 // Merge split partials: grid (T * H), block D/2 threads (one channel pair each).
-template <int D>
+// Every load that does not depend on another (the channel pair of every split,
+// the splits' (max, sum)) is issued first, so the merge costs about one memory
+// round trip next to the row plan and the rope angles.
+constexpr int kMaxSplit = 64;
+template <int D, int MS>   // MS: upper bound of the split count (registers per thread)
 __global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
   const int rh = blockIdx.x;
   const int r = rh / A.H, h = rh % A.H;
   const int pr = threadIdx.x;
+  const int ns = A.nsplit;
   __shared__ float rc[32], rs[32];
+  __shared__ float sm[kMaxSplit], sl[kMaxSplit];
+  const int64_t q0 = (int64_t)r * ns * A.H + h;   // partial row of split s: q0 + s * H
+  uint32_t ov[MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s)
+    if (s < ns) ov[s] = reinterpret_cast<const uint32_t *>(A.part_o + (q0 + (int64_t)s * A.H) * D)[pr];
+  if (pr < ns) {
+    sm[pr] = A.part_ml[2 * (q0 + (int64_t)pr * A.H)];
+    sl[pr] = A.part_ml[2 * (q0 + (int64_t)pr * A.H) + 1];
+  }
+  const float sg = A.sinks ? A.sinks[h] * kLog2e : -INFINITY;
   const int b = A.seq[r];
   const int64_t p = (A.pos0 ? A.pos0[b] : 0) + A.tok[r];
   const int R = A.rope_dim;
   if (pr < R / 2) rope_cs_f((double)p, A.inv_freq[pr], 1.f, &rc[pr], &rs[pr]);
   __syncthreads();
-  float M = A.sinks ? A.sinks[h] * kLog2e : -INFINITY;
-  for (int s = 0; s < A.nsplit; ++s) M = fmaxf(M, A.part_ml[2 * (((int64_t)r * A.nsplit + s) * A.H + h)]);
-  float den = A.sinks ? exp2f(A.sinks[h] * kLog2e - M) : 0.f;
+  float M = sg;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, sm[s]);
+  float den = A.sinks ? exp2f(sg - M) : 0.f;
   float o0 = 0.f, o1 = 0.f;
-  for (int s = 0; s < A.nsplit; ++s) {
-    const int64_t q = ((int64_t)r * A.nsplit + s) * A.H + h;
-    const float ms = A.part_ml[2 * q];
-    if (ms == -INFINITY) continue;   // split without rows
-    const float f = A.part_ml[2 * q + 1] * exp2f(ms - M);   // the split's weight: its sum at the common max
-    den += f;
-    const uint32_t u = reinterpret_cast<const uint32_t *>(A.part_o + q * D)[pr];
-    _Float16 h0, h1;
-    const uint16_t lo = (uint16_t)(u & 0xFFFFu), hi = (uint16_t)(u >> 16);
-    __builtin_memcpy(&h0, &lo, 2);
-    __builtin_memcpy(&h1, &hi, 2);
-    o0 = fmaf((float)h0, f, o0);
-    o1 = fmaf((float)h1, f, o1);
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    if (s < ns) {
+      const float ms = sm[s];
+      // the split's weight: its sum at the common max (0 for a split without rows)
+      const float f = ms == -INFINITY ? 0.f : sl[s] * exp2f(ms - M);
+      den += f;
+      _Float16 h0, h1;
+      const uint16_t lo = (uint16_t)(ov[s] & 0xFFFFu), hi = (uint16_t)(ov[s] >> 16);
+      __builtin_memcpy(&h0, &lo, 2);
+      __builtin_memcpy(&h1, &hi, 2);
+      if (f != 0.f) {
+        o0 = fmaf((float)h0, f, o0);
+        o1 = fmaf((float)h1, f, o1);
+      }
+    }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
   o0 *= inv;
@@ -1242,6 +1261,15 @@ size_t attn_ws(int T, int H, int D, int64_t max_rows) {
   return (size_t)T * ns * H * ((size_t)D * 2 + 8) + 256;   // fp16 outputs, fp32 (max, sum)
 }
 
+// the merge kernel instance with the smallest split bound that holds nsplit
+static void launch_combine(const AttnArgs &A, int T, int H, hipStream_t st) {
+  const dim3 g((unsigned)((int64_t)T * H)), b(256);
+  if (A.nsplit <= 8) hipLaunchKernelGGL((k_attn_combine<512, 8>), g, b, 0, st, A);
+  else if (A.nsplit <= 16) hipLaunchKernelGGL((k_attn_combine<512, 16>), g, b, 0, st, A);
+  else if (A.nsplit <= 32) hipLaunchKernelGGL((k_attn_combine<512, 32>), g, b, 0, st, A);
+  else hipLaunchKernelGGL((k_attn_combine<512, kMaxSplit>), g, b, 0, st, A);
+}
+
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
                 const dsv4_rows *pool, const int32_t *idx, int topk, int m, int csa, const float *sinks,
                 float sm_scale, int rope_dim, double theta, void *out, int out_dtype, void *ws,
@@ -1301,7 +1329,7 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
 #undef DSV4_F16K
     int rc = check_launch("k_attn_f16");
     if (rc || ns == 1) return rc;
-    hipLaunchKernelGGL(k_attn_combine<512>, dim3((unsigned)((int64_t)T * H)), dim3(256), 0, st, A);
+    launch_combine(A, T, H, st);
     return check_launch("k_attn_combine");
   }
   switch (H / 16) {
@@ -1318,7 +1346,7 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   }
   int rc = check_launch("k_attn_mfma");
   if (rc || ns == 1) return rc;
-  hipLaunchKernelGGL(k_attn_combine<512>, dim3((unsigned)((int64_t)T * H)), dim3(256), 0, st, A);
+  launch_combine(A, T, H, st);
   return check_launch("k_attn_combine");
 }
 
