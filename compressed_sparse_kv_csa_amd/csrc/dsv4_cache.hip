@@ -26,6 +26,7 @@ namespace dsv4 {
 
 struct CacheStreamD {
   int dim, rope, dtype, tail;
+  RopeTab tab;   // inverse frequencies of this stream's rope pairs
   const float *bias;
   float *buf;
   uint8_t *pool;
@@ -47,6 +48,7 @@ struct CacheArgs {
   uint8_t *win;
   float *wsc;
   int wdtype, wtail, wcap, wdim, wrope;
+  RopeTab wtab;
   int32_t *wcount, *wfirst;
   // work items per sequence: [0, nwi) window tokens, then nei entries per stream
   int nwi, nei, ns;
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(256) void k_cache_write(CacheArgs A) {
       v = load_pair<BF>(A.kv, ((int64_t)b * A.n + i) * half + p);
       if (A.wrope > 0 && d0 >= A.wdim - A.wrope) {
         float cs, sn;
-        rope_cs((double)(pos0 + j), (d0 - (A.wdim - A.wrope)) >> 1, A.wrope, A.theta, 1.f, &cs, &sn);
+        rope_cs_f((double)(pos0 + j), A.wtab.f[(d0 - (A.wdim - A.wrope)) >> 1], 1.f, &cs, &sn);
         rope_rotate(v.x, v.y, cs, sn);
       }
     }
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256) void k_cache_write(CacheArgs A) {
     o1 = a1.acc / a1.den;
     if (S.rope > 0 && d0 >= S.dim - S.rope) {
       float cs, sn;
-      rope_cs((double)(pos0 + (int64_t)s * m), (d0 - (S.dim - S.rope)) >> 1, S.rope, A.theta, 1.f, &cs, &sn);
+      rope_cs_f((double)(pos0 + (int64_t)s * m), S.tab.f[(d0 - (S.dim - S.rope)) >> 1], 1.f, &cs, &sn);
       rope_rotate(o0, o1, cs, sn);
     }
   }
@@ -265,14 +267,17 @@ int launch_cache_append(const dsv4_cache *C, int n, const int32_t *n_new, const 
   A.wcap = C->win_cap;
   A.wdim = C->win_dim;
   A.wrope = C->win_rope_dim;
+  A.wtab = rope_table(C->rope_theta, A.wrope);
   A.wcount = C->win_count;
   A.wfirst = C->win_first;
   A.nwi = C->win_cap > 0 ? (n < C->win_cap ? n : C->win_cap) : 0;
   A.nei = (n + C->m - 1) / C->m;
   A.ns = 1;
   fill_stream(A.st[0], C->kv, kv_c, kv_z);
+  A.st[0].tab = rope_table(C->rope_theta, A.st[0].rope);
   if (C->idx.dim > 0) {
     fill_stream(A.st[1], C->idx, idx_c, idx_z);
+    A.st[1].tab = rope_table(C->rope_theta, A.st[1].rope);
     A.ns = 2;
   }
   const bool bf = in_dtype == DSV4_BF16;

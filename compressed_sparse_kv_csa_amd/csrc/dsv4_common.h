@@ -64,9 +64,16 @@ __device__ __forceinline__ void rope_cs_f(double pos, double inv_freq, float sig
   *s = sn * sign;
 }
 
-__device__ __forceinline__ void rope_cs(double pos, int pair, int rope_dim, double theta, float sign,
-                                        float *c, float *s) {
-  rope_cs_f(pos, pow(theta, -2.0 * (double)pair / (double)rope_dim), sign, c, s);
+// Inverse frequencies theta^(-2i/R) of the (at most 32) rope pairs, formed
+// once on the host in fp64 and passed by value, so that every kernel that
+// rotates uses the same table and none evaluates pow per element.
+struct RopeTab {
+  double f[32];
+};
+static inline RopeTab rope_table(double theta, int rope_dim) {
+  RopeTab t;
+  for (int i = 0; i < 32; ++i) t.f[i] = (i < rope_dim / 2) ? pow(theta, -2.0 * i / (double)rope_dim) : 0.0;
+  return t;
 }
 
 // Rotate one interleaved rope pair by the angle whose (cos, sin) is (cs, sn).

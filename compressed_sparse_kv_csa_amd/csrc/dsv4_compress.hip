@@ -57,7 +57,7 @@ struct Pair<uint16_t> {
 template <typename TI, typename TO>
 __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, const void *__restrict__ z,
                                                   const float *__restrict__ bias, int S, int dim, int m,
-                                                  int overlap, int rope_dim, double theta,
+                                                  int overlap, int rope_dim, RopeTab tab,
                                                   const int64_t *__restrict__ pos0, void *__restrict__ pool) {
   const int half = dim >> 1;
   const int pblocks = (half + blockDim.x - 1) / blockDim.x;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, co
     const int pair = (d0 - (dim - rope_dim)) >> 1;
     const double P = (double)((pos0 ? pos0[b] : 0) + (int64_t)s * m);
     float cs, sn;
-    rope_cs(P, pair, rope_dim, theta, 1.f, &cs, &sn);
+    rope_cs_f(P, tab.f[pair], 1.f, &cs, &sn);
     rope_rotate(o0, o1, cs, sn);
   }
   Pair<TO>::store(pool, ((int64_t)b * N + s) * half + pr, o0, o1);
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, co
 template <typename T, typename TO>
 __global__ __launch_bounds__(256) void k_rope(const void *x, void *y, int64_t n_rows,
                                               int dim, int rope_dim, const int64_t *__restrict__ pos,
-                                              double theta, float sign) {
+                                              RopeTab tab, float sign) {
   const int half = dim >> 1;
   const int pr = blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t r = blockIdx.y;
@@ -106,10 +106,91 @@ __global__ __launch_bounds__(256) void k_rope(const void *x, void *y, int64_t n_
   const int d0 = 2 * pr;
   if (d0 >= dim - rope_dim) {
     float cs, sn;
-    rope_cs((double)pos[r], (d0 - (dim - rope_dim)) >> 1, rope_dim, theta, sign, &cs, &sn);
+    rope_cs_f((double)pos[r], tab.f[(d0 - (dim - rope_dim)) >> 1], sign, &cs, &sn);
     rope_rotate(v.x, v.y, cs, sn);
   }
   Pair<TO>::store(y, e, v.x, v.y);
+}
+
+// Eight channels (16-byte bf16/fp16 or 2 x 16-byte fp32 accesses) per thread,
+// rows flattened into one grid dimension: for dim % 8 == 0 and 16-byte
+// aligned rows.  Same arithmetic per pair as k_rope.
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<uint16_t> {   // bf16
+  static __device__ __forceinline__ void load(const void *p, int64_t i, float (&v)[8]) {
+    const u32x4 u = reinterpret_cast<const u32x4 *>(p)[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_to_f32((uint16_t)(w[k] & 0xFFFF));
+      v[2 * k + 1] = bf16_to_f32((uint16_t)(w[k] >> 16));
+    }
+  }
+  static __device__ __forceinline__ void store(void *p, int64_t i, const float (&v)[8]) {
+    reinterpret_cast<u32x4 *>(p)[i] =
+        u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+};
+template <>
+struct Vec8<F16T> {
+  static __device__ __forceinline__ void load(const void *p, int64_t i, float (&v)[8]) {
+    const u32x4 u = reinterpret_cast<const u32x4 *>(p)[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      _Float16 a, b;
+      const uint16_t lo = (uint16_t)(w[k] & 0xFFFF), hi = (uint16_t)(w[k] >> 16);
+      __builtin_memcpy(&a, &lo, 2);
+      __builtin_memcpy(&b, &hi, 2);
+      v[2 * k] = (float)a;
+      v[2 * k + 1] = (float)b;
+    }
+  }
+  static __device__ __forceinline__ void store(void *p, int64_t i, const float (&v)[8]) {
+    reinterpret_cast<u32x4 *>(p)[i] =
+        u32x4{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3]), pack_f16x2(v[4], v[5]), pack_f16x2(v[6], v[7])};
+  }
+};
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const void *p, int64_t i, float (&v)[8]) {
+    const f32x4 a = reinterpret_cast<const f32x4 *>(p)[2 * i], b = reinterpret_cast<const f32x4 *>(p)[2 * i + 1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = a[k];
+      v[4 + k] = b[k];
+    }
+  }
+  static __device__ __forceinline__ void store(void *p, int64_t i, const float (&v)[8]) {
+    reinterpret_cast<f32x4 *>(p)[2 * i] = f32x4{v[0], v[1], v[2], v[3]};
+    reinterpret_cast<f32x4 *>(p)[2 * i + 1] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+};
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void k_rope8(const void *x, void *y, int64_t n_rows, int dim, int rope_dim,
+                                               const int64_t *__restrict__ pos, RopeTab tab, float sign) {
+  const int per = dim >> 3;   // 8-channel groups per row
+  const int64_t it = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (it >= n_rows * per) return;
+  const int64_t r = it / per;
+  const int d0 = 8 * (int)(it - r * per);
+  float v[8];
+  Vec8<T>::load(x, it, v);
+  if (d0 + 8 > dim - rope_dim) {
+    const double p = (double)pos[r];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = d0 + 2 * k;
+      if (d >= dim - rope_dim) {
+        float cs, sn;
+        rope_cs_f(p, tab.f[(d - (dim - rope_dim)) >> 1], sign, &cs, &sn);
+        rope_rotate(v[2 * k], v[2 * k + 1], cs, sn);
+      }
+    }
+  }
+  Vec8<TO>::store(y, it, v);
 }
 
 }  // namespace dsv4
@@ -124,9 +205,10 @@ int launch_compress(const void *c, const void *z, int in_dtype, const float *bia
   const int N = S / m;
   if (B == 0 || N == 0) return DSV4_OK;
   dim3 grid((unsigned)(N * ((dim / 2 + 255) / 256)), B), block(256);
+  const RopeTab tab = rope_table(theta, rope_dim);
 #define DSV4_CMP(TI, TO)                                                                               \
   hipLaunchKernelGGL((k_compress<TI, TO>), grid, block, 0, st, c, z, bias, S, dim, m, overlap, rope_dim, \
-                     theta, pos0, pool)
+                     tab, pos0, pool)
   if (in_dtype == DSV4_F32) {
     if (out_dtype == DSV4_F32) DSV4_CMP(float, float);
     else if (out_dtype == DSV4_BF16) DSV4_CMP(float, uint16_t);
@@ -144,6 +226,23 @@ int launch_rope(const void *x, int x_dtype, void *y, int y_dtype, int64_t n_rows
                 const int64_t *pos, double theta, int inverse, hipStream_t st) {
   if (n_rows == 0) return DSV4_OK;
   const float sign = inverse ? -1.f : 1.f;
+  const RopeTab tab = rope_table(theta, rope_dim);
+  if (dim % 8 == 0 && ((uintptr_t)x & 15) == 0 && ((uintptr_t)y & 15) == 0) {
+    const int64_t items = n_rows * (dim / 8);
+    dim3 grid((unsigned)((items + 255) / 256)), block(256);
+#define DSV4_ROPE8(TI, TO) hipLaunchKernelGGL((k_rope8<TI, TO>), grid, block, 0, st, x, y, n_rows, dim, rope_dim, pos, tab, sign)
+    if (x_dtype == DSV4_F32) {
+      if (y_dtype == DSV4_F32) DSV4_ROPE8(float, float);
+      else if (y_dtype == DSV4_BF16) DSV4_ROPE8(float, uint16_t);
+      else DSV4_ROPE8(float, F16T);
+    } else {
+      if (y_dtype == DSV4_F32) DSV4_ROPE8(uint16_t, float);
+      else if (y_dtype == DSV4_BF16) DSV4_ROPE8(uint16_t, uint16_t);
+      else DSV4_ROPE8(uint16_t, F16T);
+    }
+#undef DSV4_ROPE8
+    return check_launch("k_rope8");
+  }
   int64_t done = 0;
   while (done < n_rows) {   // grid.y is limited to 65535 rows per launch
     const int64_t n = (n_rows - done) < 65535 ? (n_rows - done) : 65535;
@@ -151,7 +250,7 @@ int launch_rope(const void *x, int x_dtype, void *y, int y_dtype, int64_t n_rows
     const void *xs = (const char *)x + done * (int64_t)dim * (x_dtype == DSV4_F32 ? 4 : 2);
     void *ys = (char *)y + done * (int64_t)dim * (y_dtype == DSV4_F32 ? 4 : 2);
 #define DSV4_ROPE(TI, TO) \
-  hipLaunchKernelGGL((k_rope<TI, TO>), grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, theta, sign)
+  hipLaunchKernelGGL((k_rope<TI, TO>), grid, block, 0, st, xs, ys, n, dim, rope_dim, pos + done, tab, sign)
     if (x_dtype == DSV4_F32) {
       if (y_dtype == DSV4_F32) DSV4_ROPE(float, float);
       else if (y_dtype == DSV4_BF16) DSV4_ROPE(float, uint16_t);
