@@ -293,6 +293,7 @@ def test_hca_attn_prefill(K, B, Sx, H, W, m, sink, rows):
     ("csa", 2, [9000, 37], 512, 16, 64),      # 16 heads; a sequence shorter than the window
     ("csa", 2, [5000, 2222], 256, 32, 32),    # 32 bf16 tail channels: the generic FP8 kernel
     ("hca", 2, [70000, 3000], 0, 64, 64),
+    ("hca", 1, [3000], 0, 32, 64),           # 32 heads: two waves on the channel-split path
     ("hca", 1, [100], 0, 48, 64),
 ])
 def test_attn_decode_fp8(K, kind, B, L, k, H, tail):
@@ -321,6 +322,47 @@ def test_attn_decode_fp8(K, kind, B, L, k, H, tail):
                               layer.theta, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), ref, "bf16", f"{kind} decode")
+
+
+@pytest.mark.parametrize("kind,B,L,k,H", [
+    ("csa", 2, [20000, 3001], 256, 64),
+    ("hca", 2, [70000, 3000], 0, 32),
+    ("csa", 1, [5000], 128, 16),
+])
+def test_attn_decode_f16_split(K, kind, B, L, k, H):
+    """fp16 K=V rows at decode shapes: a few query rows over long row lists, so
+    each query's rows are split over several workgroups on the channel-split PV
+    path (partials of every wave's channel slice) and merged by k_attn_combine."""
+    say("attn decode f16 split", kind, B, L, k, H)
+    layer = S.decode_layer(70 + B, kind, B, L, H=H, topk=max(k, 1))
+    rng = np.random.default_rng(71)
+    D = layer.D
+    pool = S.rowset_from_values(rng.standard_normal((B, layer.pool.rows_per_seq, D)).astype(np.float32), "f16",
+                                count=layer.pool.count)
+    win = S.rowset_from_values(rng.standard_normal((B, layer.W, D)).astype(np.float32), "f16",
+                               count=layer.win.count, first_tok=layer.win.first_tok)
+    seq = np.arange(B, dtype=np.int32)
+    tok = layer.tok
+    qs = S.bf16_bits(layer.q)
+    Q = K.QueryRows(dev(seq), dev(tok), dev(layer.pos0), B)
+    if kind == "csa":
+        N = pool.count
+        sc = rng.standard_normal((B, pool.rows_per_seq))
+        nv = O.n_visible(tok, layer.m, N)
+        idx = O.topk(np.where(np.arange(sc.shape[1])[None] < nv[:, None], sc, -np.inf), nv, k)
+        ref = O.attn(seq, tok, layer.pos0, qs, "bf16", win, layer.W, pool, "csa", idx=idx, sinks=layer.sinks,
+                     sm_scale=layer.sm_scale, rope_dim=layer.R, theta=layer.theta)
+        out = K.dsv4_sparse_attn(Q, tensor_of(layer.q, "bf16"), upload_rows(win), layer.W, upload_rows(pool),
+                                 dev(idx), dev(layer.sinks), layer.sm_scale, layer.R, layer.theta,
+                                 out_dtype=torch.float32)
+    else:
+        ref = O.attn(seq, tok, layer.pos0, qs, "bf16", win, layer.W, pool, "hca", m=layer.m, sinks=layer.sinks,
+                     sm_scale=layer.sm_scale, rope_dim=layer.R, theta=layer.theta)
+        out = K.dsv4_hca_attn(Q, tensor_of(layer.q, "bf16"), upload_rows(win), layer.W, upload_rows(pool),
+                              layer.m, dev(layer.sinks), layer.sm_scale, layer.R, layer.theta,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, "bf16", f"{kind} decode, fp16 rows")
 
 
 # --------------------------------------------------------------------------- end to end
