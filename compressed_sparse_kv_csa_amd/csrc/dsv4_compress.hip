@@ -70,14 +70,31 @@ __global__ __launch_bounds__(256) void k_compress(const void *__restrict__ c, co
   const int jlo = t0 < 0 ? -t0 : 0;
   const int64_t rowbase = (int64_t)b * S;
   PoolAcc a0 = pool_init(), a1 = pool_init();
-  for (int j = jlo; j < width; ++j) {
-    const int t = t0 + j;
-    if (t >= S) break;
-    const int64_t e = (rowbase + t) * half + pr;
+  // window tokens in batches of 8: a batch's loads are all issued before its
+  // online-softmax steps, which run in token order as one at a time would
+  const int jhi = width < S - t0 ? width : S - t0;   // tokens t0 + j < S
+  int j = jlo;
+  for (; j + 8 <= jhi; j += 8) {
+    float2 zz[8], cc[8], bb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t e = (rowbase + t0 + j + u) * half + pr;
+      zz[u] = Pair<TI>::load(z, e);
+      cc[u] = Pair<TI>::load(c, e);
+      bb[u] = reinterpret_cast<const float2 *>(bias)[(int64_t)(j + u) * half + pr];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      pool_step(a0, zz[u].x + bb[u].x, cc[u].x);
+      pool_step(a1, zz[u].y + bb[u].y, cc[u].y);
+    }
+  }
+  for (; j < jhi; ++j) {
+    const int64_t e = (rowbase + t0 + j) * half + pr;
     const float2 zz = Pair<TI>::load(z, e);
     const float2 cc = Pair<TI>::load(c, e);
     const float2 bb = reinterpret_cast<const float2 *>(bias)[(int64_t)j * half + pr];
-    pool_step(a0, zz.x + bb.x, cc.x);   // online softmax per channel
+    pool_step(a0, zz.x + bb.x, cc.x);
     pool_step(a1, zz.y + bb.y, cc.y);
   }
   float o0 = a0.acc / a0.den, o1 = a1.acc / a1.den;
