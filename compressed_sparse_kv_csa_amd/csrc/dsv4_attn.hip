@@ -470,6 +470,21 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48):
+// two row-swapping permutes on the VALU instead of two LDS round trips
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -773,16 +788,19 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     f16x8 pb[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
+      if (base + 32 > nrows) {   // only the last tile holds positions past the list
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (base + 16 * mb + 4 * g + i >= nrows) s[hb][mb][i] = -INFINITY;
+      }
       float mloc = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (base + 16 * mb + 4 * g + i >= nrows) s[hb][mb][i] = -INFINITY;
-          mloc = fmaxf(mloc, s[hb][mb][i]);
-        }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[hb][mb][i]);
+      mloc = rows_max(mloc);
       m_seen[hb] = fmaxf(m_seen[hb], mloc);
       if (m_ref[hb] == -INFINITY) m_ref[hb] = mloc;   // first tile of this pass
       over = over || (mloc > m_ref[hb] + kRefSlack);
@@ -930,9 +948,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // DSPV: the head-owning waves' (reference, sum) pairs through LDS
   float *shml = reinterpret_cast<float *>(PB);
   if constexpr (DSPV) {
-    float lr = l_run[0];
-    lr += __shfl_xor(lr, 16, 64);
-    lr += __shfl_xor(lr, 32, 64);
+    const float lr = rows_sum(l_run[0]);
     if (g == 0) {
       shml[2 * (16 * wv + c)] = m_ref[0];
       shml[2 * (16 * wv + c) + 1] = lr;
