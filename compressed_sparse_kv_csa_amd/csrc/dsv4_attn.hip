@@ -436,8 +436,9 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
 //
 // fp16 rows with 16, 32 or 64 heads split PV by output channel instead of by
 // head: after S^T and the softmax, every wave writes its 16-head P^T fragment
-// to LDS, and after one barrier wave w accumulates O^T for all heads over
-// channels [w D/NW, (w+1) D/NW).  Each V^T fragment read from LDS then feeds
+// to LDS, and after one barrier wave w accumulates O^T for all heads over the
+// 16-channel blocks w, w + NW, w + 2 NW, ... (a D/NW share, with the rotated
+// last channels spread over all waves).  Each V^T fragment read from LDS then feeds
 // NW matrix products, and the tile's V^T is read once per workgroup instead of
 // once per wave (the transposing reads run at about half the rate of plain
 // 16-byte reads).  The accumulators stay 128 VGPRs per wave either way.  The
@@ -509,6 +510,9 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // once per wave).  AH: head blocks and DB: 16-channel blocks a wave accumulates.
   constexpr bool DSPV = NHB == 1 && (NW == 1 || NW == 2 || NW == 4);
   constexpr int AH = DSPV ? NW : NHB, DB = DSPV ? NDB / NW : NDB;
+  // dimension-split PV: wave w owns the 16-channel blocks w, w + NW, w + 2 NW, ...
+  // (so the rotated last channels are spread over all waves)
+  constexpr int CS = DSPV ? NW : 1;
   static_assert(!FP8 || 32 * kF8Row % 1024 == 0, "raw tile must be whole DMA instructions");
   __shared__ __attribute__((aligned(16))) uint16_t T0[32 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t T1[FP8 ? 8 : 32 * KP];   // FP8 rows: one fp16 tile
@@ -564,11 +568,15 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     const int rk = row_id(32 * tile + wv + NW * lane);
     return (uint64_t)(rk >= 0 ? wbase + (int64_t)rk * RB : pbase + (int64_t)(-1 - rk) * RB);
   };
+  // when NW divides 32 every lane k < RPW holds a row address (positions past
+  // the list are clamped to its last row), so no DMA is conditional
+  const uint32_t loff = 16u * (uint32_t)lane;
   auto dma_row = [&](uint64_t ad, int k, uint16_t *T) {   // row wv + NW*k of a tile, one 1 KB DMA
     const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)ad, k);
     const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(ad >> 32), k);
     const uint8_t *rp = (const uint8_t *)(((uint64_t)hi << 32) | lo);
-    if (rp) __builtin_amdgcn_global_load_lds(rp + 16 * lane, (lds_void *)(lds_u16 *)(T + (wvs + NW * k) * KP), 16, 0, 0);
+    if (32 % NW == 0 || rp)
+      __builtin_amdgcn_global_load_lds(rp + loff, (lds_void *)(lds_u16 *)(T + (wvs + NW * k) * KP), 16, 0, 0);
   };
   auto gather = [&](int tile, uint16_t *T) {
     const uint64_t ad = tile_addr(tile);
@@ -592,6 +600,15 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   if (tid < A.H) sk[tid] = A.sinks ? A.sinks[tid] * kLog2e : -INFINITY;
   if (tid < 2) rflag[tid] = 0;
   __syncthreads();
+  // the epilogue's output row and mode, formed now and held in scalars so that
+  // the epilogue does not wait for argument reloads
+  int e_ns = __builtin_amdgcn_readfirstlane(A.nsplit), e_odt = __builtin_amdgcn_readfirstlane(A.out_dtype);
+  int e_H = __builtin_amdgcn_readfirstlane(A.H), e_sk = __builtin_amdgcn_readfirstlane(A.sinks != nullptr ? 1 : 0);
+  uint16_t *orow = (uint16_t *)A.out + (int64_t)r * A.H * D;
+  uint16_t *e_po = A.part_o;
+  float *e_pml = A.part_ml;
+  asm volatile("" : "+s"(orow), "+s"(e_ns), "+s"(e_odt), "+s"(e_H), "+s"(e_sk), "+s"(e_po), "+s"(e_pml));
+  const bool stage = DSPV && !FP8 && e_ns == 1 && e_odt != DSV4_F32;
 
   // FP8: the raw 32-row tile is 18 KB of consecutive 1 KB DMA chunks (wave w:
   // chunks w, w+NW, ...); lane l of chunk q copies bytes [1024q + 16l, +16) of
@@ -833,7 +850,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       lds_barrier();   // P^T of every wave visible; the next tile's DMAs stay in flight
       // head blocks in groups of HG (P^T fragments live: HG; V^T read NW/HG times)
       constexpr int HG = NW;
-      const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * DB * wv;
+      const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * wv;
       const uint16_t *v1p = v0p + 16 * KP;
 #pragma unroll
       for (int w0 = 0; w0 < NW; w0 += HG) {
@@ -844,8 +861,8 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         v4i16 vlo[VD], vhi[VD];
 #pragma unroll
         for (int db = 0; db < VD; ++db) {
-          vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * db));
-          vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * db));
+          vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * CS * db));
+          vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * CS * db));
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -853,8 +870,8 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
           __builtin_memcpy(&a, &vlo[db % VD], 8);
           __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &vhi[db % VD], 8);
           if (db + VD < DB) {
-            vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * (db + VD)));
-            vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * (db + VD)));
+            vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * CS * (db + VD)));
+            vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * CS * (db + VD)));
           }
 #pragma unroll
           for (int w = 0; w < HG; ++w)
@@ -957,7 +974,6 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   }
   // bf16 outputs of the dimension-split path are staged in the (now idle) tile
   // buffers, heads as rows, so that every global store writes one whole 1 KB row
-  const bool stage = DSPV && !FP8 && A.nsplit == 1 && A.out_dtype != DSV4_F32;
 #pragma unroll
   for (int hb = 0; hb < AH; ++hb) {
     const int h = DSPV ? 16 * hb + c : h0 + 16 * hb + c;
@@ -971,25 +987,25 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       lr += __shfl_xor(lr, 32, 64);
       mr = m_ref[hb];
     }
-    const int dlo = DSPV ? 16 * DB * wv : 0;   // this wave's first output channel
-    if (A.nsplit > 1) {
-      const int64_t pr = ((int64_t)r * A.nsplit + split) * A.H + h;
-      uint16_t *po = A.part_o + pr * D;
+    const int dlo = DSPV ? 16 * wv : 0;   // this wave's first output channel
+    if (e_ns > 1) {
+      const int64_t pr = ((int64_t)r * e_ns + split) * e_H + h;
+      uint16_t *po = e_po + pr * D;
       const float inv = lr > 0.f ? 1.f / lr : 0.f;   // normalised: within the rows' range, fp16-safe
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4 a = acc_o[hb][db];
-        *reinterpret_cast<u32x2 *>(po + dlo + 16 * db + 4 * g) =
+        *reinterpret_cast<u32x2 *>(po + dlo + 16 * CS * db + 4 * g) =
             u32x2{pack_f16x2(a[0] * inv, a[1] * inv), pack_f16x2(a[2] * inv, a[3] * inv)};
       }
       if (g == 0 && (!DSPV || hb == wv)) {
-        A.part_ml[2 * pr] = mr;
-        A.part_ml[2 * pr + 1] = lr;
+        e_pml[2 * pr] = mr;
+        e_pml[2 * pr + 1] = lr;
       }
       continue;
     }
     float f = 1.f, den = lr;
-    if (A.sinks) {
+    if (e_sk) {
       const float sg = sk[h];
       const float M = fmaxf(mr, sg);
       f = exp2f(mr - M);
@@ -999,7 +1015,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float o[4];
-      const int d0 = dlo + 16 * db + 4 * g;
+      const int d0 = dlo + 16 * CS * db + 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
       if (d0 >= D - R) {
@@ -1012,11 +1028,11 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
           o[2 * k + 1] = bb;
         }
       }
-      const int64_t oe = ((int64_t)r * A.H + h) * D + d0;
+      const int64_t oe = ((int64_t)r * e_H + h) * D + d0;
       if (stage) {
         *reinterpret_cast<u32x2 *>((h < 32 ? T0 : T1) + (h & 31) * KP + d0) =
             u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      } else if (A.out_dtype == DSV4_F32) {
+      } else if (e_odt == DSV4_F32) {
         *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
       } else {
         *reinterpret_cast<u32x2 *>((uint16_t *)A.out + oe) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
@@ -1030,7 +1046,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     for (int k = 0; k < 16; ++k) {
       const int h = 16 * wv + k;
       const u32x4 v = *reinterpret_cast<const u32x4 *>((h < 32 ? T0 : T1) + (h & 31) * KP + 8 * lane);
-      *reinterpret_cast<u32x4 *>((uint16_t *)A.out + ((int64_t)r * A.H + h) * D + 8 * lane) = v;
+      *reinterpret_cast<u32x4 *>(orow + h * D + 8 * lane) = v;
     }
   }
 }
