@@ -170,6 +170,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// max / sum over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48):
+// two row-swapping permutes on the VALU instead of two LDS round trips
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// max(x, 0) by the bit pattern: non-negative floats order like their bit
+// patterns read as signed integers and negative ones read as negative, so one
+// integer maximum gives the result without the NaN canonicalisation a float
+// maximum of a matrix-core result needs (inputs here are finite)
+__device__ __forceinline__ float relu_f(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 }  // namespace dsv4
 
 // Host-side helpers shared by the launchers (defined in dsv4_api.cpp)

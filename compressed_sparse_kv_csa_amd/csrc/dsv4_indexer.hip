@@ -149,11 +149,10 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
           for (int j = 0; j < KS; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[hb][j], f.kb[eb][j], acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], fmaxf(acc[i], 0.f), s);
+        for (int i = 0; i < 4; ++i) s = fmaf(wt[hb][i], relu_f(acc[i]), s);
       }
       // sum over the four lane groups (heads 4g..4g+3 of every head block)
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
+      s = rows_sum(s);
       const int e = e0 + 16 * eb + c;
       if (g == 0 && e < hi) scores[(int64_t)r * ld + e] = s * scale;
     }
@@ -288,17 +287,13 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
 #pragma unroll
           for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sacc[qq][eb] = fmaf(wt[qq][hb][i], fmaxf(acc[hb][i], 0.f), sacc[qq][eb]);
+            for (int i = 0; i < 4; ++i) sacc[qq][eb] = fmaf(wt[qq][hb][i], relu_f(acc[hb][i]), sacc[qq][eb]);
         }
       }
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq)
 #pragma unroll
-        for (int eb = 0; eb < 4; ++eb) sacc[qq][eb] += __shfl_xor(sacc[qq][eb], 16, 64);
-#pragma unroll
-      for (int qq = 0; qq < QPW; ++qq)
-#pragma unroll
-        for (int eb = 0; eb < 4; ++eb) sacc[qq][eb] += __shfl_xor(sacc[qq][eb], 32, 64);
+        for (int eb = 0; eb < 4; ++eb) sacc[qq][eb] = rows_sum(sacc[qq][eb]);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
         if (!mine[qq] || g != 0) continue;
