@@ -989,14 +989,16 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       }
       continue;
     }
+    // the sink joins the denominator; both exponents are <= 0 (hardware exp2,
+    // reciprocal within an ulp: far below the output's bf16 rounding)
     float f = 1.f, den = lr;
     if (e_sk) {
       const float sg = sk[h];
       const float M = fmaxf(mr, sg);
-      f = exp2f(mr - M);
-      den = lr * f + exp2f(sg - M);
+      f = __builtin_amdgcn_exp2f(mr - M);
+      den = lr * f + __builtin_amdgcn_exp2f(sg - M);
     }
-    const float inv = den > 0.f ? f / den : 0.f;
+    const float inv = den > 0.f ? f * __builtin_amdgcn_rcpf(den) : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float o[4];
