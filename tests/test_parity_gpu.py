@@ -260,6 +260,35 @@ def test_sparse_attn_prefill(K, B, Sx, H, W, m, k, rows):
     assert_close(out.cpu().numpy(), ref, "bf16", "sparse_attn")
 
 
+@pytest.mark.parametrize("B,R,out", [
+    (1, 64, "bf16"),    # bf16 outputs staged as whole head rows
+    (2, 32, "bf16"),    # fewer rotated channels: the inverse rotation in one or two waves' blocks
+    (1, 0, "bf16"),     # no rotated channels
+    (1, 16, "f32"),
+])
+def test_sparse_attn_prefill_rope_out(K, B, R, out):
+    """The fp16-row kernel's epilogue with every output-channel split of the rotated channels."""
+    say("sparse_attn prefill rope/out", B, R, out)
+    Sx, H, W, m, k, D, theta = 400, 64, 128, 4, 64, 512, 1.6e5
+    q, win, pool, sinks, pos0 = _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, 60 + R, rows="f16")
+    rng = np.random.default_rng(5)
+    N = Sx // m
+    seq = np.repeat(np.arange(B), Sx).astype(np.int32)
+    tok = np.tile(np.arange(Sx), B).astype(np.int32)
+    nv = O.n_visible(tok, m, np.full(len(tok), N))
+    sc = rng.standard_normal((B * Sx, N))
+    idx = O.topk(np.where(np.arange(N)[None] < nv[:, None], sc, -np.inf), nv, k)
+    qs = S.bf16_bits(q.reshape(B * Sx, H, D))
+    ref = O.attn(seq, tok, pos0, qs, "bf16", win, W, pool, "csa", idx=idx, sinks=sinks,
+                 sm_scale=1 / np.sqrt(D), rope_dim=R, theta=theta)
+    Q = K.QueryRows(dev(seq), dev(tok), dev(pos0), B)
+    got = K.dsv4_sparse_attn(Q, tensor_of(q.reshape(B * Sx, H, D), "bf16"), upload_rows(win), W,
+                             upload_rows(pool), dev(idx), dev(sinks), 1 / np.sqrt(D), R, theta,
+                             out_dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    assert_close(got.float().cpu().numpy(), ref, "bf16", f"sparse_attn R={R} out={out}")
+
+
 @pytest.mark.parametrize("B,Sx,H,W,m,sink,rows", [
     (1, 1100, 64, 128, 16, True, "bf16"),
     (2, 300, 64, 128, 128, True, "bf16"),
