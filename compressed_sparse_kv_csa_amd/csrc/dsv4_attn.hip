@@ -34,6 +34,7 @@
 #include "dsv4_common.h"
 
 #include <atomic>
+#include <type_traits>
 
 namespace dsv4 {
 
@@ -484,7 +485,9 @@ constexpr float kRefSlack = 15.f;   // log2 units: P <= 2^15 stays finite in fp1
 constexpr int kF8Nope = 448, kF8Row = kF8Nope + 2 * 64;
 constexpr int kF8Chunks = 32 * kF8Row / 1024;   // 1 KB DMA instructions per 32-row raw tile
 
-template <int NHB, int NW, bool FP8>
+// R64: the rope width is the 64 channels of every configuration in the pages,
+// fixed at compile time so that the per-block rotation tests fold away
+template <int NHB, int NW, bool FP8, bool R64>
 __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
   constexpr int RB = FP8 ? kF8Row : 2 * D;   // stored row bytes
@@ -527,7 +530,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   IdxPre<NT> ipre;
   if (A.csa && A.topk > 0) ipre = load_idx<NT>(A, r);
   RowPlan P = row_plan(A, r);
-  const int R = A.rope_dim;
+  const int R = R64 ? 64 : A.rope_dim;
   const int nwin = P.nwin, csa = A.csa;
   // row addressing in scalars: window rows first, then pool rows
   const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * RB : nullptr;
@@ -958,74 +961,83 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     __syncthreads();
   }
   // bf16 outputs of the dimension-split path are staged in the (now idle) tile
-  // buffers, heads as rows, so that every global store writes one whole 1 KB row
+  // buffers, heads as rows, so that every global store writes one whole 1 KB row.
+  // The output form is chosen once (MD: 0 split partials, 1 staged bf16, 2 fp32,
+  // 3 bf16), not per channel block.
+  auto finish = [&](auto MDc) {
+    constexpr int MD = decltype(MDc)::value;
 #pragma unroll
-  for (int hb = 0; hb < AH; ++hb) {
-    const int h = DSPV ? 16 * hb + c : h0 + 16 * hb + c;
-    float lr, mr;
-    if constexpr (DSPV) {
-      mr = shml[2 * h];
-      lr = shml[2 * h + 1];
-    } else {
-      lr = l_run[hb];
-      lr += __shfl_xor(lr, 16, 64);
-      lr += __shfl_xor(lr, 32, 64);
-      mr = m_ref[hb];
-    }
-    const int dlo = DSPV ? 16 * wv : 0;   // this wave's first output channel
-    if (e_ns > 1) {
-      const int64_t pr = ((int64_t)r * e_ns + split) * e_H + h;
-      uint16_t *po = e_po + pr * D;
-      const float inv = lr > 0.f ? 1.f / lr : 0.f;   // normalised: within the rows' range, fp16-safe
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const f32x4 a = acc_o[hb][db];
-        *reinterpret_cast<u32x2 *>(po + dlo + 16 * CS * db + 4 * g) =
-            u32x2{pack_f16x2(a[0] * inv, a[1] * inv), pack_f16x2(a[2] * inv, a[3] * inv)};
+    for (int hb = 0; hb < AH; ++hb) {
+      const int h = DSPV ? 16 * hb + c : h0 + 16 * hb + c;
+      float lr, mr;
+      if constexpr (DSPV) {
+        mr = shml[2 * h];
+        lr = shml[2 * h + 1];
+      } else {
+        lr = l_run[hb];
+        lr += __shfl_xor(lr, 16, 64);
+        lr += __shfl_xor(lr, 32, 64);
+        mr = m_ref[hb];
       }
-      if (g == 0 && (!DSPV || hb == wv)) {
-        e_pml[2 * pr] = mr;
-        e_pml[2 * pr + 1] = lr;
-      }
-      continue;
-    }
-    // the sink joins the denominator; both exponents are <= 0 (hardware exp2,
-    // reciprocal within an ulp: far below the output's bf16 rounding)
-    float f = 1.f, den = lr;
-    if (e_sk) {
-      const float sg = sk[h];
-      const float M = fmaxf(mr, sg);
-      f = __builtin_amdgcn_exp2f(mr - M);
-      den = lr * f + __builtin_amdgcn_exp2f(sg - M);
-    }
-    const float inv = den > 0.f ? f * __builtin_amdgcn_rcpf(den) : 0.f;
+      const int dlo = DSPV ? 16 * wv : 0;   // this wave's first output channel
+      if constexpr (MD == 0) {
+        const int64_t pr = ((int64_t)r * e_ns + split) * e_H + h;
+        uint16_t *po = e_po + pr * D;
+        const float inv = lr > 0.f ? 1.f / lr : 0.f;   // normalised: within the rows' range, fp16-safe
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      float o[4];
-      const int d0 = dlo + 16 * CS * db + 4 * g;
+        for (int db = 0; db < DB; ++db) {
+          const f32x4 a = acc_o[hb][db];
+          *reinterpret_cast<u32x2 *>(po + dlo + 16 * CS * db + 4 * g) =
+              u32x2{pack_f16x2(a[0] * inv, a[1] * inv), pack_f16x2(a[2] * inv, a[3] * inv)};
+        }
+        if (g == 0 && (!DSPV || hb == wv)) {
+          e_pml[2 * pr] = mr;
+          e_pml[2 * pr + 1] = lr;
+        }
+      } else {
+        // the sink joins the denominator; both exponents are <= 0 (hardware exp2,
+        // reciprocal within an ulp: far below the output's bf16 rounding)
+        float f = 1.f, den = lr;
+        if (e_sk) {
+          const float sg = sk[h];
+          const float M = fmaxf(mr, sg);
+          f = __builtin_amdgcn_exp2f(mr - M);
+          den = lr * f + __builtin_amdgcn_exp2f(sg - M);
+        }
+        const float inv = den > 0.f ? f * __builtin_amdgcn_rcpf(den) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
-      if (d0 >= D - R) {
+        for (int db = 0; db < DB; ++db) {
+          float o[4];
+          const int d0 = dlo + 16 * CS * db + 4 * g;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int pi = (d0 + 2 * k - (D - R)) >> 1;
-          const float cs = rc[pi], sn = rs[pi];
-          const float a = o[2 * k] * cs + o[2 * k + 1] * sn, bb = -o[2 * k] * sn + o[2 * k + 1] * cs;
-          o[2 * k] = a;
-          o[2 * k + 1] = bb;
+          for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
+          if (d0 >= D - R) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const int pi = (d0 + 2 * k - (D - R)) >> 1;
+              const float cs = rc[pi], sn = rs[pi];
+              const float a = o[2 * k] * cs + o[2 * k + 1] * sn, bb = -o[2 * k] * sn + o[2 * k + 1] * cs;
+              o[2 * k] = a;
+              o[2 * k + 1] = bb;
+            }
+          }
+          const int64_t oe = ((int64_t)r * e_H + h) * D + d0;
+          if constexpr (MD == 1) {
+            *reinterpret_cast<u32x2 *>((h < 32 ? T0 : T1) + (h & 31) * KP + d0) =
+                u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          } else if constexpr (MD == 2) {
+            *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
+          } else {
+            *reinterpret_cast<u32x2 *>((uint16_t *)A.out + oe) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          }
         }
       }
-      const int64_t oe = ((int64_t)r * e_H + h) * D + d0;
-      if (stage) {
-        *reinterpret_cast<u32x2 *>((h < 32 ? T0 : T1) + (h & 31) * KP + d0) =
-            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      } else if (e_odt == DSV4_F32) {
-        *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
-      } else {
-        *reinterpret_cast<u32x2 *>((uint16_t *)A.out + oe) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      }
     }
-  }
+  };
+  if (e_ns > 1) finish(std::integral_constant<int, 0>{});
+  else if (stage) finish(std::integral_constant<int, 1>{});
+  else if (e_odt == DSV4_F32) finish(std::integral_constant<int, 2>{});
+  else finish(std::integral_constant<int, 3>{});
   if (stage) {
     __syncthreads();
     // wave w writes the rows of heads 16w .. 16w+15: lane l carries channels 8l .. 8l+7
@@ -1337,8 +1349,10 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   dim3 grid((unsigned)((int64_t)T * ns));
   if (f16 || fp8fast) {
 #define DSV4_F16K(NW)                                                                                 \
-  if (f16) hipLaunchKernelGGL((k_attn_f16<1, NW, false>), grid, dim3(NW * 64), 0, st, A);             \
-  else hipLaunchKernelGGL((k_attn_f16<1, NW, true>), grid, dim3(NW * 64), 0, st, A);
+  if (f16 && rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, NW, false, true>), grid, dim3(NW * 64), 0, st, A); \
+  else if (f16) hipLaunchKernelGGL((k_attn_f16<1, NW, false, false>), grid, dim3(NW * 64), 0, st, A);       \
+  else if (rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, NW, true, true>), grid, dim3(NW * 64), 0, st, A); \
+  else hipLaunchKernelGGL((k_attn_f16<1, NW, true, false>), grid, dim3(NW * 64), 0, st, A);
     switch (H) {
     case 16: DSV4_F16K(1) break;
     case 32: DSV4_F16K(2) break;
