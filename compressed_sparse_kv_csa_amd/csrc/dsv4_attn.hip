@@ -510,7 +510,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   __shared__ float rc[32], rs[32];
   __shared__ float sk[64];   // the heads' sinks (log2 units), loaded with the setup
   __shared__ int sh_cnt[kMaxSel / 64];
-  __shared__ int rflag[2];
+  __shared__ int rflag[3];   // overflow flags of tiles it mod 3: a flag is cleared two tiles after its last read
   __shared__ __attribute__((aligned(16))) uint16_t PB[DSPV ? NW * 64 * 8 : 8];   // P^T fragments, wave-major
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   if (tid < A.H) sk[tid] = A.sinks ? A.sinks[tid] * kLog2e : -INFINITY;
-  if (tid < 2) rflag[tid] = 0;
+  if (tid < 3) rflag[tid] = 0;
   __syncthreads();
   // the epilogue's output row and mode, formed now and held in scalars so that
   // the epilogue does not wait for argument reloads
@@ -914,12 +914,12 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         const bool odd = it & 1;
         const bool more = tile + 1 < tile_hi;
         const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_addr(tile + 1) : 0,
-                                  nullptr, nullptr, 0, it & 1);
-        if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
-        if (tid == 0) rflag[(it + 1) & 1] = 0;
+                                  nullptr, nullptr, 0, it % 3);
+        if (__ballot(over) && lane == 0) rflag[it % 3] = 1;
+        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
         vm_wait_all();     // this wave's rows of the next tile landed ...
         __syncthreads();   // ... and every wave's; this one fully read, flags visible
-        if (rflag[it & 1]) { restart = true; break; }
+        if (rflag[it % 3]) { restart = true; break; }
       }
     } else {
       // one raw buffer and one fp16 tile (two workgroups share a CU, so one's
@@ -932,19 +932,19 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       lds_barrier();
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool more = tile + 1 < tile_hi;
-        const bool over = compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1, it & 1);
-        if (__ballot(over) && lane == 0) rflag[it & 1] = 1;
-        if (tid == 0) rflag[(it + 1) & 1] = 0;
+        const bool over = compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1, it % 3);
+        if (__ballot(over) && lane == 0) rflag[it % 3] = 1;
+        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
         vm_wait_all();     // this wave's part of raw tile+1 landed ...
         __syncthreads();   // ... and every wave's; the tile fully read, flags visible
-        if (rflag[it & 1]) { restart = true; break; }
+        if (rflag[it % 3]) { restart = true; break; }
         if (more) convert(RW, RSC, T0);
         lds_barrier();
       }
     }
     if (!restart) break;
     __syncthreads();
-    if (tid < 2) rflag[tid] = 0;
+    if (tid < 3) rflag[tid] = 0;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) m_ref[hb] = m_seen[hb];
     __syncthreads();
