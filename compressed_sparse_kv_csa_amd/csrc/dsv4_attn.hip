@@ -755,7 +755,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     // S^T = K q~^T, software-pipelined QD k-steps deep; the scheduling barriers
     // keep the compiler from hoisting every LDS read at once
     {
-      constexpr int QD = 2;
+      constexpr int QD = DSPV ? 3 : 2;   // k-steps of K prefetch (registers left after the accumulators)
       const uint16_t *k0 = T + c * KP + 8 * g;
       const uint16_t *k1 = k0 + 16 * KP;
       f16x8 r0[QD], r1[QD];
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         f16x8 pw[HG];
 #pragma unroll
         for (int w = 0; w < HG; ++w) pw[w] = *reinterpret_cast<const f16x8 *>(PB + ((w0 + w) * 64 + lane) * 8);
-        constexpr int VD = 2;
+        constexpr int VD = 4;
         v4i16 vlo[VD], vhi[VD];
 #pragma unroll
         for (int db = 0; db < VD; ++db) {
