@@ -1055,19 +1055,21 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 // the splits' (max, sum)) is issued first, so the merge costs about one memory
 // round trip next to the row plan and the rope angles.
 constexpr int kMaxSplit = 64;
-template <int D, int MS>   // MS: upper bound of the split count (registers per thread)
+// MS: upper bound of the split count (registers per thread); EX: the count is
+// exactly MS, so no per-split guard is needed
+template <int D, int MS, bool EX>
 __global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
   const int rh = blockIdx.x;
   const int r = rh / A.H, h = rh % A.H;
   const int pr = threadIdx.x;
-  const int ns = A.nsplit;
+  const int ns = EX ? MS : A.nsplit;
   __shared__ float rc[32], rs[32];
   __shared__ float sm[kMaxSplit], sl[kMaxSplit];
   const int64_t q0 = (int64_t)r * ns * A.H + h;   // partial row of split s: q0 + s * H
   uint32_t ov[MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s)
-    if (s < ns) ov[s] = reinterpret_cast<const uint32_t *>(A.part_o + (q0 + (int64_t)s * A.H) * D)[pr];
+    if (EX || s < ns) ov[s] = reinterpret_cast<const uint32_t *>(A.part_o + (q0 + (int64_t)s * A.H) * D)[pr];
   if (pr < ns) {
     sm[pr] = A.part_ml[2 * (q0 + (int64_t)pr * A.H)];
     sl[pr] = A.part_ml[2 * (q0 + (int64_t)pr * A.H) + 1];
@@ -1084,19 +1086,18 @@ __global__ __launch_bounds__(D / 2) void k_attn_combine(AttnArgs A) {
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
-    if (s < ns) {
+    if (EX || s < ns) {
       const float ms = sm[s];
-      // the split's weight: its sum at the common max (0 for a split without rows)
-      const float f = ms == -INFINITY ? 0.f : sl[s] * exp2f(ms - M);
+      // the split's weight: its sum at the common max (0 for a split without
+      // rows, whose partial output is zero); the exponent is <= 0
+      const float f = ms == -INFINITY ? 0.f : sl[s] * __builtin_amdgcn_exp2f(ms - M);
       den += f;
       _Float16 h0, h1;
       const uint16_t lo = (uint16_t)(ov[s] & 0xFFFFu), hi = (uint16_t)(ov[s] >> 16);
       __builtin_memcpy(&h0, &lo, 2);
       __builtin_memcpy(&h1, &hi, 2);
-      if (f != 0.f) {
-        o0 = fmaf((float)h0, f, o0);
-        o1 = fmaf((float)h1, f, o1);
-      }
+      o0 = fmaf((float)h0, f, o0);
+      o1 = fmaf((float)h1, f, o1);
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -1295,10 +1296,15 @@ size_t attn_ws(int T, int H, int D, int64_t max_rows) {
 // the merge kernel instance with the smallest split bound that holds nsplit
 static void launch_combine(const AttnArgs &A, int T, int H, hipStream_t st) {
   const dim3 g((unsigned)((int64_t)T * H)), b(256);
-  if (A.nsplit <= 8) hipLaunchKernelGGL((k_attn_combine<512, 8>), g, b, 0, st, A);
-  else if (A.nsplit <= 16) hipLaunchKernelGGL((k_attn_combine<512, 16>), g, b, 0, st, A);
-  else if (A.nsplit <= 32) hipLaunchKernelGGL((k_attn_combine<512, 32>), g, b, 0, st, A);
-  else hipLaunchKernelGGL((k_attn_combine<512, kMaxSplit>), g, b, 0, st, A);
+  const int ns = A.nsplit;
+  if (ns == 8) hipLaunchKernelGGL((k_attn_combine<512, 8, true>), g, b, 0, st, A);
+  else if (ns < 8) hipLaunchKernelGGL((k_attn_combine<512, 8, false>), g, b, 0, st, A);
+  else if (ns == 16) hipLaunchKernelGGL((k_attn_combine<512, 16, true>), g, b, 0, st, A);
+  else if (ns < 16) hipLaunchKernelGGL((k_attn_combine<512, 16, false>), g, b, 0, st, A);
+  else if (ns == 32) hipLaunchKernelGGL((k_attn_combine<512, 32, true>), g, b, 0, st, A);
+  else if (ns < 32) hipLaunchKernelGGL((k_attn_combine<512, 32, false>), g, b, 0, st, A);
+  else if (ns == kMaxSplit) hipLaunchKernelGGL((k_attn_combine<512, kMaxSplit, true>), g, b, 0, st, A);
+  else hipLaunchKernelGGL((k_attn_combine<512, kMaxSplit, false>), g, b, 0, st, A);
 }
 
 int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D, const dsv4_rows *win, int W,
