@@ -21,10 +21,13 @@
 // holding 8 rows of one head, which is exactly the B-operand layout P^T needs
 // for the PV product (no shuffle of P), and O^T accumulates with each lane
 // holding 4 dims of the same head (so the online-softmax rescale is per lane).
-// The tile, q~ and P are fp16 on the matrix cores: stored bf16 values are exact
-// in fp16 (|x| < 65504), and fp16's 11-bit significand keeps the rounding of
-// q~ and P four times smaller than bf16 would, which matters when a query has
-// only a few rows and every logit error moves the output directly.  FP8 rows
+// The tile, q~ and P are fp16 on the matrix cores: a stored bf16 value whose
+// magnitude lies in [2^-14, 65504] is exact in fp16 (smaller ones lose
+// significand bits to fp16's subnormals, larger ones overflow; the callers'
+// rows and queries are far inside that range), and fp16's 11-bit significand
+// keeps the rounding of q~ and P four times smaller than bf16 would, which
+// matters when a query has only a few rows and every logit error moves the
+// output directly.  FP8 rows
 // (E4M3 x row scale, bf16 rope channels) are decoded to fp16 while staging.
 // Several splits per query (decode) each write their output normalised by
 // their own sum (fp16: a convex combination of rows stays in the rows' range)
@@ -1273,8 +1276,9 @@ static std::atomic<int> g_batch_invariant{0};
 int set_batch_invariant(bool on) { return g_batch_invariant.exchange(on ? 1 : 0); }
 
 // Splits per query (decode): enough workgroups to occupy the chip, but at least
-// four 32-row tiles per split, because every split writes a 64 x 512 fp32
-// partial that the combine kernel reads back.
+// four 32-row tiles per split, because every split writes a 64 x 512 fp16
+// partial (normalised by its own sum) plus fp32 (max, sum) per head that the
+// combine kernel reads back.
 int attn_nsplit(int T, int64_t max_rows) {
   const int64_t tiles = (max_rows + 31) / 32;
   // batch-invariant mode: one workgroup reduces a query's rows in one order

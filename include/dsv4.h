@@ -13,8 +13,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major and
  *     contiguous as described per argument.  The library allocates nothing,
  *     keeps no pointer after the call returns (apart from work already queued)
- *     and holds no global state beyond its code objects and a thread-local
- *     error string.
+ *     and holds no global state beyond its code objects, a thread-local error
+ *     string and the batch-invariant switch.
  *   - Every call validates its arguments on the host first; a call that returns
  *     an error has launched nothing.  dsv4_last_error() describes the failure.
  *   - Work is queued on `stream` (a hipStream_t; 0 = the null stream) with no
@@ -170,8 +170,18 @@ int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_i
  *   out    : [T, n_heads, dim] in out_dtype (DSV4_BF16 or DSV4_F32)
  *   ws     : scratch of at least dsv4_attn_workspace(...) bytes (may be 0 bytes)
  * A query with no rows and no sink gets a zero output.
- * Supported: dim 512 or 64, n_heads multiple of 16 and <= 64, rope_dim even
- * and <= 64, topk <= 2048. */
+ * Supported: bf16 queries -- dim 512, n_heads in {16, 32, 48, 64}, window and
+ * pool rows DSV4_F16, DSV4_BF16 or DSV4_FP8R (one dtype for both); fp32
+ * queries -- fp32 rows, any even dim <= 512 with 1..64 heads such that
+ * n_heads*dim + 32*dim + 35*n_heads <= 16384; rope_dim even and <= 64,
+ * topk <= 2048.
+ * Range: the bf16 path runs its products on the fp16 matrix cores.  Stored
+ * rows (DSV4_BF16 values, decoded DSV4_FP8R values) and the rotated queries
+ * scaled by sm_scale*log2(e) must stay below 65504 in magnitude (larger values
+ * become infinite and the output NaN); values below 2^-14 lose significand
+ * bits to fp16's subnormal range (at most 2^-24 absolute).  Every workload
+ * here is far inside that range (activations of a few units, FP8 rows at
+ * most 448 x their row scale). */
 size_t dsv4_attn_workspace(int32_t n_rows, int32_t n_heads, int32_t dim, int64_t max_rows_per_query);
 int dsv4_sparse_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int32_t n_heads,
                      int32_t dim, const dsv4_rows *window, int32_t W, const dsv4_rows *pool,

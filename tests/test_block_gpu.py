@@ -105,8 +105,14 @@ def test_csa_block(K, Sx, pos0):
     y_d = lin(oa_d, t(Wob), out_dtype=torch.float32)
     torch.cuda.synchronize()
 
+    # the block's own picks: its keys and queries come from GPU products, which
+    # round to bf16 where the oracle's do not always, so the end-to-end gap bound
+    # applies; on shared stored keys and queries the 1e-5 rule applies
     res = check_topk(idx_g.cpu().numpy(), sc_o, nv, k, "block top-k", gap=1e-3)
     say("top-k rows exact / near-tie", res)
+    idx_s = K.dsv4_index_topk(Q, t(qI), dev(w), upload_rows(kp_set), m, k, ss)
+    torch.cuda.synchronize()
+    say("shared-key top-k", check_topk(idx_s.cpu().numpy(), sc_o, nv, k, "block top-k (shared keys)"))
     assert_close(qa_d.float().cpu().numpy(), qa, "bf16", "q_a")
     assert_close(pool_d.float().cpu().numpy(), pool, "bf16", "pooled K=V entries")
     assert_close(o_d.float().cpu().numpy(), o, "bf16", "attention output")

@@ -4,9 +4,11 @@ Each test builds the bench workload (same seeds, shapes and calls), runs one
 step on the GPU, and checks sampled outputs against the oracle computed from
 the same synthetic inputs (copied back to the host): the oracle recomputes the
 whole chain itself (pool, index keys, rotated window, scores, top-k) and never
-takes a value produced by the HIP path.  Attention outputs are compared on the
-sampled rows whose top-k set equals the oracle's (rows with a near-tie at the
-k-th score may legitimately differ; the gap rule checks those)."""
+takes a value produced by the HIP path.  Top-k is checked under the 1e-5 gap
+rule on stored keys both sides score; attention is rerun in the same launch
+with the oracle's picks for the sampled rows (near-ties inside the gap band may
+resolve either way) and compared on every sampled row.  Each workload also runs
+twice on the same inputs and must give the same bits."""
 import os
 import sys
 
@@ -66,13 +68,26 @@ def _host_rows(rs, seqs, kind):
                     first_tok=None if rs.first_tok is None else rs.first_tok[seqs].cpu().numpy().astype(np.int32))
 
 
+def _same_bits(a, b, what):
+    assert torch.equal(a, b), f"{what}: a second run on the same inputs gave other bits"
+
+
 def test_csa_prefill_S8192(K, bench_mod):
     """Flash-shaped CSA prefill, S=8192: pool, index keys, window rope (every
-    row), top-k and attention on sampled query rows."""
+    row); top-k under the 1e-5 gap rule on >= 256 sampled rows (>= 200 of them
+    with more visible entries than k, so the 2048-entry select runs); attention
+    on every sampled row; the same step twice gives the same bits."""
     wl = bench_mod.CsaPrefill(torch, K, S)
     wl.step()
     torch.cuda.synchronize()
-    Sx, m, R, th, D = wl.S, wl.m, wl.R, wl.theta, wl.D
+    out1, idx1 = wl.out.clone(), wl.idx.clone()
+    wl.step()
+    torch.cuda.synchronize()
+    _same_bits(wl.out, out1, "csa prefill attention")
+    _same_bits(wl.idx, idx1, "csa prefill top-k")
+    del out1, idx1
+    Sx, m, R, th, D, Di = wl.S, wl.m, wl.R, wl.theta, wl.D, wl.Di
+    N = Sx // m
     say("csa prefill S=8192: oracle pools")
     pool_o = O.compress(_b16(wl.c), _b16(wl.z), wl.bias.cpu().numpy(), m, True, R, th, np.zeros(1, np.int64),
                         kind="bf16")
@@ -84,31 +99,49 @@ def test_csa_prefill_S8192(K, bench_mod):
     assert_close(wl.kv_rot[0].float().cpu().numpy(), kv_rot_o, "bf16", "window rope")
 
     rng = np.random.default_rng(8192)
-    rows = np.unique(np.concatenate([[0, 1, 3, 30, 31, 127, 128, 2046, 2047, 2048, 4095, 8190, 8191],
-                                     rng.choice(Sx, 19, replace=False)])).astype(np.int32)
+    fixed = [0, 1, 3, 30, 31, 127, 128, 2046, 2047, 2048, 2050, 2051, 2052, 4095, 4096, 8190, 8191]
+    rows = np.unique(np.concatenate([fixed, rng.choice(np.arange(2052, Sx - 2), 230, replace=False),
+                                     rng.choice(2046, 20, replace=False)])).astype(np.int32)
+    assert len(rows) >= 256
+    nv = O.n_visible(rows, m, N)
+    assert int((nv > wl.k).sum()) >= 200
     seq = np.zeros(len(rows), np.int32)
-    # the index keys are stored as bf16 (the storage type the chain asks for):
-    # the oracle scores its own keys rounded the same way.  Its fp64 pooling and
-    # the kernel's fp32 pooling can still round a few of the 262144 key values
-    # to neighbouring bf16 codes, which moves those entries' scores by ~1e-3;
-    # the gap rule here allows that much (the exact 1e-5 rule applies where
-    # both sides score identical stored keys, in the decode cases below and in
-    # the index parity tests).
-    kp_rows = _f64rows(S.bf16_to_f32(S.bf16_bits(kpool_o.astype(np.float32))))
-    sc = O.index_scores(seq, rows, _b16(wl.q_idx[rows]), "bf16", wl.w[rows].cpu().numpy(), kp_rows, m,
+
+    # (1) top-k on shared stored keys: the oracle's pooled index keys, stored as
+    # bf16, scored by the GPU (all 8192 rows, the benchmark's launch) and by the
+    # oracle (sampled rows); the 1e-5 gap rule applies.
+    kp_bits = S.bf16_bits(kpool_o.astype(np.float32))
+    kp_store = S.RowSet("bf16", kp_bits.view(np.uint8).reshape(1, N, 2 * Di), Di, np.array([N], np.int32))
+    kp_dev = torch.from_numpy(kp_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    idx_s = torch.empty_like(wl.idx)
+    K.dsv4_index_topk(wl.Q, wl.q_idx, wl.w, K.RowStore(kp_dev, K.DSV4_BF16, Di, wl.kpool_rows.count), m, wl.k,
+                      wl.score_scale, ws=wl.ws_idx, out=idx_s)
+    torch.cuda.synchronize()
+    say("oracle scores,", len(rows), "rows")
+    sc = O.index_scores(seq, rows, _b16(wl.q_idx[rows]), "bf16", wl.w[rows].cpu().numpy(), kp_store, m,
                         wl.score_scale)
-    nv = O.n_visible(rows, m, Sx // m)
     idx_o = O.topk(sc, nv, wl.k)
-    idx = wl.idx[rows].cpu().numpy()
-    stats = check_topk(idx, sc, nv, wl.k, "csa prefill S=8192", gap=2e-3)
-    say("top-k", stats)
+    stats = check_topk(idx_s[rows].cpu().numpy(), sc, nv, wl.k, "csa prefill S=8192 (shared keys)")
+    say("top-k on shared keys", stats)
+
+    # (2) the chain's own picks (GPU-pooled keys): exact counts and ranges, and
+    # the end-to-end gap bound for keys pooled in fp32 versus fp64 (one bf16 step
+    # of a few key values moves a score by <= 2e-3 at these statistics)
+    say("chain top-k", check_topk(wl.idx[rows].cpu().numpy(), sc, nv, wl.k, "csa prefill chain", gap=2e-3))
+
+    # (3) attention in the benchmark's launch (all 8192 rows), the sampled rows
+    # taking the oracle's picks; every sampled row is compared
+    idx_mix = wl.idx.clone()
+    idx_mix[torch.from_numpy(rows).long().cuda()] = torch.from_numpy(idx_o).cuda()
+    out2 = torch.empty_like(wl.out)
+    K.dsv4_sparse_attn(wl.Q, wl.q, wl.win_rows, wl.W, wl.pool_rows, idx_mix, wl.sinks, wl.sm_scale, wl.R, wl.theta,
+                       ws=wl.ws_attn, out=out2)
+    torch.cuda.synchronize()
+    say("oracle attention,", len(rows), "rows")
     out_o = O.attn(seq, rows, np.zeros(1, np.int64), _b16(wl.q[rows]), "bf16", _f64rows(kv_rot_o[None], [0]), wl.W,
                    _f64rows(pool_o), "csa", idx=idx_o, sinks=wl.sinks.cpu().numpy(), sm_scale=wl.sm_scale,
                    rope_dim=R, theta=th)
-    same = np.array([np.array_equal(np.sort(a[a >= 0]), np.sort(b[b >= 0])) for a, b in zip(idx, idx_o)])
-    say("rows with the oracle's exact set", int(same.sum()), "of", len(rows))
-    assert same.mean() >= 0.75
-    assert_close(wl.out[rows].float().cpu().numpy()[same], out_o[same], "bf16", "csa attention S=8192")
+    assert_close(out2[rows].float().cpu().numpy(), out_o, "bf16", "csa attention S=8192")
     del wl
     torch.cuda.empty_cache()
 
@@ -119,6 +152,11 @@ def test_hca_prefill_S65536(K, bench_mod):
     wl = bench_mod.HcaPrefill(torch, K, S)
     wl.step()
     torch.cuda.synchronize()
+    out1 = wl.out.clone()
+    wl.step()
+    torch.cuda.synchronize()
+    _same_bits(wl.out, out1, "hca prefill attention")
+    del out1
     Sx, m, R, th, W = wl.S, wl.m, wl.R, wl.theta, wl.W
     say("hca prefill S=65536: oracle pool")
     pool_o = O.compress(_b16(wl.c), _b16(wl.z), wl.bias.cpu().numpy(), m, False, R, th, np.zeros(1, np.int64),
@@ -143,12 +181,30 @@ def test_hca_prefill_S65536(K, bench_mod):
     torch.cuda.empty_cache()
 
 
+def _attn_with_picks(K, wl, out_ref, idx_o, seqs, call):
+    """Rerun the attention call of a decode step in its benchmark launch (every
+    sequence), with the oracle's picks in place of the GPU's for the sampled
+    sequences; returns the sampled outputs.  Near-ties inside the 1e-5 band may
+    resolve either way, so attention is compared on the picks both sides use."""
+    idx_mix = wl.idx.clone()
+    idx_mix[torch.tensor(seqs, device="cuda")] = torch.from_numpy(idx_o).cuda()
+    out = torch.empty_like(out_ref)
+    call(idx_mix, out)
+    torch.cuda.synchronize()
+    return out[seqs].float().cpu().numpy()
+
+
 def test_csa_decode_B32_L131072(K, bench_mod):
     """CSA decode, 32 sequences x 131072 tokens: indexer top-k and FP8
     attention on sampled sequences."""
     wl = bench_mod.CsaDecode(torch, K, S, copies=1)
     wl.step()
     torch.cuda.synchronize()
+    out1, idx1 = wl.out.clone(), wl.idx.clone()
+    wl.step()
+    torch.cuda.synchronize()
+    _same_bits(wl.out, out1, "csa decode attention")
+    _same_bits(wl.idx, idx1, "csa decode top-k")
     pool, win, kp, q, q_idx, w, sinks = wl.sets[0]
     seqs = [0, 13, 31]
     n = len(seqs)
@@ -164,9 +220,9 @@ def test_csa_decode_B32_L131072(K, bench_mod):
     out_o = O.attn(seq, tok, np.zeros(n, np.int64), _b16(q[seqs]), "bf16", _host_rows(win, seqs, "fp8r"), wl.W,
                    _host_rows(pool, seqs, "fp8r"), "csa", idx=idx_o, sinks=sinks.cpu().numpy(), sm_scale=wl.sm_scale,
                    rope_dim=wl.R, theta=wl.theta)
-    same = np.array([np.array_equal(np.sort(a[a >= 0]), np.sort(b[b >= 0])) for a, b in zip(idx, idx_o)])
-    assert same.sum() >= n - 1
-    assert_close(wl.out[seqs].float().cpu().numpy()[same], out_o[same], "bf16", "csa decode attention")
+    got = _attn_with_picks(K, wl, wl.out, idx_o, seqs, lambda idx_mix, out: K.dsv4_sparse_attn(
+        wl.Q, q, win, wl.W, pool, idx_mix, sinks, wl.sm_scale, wl.R, wl.theta, ws=wl.ws_attn, out=out))
+    assert_close(got, out_o, "bf16", "csa decode attention")
     del wl
     torch.cuda.empty_cache()
 
@@ -177,6 +233,12 @@ def test_mixed_decode_B8_L1048576(K, bench_mod):
     wl = bench_mod.MixedDecode(torch, K, S, copies=1)
     wl.step()
     torch.cuda.synchronize()
+    out1, hout1, idx1 = wl.out.clone(), wl.hout.clone(), wl.idx.clone()
+    wl.step()
+    torch.cuda.synchronize()
+    _same_bits(wl.out, out1, "mixed decode CSA attention")
+    _same_bits(wl.hout, hout1, "mixed decode HCA attention")
+    _same_bits(wl.idx, idx1, "mixed decode top-k")
     pool, win, kp, qpk, qsc, q, w, sinks, hpool, hwin, hq, hsinks = wl.sets[0]
     seqs = [2, 7]
     n = len(seqs)
@@ -193,9 +255,9 @@ def test_mixed_decode_B8_L1048576(K, bench_mod):
     out_o = O.attn(seq, tok, np.zeros(n, np.int64), _b16(q[seqs]), "bf16", _host_rows(win, seqs, "fp8r"), wl.W,
                    _host_rows(pool, seqs, "fp8r"), "csa", idx=idx_o, sinks=sinks.cpu().numpy(), sm_scale=wl.sm_scale,
                    rope_dim=wl.R, theta=wl.theta)
-    same = np.array([np.array_equal(np.sort(a[a >= 0]), np.sort(b[b >= 0])) for a, b in zip(idx, idx_o)])
-    assert same.sum() >= n - 1
-    assert_close(wl.out[seqs].float().cpu().numpy()[same], out_o[same], "bf16", "mixed decode CSA attention")
+    got = _attn_with_picks(K, wl, wl.out, idx_o, seqs, lambda idx_mix, out: K.dsv4_sparse_attn(
+        wl.Q, q, win, wl.W, pool, idx_mix, sinks, wl.sm_scale, wl.R, wl.theta, ws=wl.ws_attn, out=out))
+    assert_close(got, out_o, "bf16", "mixed decode CSA attention")
     hout_o = O.attn(seq, tok, np.zeros(n, np.int64), _b16(hq[seqs]), "bf16", _host_rows(hwin, seqs, "fp8r"), wl.W,
                     _host_rows(hpool, seqs, "fp8r"), "hca", m=128, sinks=hsinks.cpu().numpy(), sm_scale=wl.sm_scale,
                     rope_dim=wl.R, theta=wl.theta)
