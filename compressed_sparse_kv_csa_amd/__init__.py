@@ -23,7 +23,9 @@ DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, 
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
            "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant",
-           "dsv4_quantize", "dsv4_cache_append", "dsv4_linear", "dsv4_last_error", "dsv4_version"]
+           "dsv4_quantize", "dsv4_cache_append", "dsv4_linear", "dsv4_last_error", "dsv4_version",
+           "dsv4_index_topk_noalloc"]
+NOALLOC_SCRATCH_BYTES = 16 << 20   # DSV4_NOALLOC_SCRATCH_BYTES in include/dsv4.h
 
 
 class Dsv4Error(RuntimeError):
@@ -78,6 +80,7 @@ def lib():
         L.dsv4_index_topk_workspace.argtypes = [I32, I64, I32]
         L.dsv4_index_topk_workspace.restype = SZ
         L.dsv4_index_topk.argtypes = [P, P, P, I32, P, I32, I32, P, I32, I32, F, P, P, P, SZ, P]
+        L.dsv4_index_topk_noalloc.argtypes = [P, P, P, I32, P, I32, I32, P, I32, I32, F, P, P, P]
         L.dsv4_attn_workspace.argtypes = [I32, I32, I32, I64]
         L.dsv4_attn_workspace.restype = SZ
         L.dsv4_sparse_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, P, I32, P, F, I32, D, P, I32, P, SZ, P]
@@ -327,6 +330,23 @@ def dsv4_index_topk(q: QueryRows, q_idx: torch.Tensor, w: torch.Tensor, k_pool: 
                                  ctypes.byref(kc), m, topk, float(score_scale), _ptr(idx), _ptr(sc), _ptr(ws),
                                  ws.numel(), _stream()))
     return (idx, sc) if want_scores else idx
+
+
+def dsv4_index_topk_noalloc(q: QueryRows, q_idx: torch.Tensor, w: torch.Tensor, k_pool: RowStore, m: int,
+                            topk: int, score_scale: float, out: torch.Tensor, q_idx_scale: Optional[torch.Tensor] = None,
+                            q_dtype: Optional[int] = None, score_out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dsv4_index_topk with the library's static scratch in place of a workspace
+    (for callers that cannot allocate).  The caller passes the output idx
+    [T, topk] int32 (and optionally score_out [T, topk] float32)."""
+    H = w.shape[-1]
+    if q_dtype is None:
+        q_dtype = DSV4_MXFP4 if q_idx.dtype == torch.uint8 else _code(q_idx)
+    assert out.dtype == torch.int32 and out.shape == (q.seq.numel(), topk)
+    qc, kc = q.c(), k_pool.c()
+    _check(lib().dsv4_index_topk_noalloc(ctypes.byref(qc), _ptr(q_idx), _ptr(q_idx_scale), q_dtype, _ptr(w), H,
+                                         k_pool.dim, ctypes.byref(kc), m, topk, float(score_scale), _ptr(out),
+                                         _ptr(score_out), _stream()))
+    return out
 
 
 def index_topk_workspace(n_rows: int, pool_stride: int, topk: int, device="cuda") -> torch.Tensor:

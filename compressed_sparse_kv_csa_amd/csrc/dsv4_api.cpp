@@ -34,6 +34,8 @@ int launch_compress(const void *c, const void *z, int in_dtype, const float *bia
 int launch_rope(const void *x, int x_dtype, void *y, int y_dtype, int64_t n_rows, int dim, int rope_dim,
                 const int64_t *pos, double theta, int inverse, hipStream_t st);
 size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk);
+size_t index_topk_scratch_bytes();
+int index_topk_scratch(void **ptr);
 int index_topk_supported(int64_t stride, int topk);
 int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qscale, int q_dtype, const float *w,
                       int H, int Di, const dsv4_rows *kp, int m, int topk, float scale, int32_t *idx_out,
@@ -237,10 +239,11 @@ size_t dsv4_index_topk_workspace(int32_t n_rows, int64_t pool_seq_stride, int32_
   return index_topk_ws(n_rows, pool_seq_stride, topk);
 }
 
-int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale, int32_t q_dtype,
-                    const float *w, int32_t n_heads, int32_t head_dim, const dsv4_rows *k_pool, int32_t m,
-                    int32_t topk, float score_scale, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
-                    hipStream_t stream) {
+// Argument checks shared by dsv4_index_topk and dsv4_index_topk_noalloc;
+// *need receives the scratch bytes the call uses.
+static int index_topk_check(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale, int32_t q_dtype,
+                            const float *w, int32_t n_heads, int32_t head_dim, const dsv4_rows *k_pool, int32_t m,
+                            int32_t topk, float score_scale, int32_t *idx_out, size_t *need) {
   int rc = check_queries(q);
   if (rc) return rc;
   if (!q_idx || !w || !idx_out) return fail(DSV4_EINVAL, "index_topk: NULL tensor pointer");
@@ -267,11 +270,40 @@ int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_i
   if (!index_topk_supported(k_pool->seq_stride, topk))
     return fail(DSV4_ENOTSUP, "index_topk: pool stride %lld (at most 65535 chunks of 4096 entries)",
                 (long long)k_pool->seq_stride);
-  const size_t need = index_topk_ws(q->n_rows, k_pool->seq_stride, topk);
+  *need = index_topk_ws(q->n_rows, k_pool->seq_stride, topk);
+  return DSV4_OK;
+}
+
+int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale, int32_t q_dtype,
+                    const float *w, int32_t n_heads, int32_t head_dim, const dsv4_rows *k_pool, int32_t m,
+                    int32_t topk, float score_scale, int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+  size_t need = 0;
+  int rc = index_topk_check(q, q_idx, q_idx_scale, q_dtype, w, n_heads, head_dim, k_pool, m, topk, score_scale,
+                            idx_out, &need);
+  if (rc) return rc;
   if (q->n_rows > 0 && (!ws || ws_bytes < need))
     return fail(DSV4_EWORKSPACE, "index_topk: workspace %zu bytes, need %zu", ws_bytes, need);
   rc = launch_index_topk(q, q_idx, q_idx_scale, q_dtype, w, n_heads, head_dim, k_pool, m, topk, score_scale, idx_out,
                          score_out, ws, stream);
+  return rc ? rc : ok();
+}
+
+int dsv4_index_topk_noalloc(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale, int32_t q_dtype,
+                            const float *w, int32_t n_heads, int32_t head_dim, const dsv4_rows *k_pool, int32_t m,
+                            int32_t topk, float score_scale, int32_t *idx_out, float *score_out, hipStream_t stream) {
+  size_t need = 0;
+  int rc = index_topk_check(q, q_idx, q_idx_scale, q_dtype, w, n_heads, head_dim, k_pool, m, topk, score_scale,
+                            idx_out, &need);
+  if (rc) return rc;
+  if (need > index_topk_scratch_bytes())
+    return fail(DSV4_EWORKSPACE, "index_topk_noalloc: the call needs %zu scratch bytes, the static scratch holds %zu",
+                need, index_topk_scratch_bytes());
+  if (q->n_rows == 0) return ok();
+  void *scr = nullptr;
+  if ((rc = index_topk_scratch(&scr))) return rc;
+  rc = launch_index_topk(q, q_idx, q_idx_scale, q_dtype, w, n_heads, head_dim, k_pool, m, topk, score_scale, idx_out,
+                         score_out, scr, stream);
   return rc ? rc : ok();
 }
 

@@ -844,11 +844,41 @@ __global__ __launch_bounds__(256) void k_rt_emit(const int32_t *__restrict__ seq
   }
 }
 
+// Scratch memory of dsv4_index_topk_noalloc (the score rows, histograms,
+// per-chunk counts and thresholds that dsv4_index_topk keeps in the caller's
+// workspace).  One copy per GPU, held until the process ends; host code never
+// passes this name to a kernel, only the address hipGetSymbolAddress returns.
+constexpr size_t kNoAllocScratchBytes = DSV4_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 }  // namespace dsv4
 
 using namespace dsv4;
 
 namespace dsv4host {
+
+size_t index_topk_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of this GPU's scratch array, looked up once per device (with
+// that device current) and kept for later calls.
+int index_topk_scratch(void **ptr) {
+  static std::mutex mu;
+  static std::map<int, void *> addr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSV4_EHIP, "index_topk_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DSV4_EHIP, "index_topk_noalloc: scratch address on device %d: %s", dev, hipGetErrorString(e));
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return DSV4_OK;
+}
 
 // Top-k plan: rows of at most 16384 entries are selected by one workgroup
 // each (k_topk_chunk, KPT keys per thread); longer rows by the radix-threshold

@@ -14,7 +14,8 @@
  *     contiguous as described per argument.  The library allocates nothing,
  *     keeps no pointer after the call returns (apart from work already queued)
  *     and holds no global state beyond its code objects, a thread-local error
- *     string and the batch-invariant switch.
+ *     string, the batch-invariant switch and the static scratch array of
+ *     dsv4_index_topk_noalloc (with its per-device address).
  *   - Every call validates its arguments on the host first; a call that returns
  *     an error has launched nothing.  dsv4_last_error() describes the failure.
  *   - Work is queued on `stream` (a hipStream_t; 0 = the null stream) with no
@@ -150,6 +151,25 @@ int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_i
                     const dsv4_rows *k_pool, int32_t m, int32_t topk, float score_scale,
                     int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
                     hipStream_t stream);
+
+/* dsv4_index_topk_noalloc -- dsv4_index_topk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation and kernels, with the
+ * workspace in a static scratch array of DSV4_NOALLOC_SCRATCH_BYTES inside
+ * the library instead of a caller buffer.  Each GPU holds its own copy from
+ * its first call until the process ends; every call on one GPU shares it, so
+ * calls that overlap on one GPU (other streams, other threads) race and must
+ * be ordered by the caller.  The call allocates nothing; it returns
+ * DSV4_EWORKSPACE (launching nothing) when
+ * dsv4_index_topk_workspace(n_rows, pool_seq_stride, topk) exceeds the
+ * scratch size (e.g. 32 decode rows over 32768-entry pools take 4 MiB, 8 rows
+ * over 262144 entries 8 MiB).  Arguments and errors otherwise as
+ * dsv4_index_topk. */
+#define DSV4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int dsv4_index_topk_noalloc(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale,
+                            int32_t q_dtype, const float *w, int32_t n_heads, int32_t head_dim,
+                            const dsv4_rows *k_pool, int32_t m, int32_t topk, float score_scale,
+                            int32_t *idx_out, float *score_out, hipStream_t stream);
 
 /* dsv4_sparse_attn -- CSA core attention (HF page, "Hybrid attention" backbone
  * bullets and "Attention mask layout", CSA paragraph).  One shared K=V head:

@@ -246,3 +246,19 @@ def test_linear_rejects_bad_args(K):
     assert call(ldy=2) == K.DSV4_EINVAL
     assert call(ldx=68) == K.DSV4_EINVAL              # rows not 16-byte aligned
     assert call(groups=2, gx=4) == K.DSV4_EINVAL
+
+
+def test_index_topk_noalloc_rejects_bad_args(K):
+    """The allocation-free variant checks its arguments like dsv4_index_topk and
+    refuses, before touching the device, a call whose scratch need exceeds the
+    static array."""
+    L = K.lib()
+    fake = ctypes.c_void_p(0x1000)
+    q = _queries(K)
+    args = lambda **o: [ctypes.byref(o.get("q", q)), fake, None, K.DSV4_BF16, fake, 64, 128,
+                        ctypes.byref(o.get("kp", _rows(K, K.DSV4_BF16, 128))), 4, o.get("k", 8), 0.1, fake, None, None]
+    assert _rc(L.dsv4_index_topk_noalloc(*args(k=0))) == K.DSV4_EINVAL
+    big = _rows(K, K.DSV4_BF16, 128, seq_stride=1 << 21)   # 4 rows x 2^21 entries x 4 B = 32 MiB of scores
+    assert L.dsv4_index_topk_workspace(4, 1 << 21, 8) > K.NOALLOC_SCRATCH_BYTES
+    assert _rc(L.dsv4_index_topk_noalloc(*args(kp=big))) == K.DSV4_EWORKSPACE
+    assert "scratch" in K.dsv4_last_error()
