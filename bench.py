@@ -89,6 +89,10 @@ def hca_prefill_counts(S, m, W, H, D):
 class CsaPrefill:
     """Flash-shaped CSA layer prefill (batch 1, seq 8192, bf16)."""
     name = "flash_csa_prefill_S8192"
+    dom_kernel = "k_attn_f16<"
+    dom_desc = "k_attn_f16 (fp16 MFMA, fp32 accumulate)"
+    stats_summary = "csa_prefill_S8192_kernel_stats.txt"
+    hbm_summary = "k_attn_f16_csa_prefill_S8192_hbm.txt"
 
     def __init__(self, torch, K, S_, seed=1002, S=8192, H=64, D=512, R=64, W=128, Hi=64, Di=128, k=512, m=4):
         self.torch, self.K = torch, K
@@ -151,6 +155,10 @@ class CsaPrefill:
 class HcaPrefill:
     """Flash-shaped HCA layer prefill (batch 1, seq 65536, m'=128, bf16)."""
     name = "flash_hca_prefill_S65536"
+    dom_kernel = "k_attn_f16<"
+    dom_desc = "k_attn_f16 (fp16 MFMA, fp32 accumulate)"
+    stats_summary = "hca_prefill_S65536_kernel_stats.txt"
+    hbm_summary = "k_attn_f16_hca_prefill_S65536_hbm.txt"
 
     def __init__(self, torch, K, S_, seed=1003, S=65536, H=64, D=512, R=64, W=128, m=128):
         self.torch, self.K = torch, K
@@ -262,6 +270,23 @@ class CsaDecode:
         K.dsv4_sparse_attn(self.Q, q, win, self.W, pool, self.idx, sinks, self.sm_scale, self.R, self.theta,
                            ws=self.ws_attn, out=self.out)
 
+    def attn_calls(self):
+        """The step's attention launches (on the last step's inputs and picks):
+        [(name, callable, algorithmic bytes, split partial bytes)]."""
+        K = self.K
+        pool, win, kp, q, q_idx, w, sinks = self.sets[(self.i - 1) % len(self.sets)]
+        row = (self.D - self.R) + 2 * self.R + 4
+        alg = self.B * (self.k + self.W) * row + 2 * self.B * self.H * self.D * 2 + self.B * self.k * 4
+        f = lambda: K.dsv4_sparse_attn(self.Q, q, win, self.W, pool, self.idx, sinks, self.sm_scale, self.R,
+                                       self.theta, ws=self.ws_attn, out=self.out)
+        return [("csa_attn", f, alg, _partial_bytes(K, self.B, self.H, self.D, self.W + self.k))]
+
+
+def _partial_bytes(K, T, H, D, max_rows):
+    """Bytes of split partials written and read back by the merge (0 without splits)."""
+    ws = K.lib().dsv4_attn_workspace(T, H, D, max_rows)
+    return 0 if ws == 0 else 2 * (ws - 256)
+
 
 class MixedDecode:
     """1M-token mixed decode: 8 sequences at 1,048,576 tokens; one CSA layer (m=4,
@@ -331,6 +356,22 @@ class MixedDecode:
         K.dsv4_hca_attn(self.Q, hq, hwin, self.W, hpool, 128, hsinks, self.sm_scale, self.R, self.theta,
                         ws=self.ws_hca, out=self.hout)
 
+    def attn_calls(self):
+        """The step's attention launches: [(name, callable, algorithmic bytes, split partial bytes)]."""
+        K = self.K
+        pool, win, kp, qpk, qsc, q, w, sinks, hpool, hwin, hq, hsinks = self.sets[(self.i - 1) % len(self.sets)]
+        row = (self.D - self.R) + 2 * self.R + 4
+        qo = 2 * self.B * self.H * self.D * 2
+        Nh = self.L // 128
+        csa = lambda: K.dsv4_sparse_attn(self.Q, q, win, self.W, pool, self.idx, sinks, self.sm_scale, self.R,
+                                         self.theta, ws=self.ws_attn, out=self.out)
+        hca = lambda: K.dsv4_hca_attn(self.Q, hq, hwin, self.W, hpool, 128, hsinks, self.sm_scale, self.R,
+                                      self.theta, ws=self.ws_hca, out=self.hout)
+        return [("csa_attn", csa, self.B * (self.k + self.W) * row + qo + self.B * self.k * 4,
+                 _partial_bytes(K, self.B, self.H, self.D, self.W + self.k)),
+                ("hca_attn", hca, self.B * (Nh + self.W) * row + qo,
+                 _partial_bytes(K, self.B, self.H, self.D, self.W + Nh))]
+
 
 class CsaBlock(CsaPrefill):
     """The Flash CSA attention block from hidden states (batch 1, seq 8192):
@@ -396,7 +437,8 @@ WORKLOADS = {"csa_prefill": CsaPrefill, "hca_prefill": HcaPrefill, "csa_decode":
 
 def time_steps(torch, wl, steps, warmup):
     """W untimed steps, then exactly K steps between two synchronisations; the
-    dominant kernel is bracketed with events on the launch stream every step."""
+    dominant kernel is bracketed with events on the launch stream every step
+    (the library launches on torch's current stream, which the events see)."""
     for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
@@ -407,7 +449,87 @@ def time_steps(torch, wl, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     kern = [a.elapsed_time(b) for a, b in evs]
-    return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), float(np.median(kern))
+    return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), float(np.median(kern)), kern
+
+
+def decode_attn_roofline(torch, wl, reps=10):
+    """Each attention launch of a decode step timed alone (HIP events on the
+    launch stream; split merge included) against the HBM peak: algorithmic
+    bytes (gathered and window rows with their scales, q in, o out, picks) and
+    the split partials the merge writes and reads back, reported apart."""
+    wl.step()
+    torch.cuda.synchronize()
+    out = {}
+    for name, call, alg, part in wl.attn_calls():
+        call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        t = [a.elapsed_time(b) for a, b in ev]
+        ms = float(np.median(t))
+        out[name] = {"ms_median": round(ms, 4), "algorithmic_bytes": int(alg), "GB_per_s": round(alg / ms / 1e6, 1),
+                     "frac_hbm_peak": round(alg / ms / 1e6 / PEAK_HBM, 4), "split_partial_bytes": int(part),
+                     "GB_per_s_with_partials": round((alg + part) / ms / 1e6, 1)}
+    return {"attention": out}
+
+
+def pcts(xs):
+    """p10 / p50 / p90 of a list of per-step milliseconds."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
+def platform_info(torch):
+    """ROCm / HIP versions and the GPU's shader clock levels (sysfs), for the record."""
+    info = {"device": torch.cuda.get_device_name(0), "hip": getattr(torch.version, "hip", None),
+            "torch": torch.__version__}
+    try:
+        info["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        import glob
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            lv = [ln.split(":", 1)[1].strip() for ln in open(f).read().splitlines() if ":" in ln]
+            if lv:
+                info["sclk_levels"] = lv
+                info["sclk_max_mhz"] = max(int("".join(ch for ch in x.split("Mhz")[0] if ch.isdigit()) or 0)
+                                           for x in lv)
+                break
+    except (OSError, ValueError):
+        pass
+    return info
+
+
+def profile_kernel_us(summary, kernel_prefix):
+    """Average duration (us) of a kernel in a committed rocprofv3 kernel-trace
+    summary, or None when the summary is missing, names no such kernel, or the
+    kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        text = open(path).read()
+        kv = dict(ln.split(": ", 1) for ln in text.splitlines() if ": " in ln and not ln.startswith(" "))
+        if "source_files" in kv:
+            h = hashlib.sha256()
+            for f in kv["source_files"].split():
+                h.update(open(os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f), "rb").read())
+            if h.hexdigest() != kv["source_sha256"].strip():
+                return None
+        else:
+            return None
+        for ln in text.splitlines():
+            parts = ln.split()
+            if len(parts) >= 6 and kernel_prefix in ln and parts[0].isdigit():
+                return float(parts[1])
+    except (OSError, KeyError, ValueError):
+        return None
+    return None
 
 
 def _outputs(wl):
@@ -439,15 +561,19 @@ def time_steps_graph(torch, wl, steps, warmup):
         torch.cuda.synchronize()
     except Exception as e:   # noqa: BLE001 - report and fall back to eager timing
         log("graph capture unavailable:", repr(e))
-        return None
+        return None, None
     for i in range(warmup):
         graphs[i % n].replay()
     torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     for i in range(steps):
+        marks[i].record()
         graphs[i % n].replay()
+    marks[steps].record()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
+    per_step = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
     for j in range(n):
         graphs[j].replay()
         torch.cuda.synchronize()
@@ -459,7 +585,7 @@ def time_steps_graph(torch, wl, steps, warmup):
         for a, b in zip(got, _outputs(wl)):
             assert torch.equal(a, b), "graph replay differs from the eager step"
     del graphs
-    return ms
+    return ms, per_step
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -513,11 +639,98 @@ def cpu_baseline_csa_prefill(torch, wl, target_s=12.0):
     t_rows = run_rows(sample)
     per_row = t_rows / n
     est = t_shared + per_row * S
-    return {"value": S / est, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+    # one host thread: a smaller sample of the same rows
+    nthr = O.num_threads()
+    O.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        O.compress(c, z, bias, m, True, R, th, np.zeros(1, np.int64), kind="bf16")
+        O.compress(ci, zi, bias_i, m, True, kind="bf16")
+        O.rope(kv, np.arange(S), R, th, +1)
+        t_shared1 = time.perf_counter() - t0
+        n1 = 48
+        t_rows1 = run_rows(np.sort(rng.choice(S, n1, replace=False)))
+    finally:
+        O.set_num_threads(nthr)
+    est1 = t_shared1 + t_rows1 / n1 * S
+    return {"value": S / est, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
             "sample": (f"fp64 oracle: both compressors + window rope over all {S} tokens ({t_shared:.2f} s), then "
                        f"indexer + top-k + attention for {n} random query rows ({t_rows:.2f} s), per-row cost "
                        f"scaled to {S} rows"),
-            "seconds": round(t_shared + t_rows + t_probe, 2)}
+            "extrapolated": n < S,
+            "value_1thread": round(S / est1, 2), "extrapolated_1thread": True,
+            "sample_1thread": f"{n1} random rows on one thread ({t_rows1:.2f} s), shared work {t_shared1:.2f} s",
+            "cpu_model": cpu_model(), "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
+            "seconds": round(t_shared + t_rows + t_probe + t_shared1 + t_rows1, 2)}
+
+
+def cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _host_rows(torch, S_, rs, b, kind):
+    """Sequence b of a device RowStore as a one-sequence host RowSet."""
+    data = rs.data[b:b + 1].contiguous().view(torch.uint8).cpu().numpy().reshape(1, rs.stride, -1)
+    pick = lambda t: None if t is None else t[b:b + 1].cpu().numpy()
+    return S_.RowSet(kind, data, rs.dim, rs.count[b:b + 1].cpu().numpy().astype(np.int32), tail=rs.tail,
+                     row_scale=pick(rs.row_scale), blk_scale=pick(rs.blk_scale),
+                     first_tok=pick(rs.first_tok) if rs.first_tok is not None else None)
+
+
+def cpu_baseline_decode(torch, wl):
+    """The fp64 oracle on one sequence of a decode step (its whole indexer scan,
+    top-k and attention; for the mixed step also the HCA layer), scaled to the
+    step's B sequences: step time and effective GB/s of the step's algorithmic
+    bytes."""
+    import dsv4_synth as S_
+    import oracle as O
+    O.build()
+    b16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    mixed = isinstance(wl, MixedDecode)
+    st = wl.sets[0]
+    b = 0
+    tok = np.array([wl.L - 1], np.int32)
+    seq = np.zeros(1, np.int32)
+    p0 = np.zeros(1, np.int64)
+    if mixed:
+        pool, win, kp, qpk, qsc, q, w, sinks, hpool, hwin, hq, hsinks = st
+        m, kind = 4, "mxfp4"
+        qi, qis = qpk[b:b + 1].cpu().numpy(), qsc[b:b + 1].cpu().numpy()
+    else:
+        pool, win, kp, q, q_idx, w, sinks = st
+        m, kind = wl.m, "bf16"
+        qi, qis = b16(q_idx[b:b + 1]), None
+    kp_h = _host_rows(torch, S_, kp, b, kind)
+    pool_h, win_h = _host_rows(torch, S_, pool, b, "fp8r"), _host_rows(torch, S_, win, b, "fp8r")
+    t0 = time.perf_counter()
+    sc = O.index_scores(seq, tok, qi, kind, w[b:b + 1].cpu().numpy(), kp_h, m, wl.score_scale, q_scale=qis)
+    nv = O.n_visible(tok, m, kp_h.count)
+    idx = O.topk(sc, nv, wl.k)
+    t1 = time.perf_counter()
+    O.attn(seq, tok, p0, b16(q[b:b + 1]), "bf16", win_h, wl.W, pool_h, "csa", idx=idx, sinks=sinks.cpu().numpy(),
+           sm_scale=wl.sm_scale, rope_dim=wl.R, theta=wl.theta)
+    t2 = time.perf_counter()
+    t_hca = 0.0
+    if mixed:
+        hpool_h, hwin_h = _host_rows(torch, S_, hpool, b, "fp8r"), _host_rows(torch, S_, hwin, b, "fp8r")
+        t3 = time.perf_counter()
+        O.attn(seq, tok, p0, b16(hq[b:b + 1]), "bf16", hwin_h, wl.W, hpool_h, "hca", m=128,
+               sinks=hsinks.cpu().numpy(), sm_scale=wl.sm_scale, rope_dim=wl.R, theta=wl.theta)
+        t_hca = time.perf_counter() - t3
+    per_seq = (t1 - t0) + (t2 - t1) + t_hca
+    step_s = per_seq * wl.B
+    return {"value": round(wl.bytes["total"] / step_s / 1e9, 3), "unit": "GB/s", "cores": O.num_threads(),
+            "kind": "oracle", "extrapolated": True, "step_ms": round(step_s * 1e3, 1),
+            "sample": (f"fp64 oracle on sequence 0 of {wl.B}: indexer scan + top-k {t1 - t0:.2f} s, CSA attention "
+                       f"{t2 - t1:.2f} s" + (f", HCA attention {t_hca:.2f} s" if mixed else "") +
+                       f"; scaled to {wl.B} sequences"),
+            "cpu_model": cpu_model()}
 
 
 # ----------------------------------------------------------------------------- main
@@ -549,11 +762,11 @@ def main():
     wl = WORKLOADS[args.workload](torch, K, S_)
     torch.cuda.synchronize()
     log("timing", args.steps, "steps after", args.warmup, "warmup")
-    ms, kern_ms, kern_med = time_steps(torch, wl, args.steps, args.warmup)
+    ms, kern_ms, kern_med, kern_all = time_steps(torch, wl, args.steps, args.warmup)
     log(f"eager: ms/step {ms:.3f}; dominant kernel mean {kern_ms:.3f} ms")
-    ms_eager, timing = ms, "eager launches"
+    ms_eager, timing, per_step = ms, "eager launches", None
     if not args.no_graph:
-        gms = time_steps_graph(torch, wl, args.steps, args.warmup)
+        gms, per_step = time_steps_graph(torch, wl, args.steps, args.warmup)
         if gms is not None:
             ms, timing = gms, "HIP graph replay (outputs checked against an eager step)"
             log(f"graph: ms/step {ms:.3f}")
@@ -561,6 +774,9 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded, device-drawn N(0,1.28^2) activations)",
            "timing": timing, "ms_per_step_eager": round(ms_eager, 4)}
+    if per_step:
+        rec["ms_per_step_replays"] = pcts(per_step)
+    rec["platform"] = platform_info(torch)
     if isinstance(wl, CsaBlock):
         rec["value"] = round(wl.tokens() / (ms / 1e3), 1)
         rec["unit"] = "tokens/s"
@@ -578,13 +794,20 @@ def main():
         rec["unit"] = "tokens/s"
         flop = wl.counts["attn_flop"]
         ach = flop / (kern_ms / 1e3) / 1e12
-        traffic = measured_traffic("k_attn_f16_csa_prefill_S8192_hbm.txt") if isinstance(wl, CsaPrefill) else None
-        rec["roofline"] = {"bound": "mfma", "kernel": "k_attn_f16 (fp16 MFMA, fp32 accumulate)",
+        traffic = measured_traffic(wl.hbm_summary)
+        rec["roofline"] = {"bound": "mfma", "kernel": wl.dom_desc,
                            "achieved": round(ach, 2), "peak": PEAK_MFMA_F16, "unit": "TFLOP/s",
                            "frac": round(ach / PEAK_MFMA_F16, 4), "traffic": traffic,
                            "algorithmic": f"{flop / 1e9:.1f} GFLOP per launch ({wl.counts['attn_pairs']} query-row "
                                           f"pairs x 64 heads x 512 x 4)",
-                           "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_median": round(kern_med, 4)}
+                           "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_median": round(kern_med, 4),
+                           "kernel_ms_events": pcts(kern_all)}
+        prof_us = profile_kernel_us(wl.stats_summary, wl.dom_kernel)
+        if prof_us:
+            pa = flop / (prof_us / 1e6) / 1e12
+            rec["roofline"].update({"kernel_us_profile": prof_us, "achieved_profile": round(pa, 2),
+                                    "frac_profile": round(pa / PEAK_MFMA_F16, 4),
+                                    "profile": "profiles/" + wl.stats_summary})
         rec["config"] = {"workload": wl.name, "seq_len": wl.S, "heads": wl.H, "head_dim": wl.D,
                          "window": wl.W, "m": wl.m}
         if isinstance(wl, CsaPrefill):
@@ -597,8 +820,11 @@ def main():
         ach = kb / (kern_ms / 1e3) / 1e9
         rec["roofline"] = {"bound": "hbm", "kernel": "dsv4_index_topk (key scan + top-k)", "achieved": round(ach, 1),
                            "peak": PEAK_HBM, "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "traffic": None,
-                           "kernel_ms_mean": round(kern_ms, 4)}
+                           "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_events": pcts(kern_all)}
         rec["config"] = {"workload": wl.name, "bytes_per_step": wl.bytes}
+        if not args.no_cpu:
+            log("cpu baseline (oracle, one sequence of the decode step)")
+            rec["cpu_baseline"] = cpu_baseline_decode(torch, wl)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -617,9 +843,10 @@ def main():
             log("leg", name)
             lw = WORKLOADS[name](torch, K, S_)
             torch.cuda.synchronize()
-            lms, lk, _ = time_steps(torch, lw, args.leg_steps, 2)
+            lms, lk, _, _ = time_steps(torch, lw, args.leg_steps, 2)
+            lper = None
             if not args.no_graph:
-                gms = time_steps_graph(torch, lw, args.leg_steps, 2)
+                gms, lper = time_steps_graph(torch, lw, args.leg_steps, 2)
                 lms = gms if gms is not None else lms
             if isinstance(lw, CsaBlock):
                 ach = lw.qb_flop / (lk / 1e3) / 1e12
@@ -640,6 +867,11 @@ def main():
                 legs[name] = {"workload": lw.name, "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM, 4),
                               "ms_per_step": round(lms, 4), "bytes_per_step": lw.bytes["total"],
                               "index_topk_ms": round(lk, 4), "index_scan_GB_per_s": round(ik, 1)}
+                legs[name].update(decode_attn_roofline(torch, lw))
+                if not args.no_cpu:
+                    legs[name]["cpu_baseline"] = cpu_baseline_decode(torch, lw)
+            if lper:
+                legs[name]["ms_per_step_replays"] = pcts(lper)
             log(name, legs[name])
             del lw
             torch.cuda.empty_cache()
