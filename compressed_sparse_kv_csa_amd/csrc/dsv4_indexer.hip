@@ -22,10 +22,12 @@
 //       on register-resident order-preserving keys (8-bit digits counted from
 //       the top of the keys' own range), ties to the lower index, stable
 //       compaction so indices come out ascending.
-//   k_rt_hist / k_rt_count / k_rt_emit  longer rows: the exact kk-th largest
-//       key from three global histogram passes (11 + 11 + 10 bits) over every
-//       chunk of the row, then per-chunk counts and an ordered emission; the
-//       same picks, spread over (row, chunk) workgroups.
+//   k_rt_cand / k_rt_final  longer rows: a histogram of the top 11 key bits
+//       (built while the decode scan stores the scores) bounds the kk-th
+//       largest key from below; the keys at or above that bound are
+//       compacted in position order, and one workgroup per row selects the
+//       exact picks among them (or over the whole row when a chunk's
+//       candidates overflow).
 #include "dsv4_common.h"
 
 #include <algorithm>
@@ -76,21 +78,26 @@ __device__ __forceinline__ float keyf(uint32_t k) {
 // The key loads of iteration it+1 are issued before the MFMAs of iteration it
 // (two register stages), so each wave keeps 2*EB*16 key rows in flight: the
 // decode scan is one pass over a large pool and is bound by how many bytes
-// are outstanding, not by the matrix cores.
+// are outstanding, not by the matrix cores.  With hist0 set (rows that take
+// the long-row top-k) every stored score is also counted in an LDS histogram
+// of its key's top 11 bits, added to the row's histogram at the end.
+constexpr int kHistBins = 2048;
 template <int NHB, int KS, bool FP4, int EB>
-__global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, uint32_t *hzero,
-                                                           int hwords, float *__restrict__ scores, int64_t ld) {
+__global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, uint32_t *hist0,
+                                                           float *__restrict__ scores, int64_t ld) {
+  __shared__ uint32_t lh[kHistBins];
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  // clear this row's top-k histograms (when the radix passes follow)
-  if (hzero && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < hwords; i += 256) hzero[(int64_t)r * hwords + i] = 0u;
   const int b = Q.seq[r];
   const int hi = n_visible(Q.tok[r], K.m, K.count[b]);
   constexpr int STEP = 64 * EB;   // entries per super-block
   if ((int64_t)blockIdx.y * STEP >= hi) return;
   const int H = Q.H, Di = Q.Di;
+  if (hist0) {
+    for (int i = threadIdx.x; i < kHistBins; i += 256) lh[i] = 0u;
+    __syncthreads();
+  }
 
   // query operand and head weights in registers
   bf16x8 qb[NHB][FP4 ? 1 : KS];
@@ -154,7 +161,11 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
       // sum over the four lane groups (heads 4g..4g+3 of every head block)
       s = rows_sum(s);
       const int e = e0 + 16 * eb + c;
-      if (g == 0 && e < hi) scores[(int64_t)r * ld + e] = s * scale;
+      if (g == 0 && e < hi) {
+        const float v = s * scale;
+        scores[(int64_t)r * ld + e] = v;
+        if (hist0) atomicAdd(&lh[fkey(v) >> 21], 1u);
+      }
     }
   };
   const int gstride = (int)gridDim.y * STEP;
@@ -168,6 +179,11 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
     if (e1 >= hi) break;
     if (e1 + gstride < hi) load(e1 + gstride, f0);
     comp(e1, f1);
+  }
+  if (hist0) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kHistBins; i += 256)
+      if (lh[i]) atomicAdd(&hist0[(int64_t)r * kHistBins + i], lh[i]);
   }
 }
 
@@ -588,27 +604,35 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ 
   }
 }
 
-// -------------------------------------------------------------------- long rows: radix threshold
+// -------------------------------------------------------------------- long rows: candidates
 // Rows longer than one workgroup's 16384 register-resident keys (decode over
-// long pools) are selected by finding the exact kk-th largest key t* of the
-// row with three histogram passes over all of the row's chunks (11, 11 and 10
-// key bits, global atomic histograms), then counting, per chunk of 4096 keys,
-// the keys above t* and equal to t*, and emitting: every key above t*, and the
-// lowest-position keys equal to t* up to kk.  Every pass runs one workgroup
-// per (row, chunk), so a few long rows still spread over the whole GPU; the
-// picks come out in ascending position order (per-chunk prefix counts), with
-// the same result as the register-resident select.
-constexpr int kRtChunk = 4096;   // keys per workgroup: 16 per thread
-constexpr int kRtBins = 2048;
+// long pools) take three steps:
+//   1. a histogram of the top 11 key bits over the whole row (built by the
+//      decode scoring kernel as it stores the scores, or by k_rt_hist0);
+//   2. k_rt_cand, one workgroup per (row, chunk): the bin b0 holding the
+//      kk-th largest key is found from the histogram, and every key at or
+//      above b0's lower edge is a candidate; each chunk compacts its
+//      candidates in position order into its own slot range (at most cc
+//      slots; the true count is recorded).  The candidates hold every key of
+//      the top kk, since the histogram counted at least kk keys at or above
+//      the edge;
+//   3. k_rt_final, one workgroup per row: the candidates above bin b0 are all
+//      picked; the keys of bin b0 are refined by two more histogram levels
+//      (11 and 10 bits, spread over many bins, so LDS atomics rarely collide)
+//      to the exact kk-th largest key t*; the keys above t* and the
+//      lowest-position keys equal to t* are written in ascending position
+//      order.  A row whose chunk overflowed its slots or that has more than
+//      8192 candidates (heavy ties at the edge) is selected by the same
+//      workgroup over the whole score row instead: three histogram levels
+//      (11, 11, 10 bits), then the ordered emission.
+constexpr int kRtChunk = 4096;    // keys per load round: 16 per thread
+constexpr int kRtBins = 2048;     // level-0 histogram (top 11 key bits)
+constexpr int kCandSlots = 16384; // candidate slots per row (the select's register capacity)
+constexpr int kCandMaxChunks = 64;
+constexpr int kCandRow = kCandMaxChunks + 4;   // per row: chunk counts, then b0 and the count above it
 
-struct RtHist {                   // per row
-  uint32_t h[3][kRtBins];
-  uint32_t st[2][4];              // prefix, above, want after levels 1 and 2
-};
-
-__device__ __forceinline__ int rt_pos(int j) { return 4 * ((int)threadIdx.x + 256 * (j >> 2)) + (j & 3); }
-
-// keys of chunk c of row r (0 = no entry)
+// keys of positions lo + 4*(t + 256q) + e (q, e < 4) of row r (0 = no entry at
+// or past n)
 __device__ __forceinline__ void rt_load(const float *scores, int64_t ld, int r, int lo, int n, uint32_t (&k)[16]) {
   const float *src = scores + (int64_t)r * ld + lo;
   const bool vec = ((((int64_t)r * ld + lo) & 3) == 0) && (((uintptr_t)scores & 15) == 0);
@@ -676,172 +700,310 @@ __device__ __forceinline__ RtThr rt_next(const uint32_t *h, int nb, int bits, Rt
   return RtThr{(t.prefix << bits) | (uint32_t)bin, t.above + ab, t.want - ab};
 }
 
-// grid (3*kRtBins*T/256), 256 threads: clear the histograms
+// grid ((n + 255) / 256), 256 threads: clear n words
 __global__ __launch_bounds__(256) void k_rt_zero(uint32_t *h, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) h[i] = 0u;
 }
 
-// grid (T, n_chunks), 256 threads: histogram level L (0, 1, 2) of the keys
-// that match the prefix fixed by the levels before it
+// Add the keys of positions [lo, hi) of row r (a multiple of kRtChunk apart)
+// to the LDS histogram lh: level 0 all keys by their top 11 bits; level 1 the
+// keys whose top 11 bits equal the prefix, by the next 11; level 2 the keys
+// whose top 22 bits equal it, by the last 10.
 template <int L>
-__global__ __launch_bounds__(256) void k_rt_hist(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
-                                                 const int32_t *__restrict__ count, int m, const float *__restrict__ scores,
-                                                 int64_t ld, int topk, RtHist *__restrict__ hist) {
-  __shared__ uint32_t lh[kRtBins];
-  __shared__ uint32_t sh[8];
-  const int r = blockIdx.x, lo = blockIdx.y * kRtChunk;
-  const int n = n_visible(tok[r], m, count[seq[r]]);
-  const int kk = min(topk, n);
-  if (kk == n || lo >= n) return;   // every entry taken, or nothing here
-  RtHist &H = hist[r];
-  // the prefix fixed by the levels before this one: level 1 scans level 0's
-  // histogram; level 2 starts from the state level 1's chunk 0 recorded
-  RtThr t{0u, 0u, (uint32_t)kk};
-  if constexpr (L == 1) t = rt_next(H.h[0], kRtBins, 11, t, sh);
-  if constexpr (L == 2) t = rt_next(H.h[1], kRtBins, 11, RtThr{H.st[0][0], H.st[0][1], H.st[0][2]}, sh);
-  if (L > 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    H.st[L - 1][0] = t.prefix;
-    H.st[L - 1][1] = t.above;
-    H.st[L - 1][2] = t.want;
-  }
-  for (int i = threadIdx.x; i < kRtBins; i += 256) lh[i] = 0u;
-  uint32_t k[16];
-  rt_load(scores, ld, r, lo, n, k);
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t key = k[j];
-    if (key == 0u) continue;
-    if constexpr (L == 0) atomicAdd(&lh[key >> 21], 1u);
-    else if constexpr (L == 1) {
-      if ((key >> 21) == t.prefix) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
-    } else {
-      if ((key >> 10) == t.prefix) atomicAdd(&lh[key & 1023u], 1u);
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < (L == 2 ? 1024 : kRtBins); i += 256)
-    if (lh[i]) atomicAdd(&H.h[L][i], lh[i]);
-}
-
-// grid (T, n_chunks), 256 threads: keys above t* and equal to t* per chunk;
-// chunk 0 also records (t*, keys wanted at t*)
-__global__ __launch_bounds__(256) void k_rt_count(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
-                                                  const int32_t *__restrict__ count, int m,
-                                                  const float *__restrict__ scores, int64_t ld, int topk,
-                                                  const RtHist *__restrict__ hist, uint32_t *__restrict__ cnt,
-                                                  uint32_t *__restrict__ thr) {
-  __shared__ uint32_t sh[8];
-  const int r = blockIdx.x, c = blockIdx.y, nch = gridDim.y, lo = c * kRtChunk;
-  const int n = n_visible(tok[r], m, count[seq[r]]);
-  const int kk = min(topk, n);
-  uint32_t gt = 0, eq = 0;
-  if (kk < n && lo < n) {
-    const RtHist &H = hist[r];
-    const RtThr t = rt_next(H.h[2], 1024, 10, RtThr{H.st[1][0], H.st[1][1], H.st[1][2]}, sh);
+__device__ __forceinline__ void rt_hist_range(const float *scores, int64_t ld, int r, int lo, int hi, uint32_t prefix,
+                                              uint32_t *lh) {
+  for (int base = lo; base < hi; base += kRtChunk) {
     uint32_t k[16];
-    rt_load(scores, ld, r, lo, n, k);
+    rt_load(scores, ld, r, base, hi, k);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      gt += k[j] > t.prefix ? 1u : 0u;
-      eq += k[j] == t.prefix ? 1u : 0u;
+      const uint32_t key = k[j];
+      if (key == 0u) continue;
+      if constexpr (L == 0) atomicAdd(&lh[key >> 21], 1u);
+      else if constexpr (L == 1) {
+        if ((key >> 21) == prefix) atomicAdd(&lh[(key >> 10) & 2047u], 1u);
+      } else {
+        if ((key >> 10) == prefix) atomicAdd(&lh[key & 1023u], 1u);
+      }
     }
-    uint32_t tot;
-    tk_scan(gt, sh, &tot);
-    gt = tot;
-    __syncthreads();
-    tk_scan(eq, sh, &tot);
-    eq = tot;
-    if (c == 0 && threadIdx.x == 0) {
-      thr[2 * r] = t.prefix;
-      thr[2 * r + 1] = t.want;
-    }
-  }
-  if (threadIdx.x == 0) {
-    cnt[2 * ((int64_t)r * nch + c)] = gt;
-    cnt[2 * ((int64_t)r * nch + c) + 1] = eq;
   }
 }
 
-// grid (T, n_chunks), 256 threads: write the picks in ascending position order
-__global__ __launch_bounds__(256) void k_rt_emit(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
-                                                 const int32_t *__restrict__ count, int m,
-                                                 const float *__restrict__ scores, int64_t ld, int topk,
-                                                 const uint32_t *__restrict__ cnt, const uint32_t *__restrict__ thr,
-                                                 int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
-  __shared__ uint32_t sh[8];
-  const int r = blockIdx.x, c = blockIdx.y, nch = gridDim.y, lo = c * kRtChunk;
+// grid (T, n_chunks), 256 threads: the level-0 histogram of rows whose scores
+// came from a kernel that does not build it (many-query and fp32 scoring)
+__global__ __launch_bounds__(256) void k_rt_hist0(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                  const int32_t *__restrict__ count, int m,
+                                                  const float *__restrict__ scores, int64_t ld, int topk,
+                                                  uint32_t *__restrict__ hist0) {
+  __shared__ uint32_t lh[kRtBins];
+  const int r = blockIdx.x, lo = blockIdx.y * kRtChunk;
   const int n = n_visible(tok[r], m, count[seq[r]]);
-  const int kk = min(topk, n);
-  int32_t *io = idx_out + (int64_t)r * topk;
-  float *so = score_out ? score_out + (int64_t)r * topk : nullptr;
-  if (c == 0)
-    for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
-      io[j] = -1;
-      if (so) so[j] = -INFINITY;
-    }
-  if (lo >= n) return;
-  if (kk == n) {   // every visible entry is taken, in order
-    for (int j = threadIdx.x; j < min(kRtChunk, n - lo); j += 256) {
-      io[lo + j] = lo + j;
-      if (so) so[lo + j] = scores[(int64_t)r * ld + lo + j];
-    }
-    return;
-  }
-  const uint32_t tstar = thr[2 * r], want = thr[2 * r + 1];
-  // keys above t* (G) and equal to t* (E) in the chunks before this one; the
-  // equal keys are taken in position order up to `want`, so the picks before
-  // this chunk are G + min(E, want)
-  uint32_t gsum = 0, esum = 0;
-  for (int cc = threadIdx.x; cc < c; cc += 256) {
-    gsum += cnt[2 * ((int64_t)r * nch + cc)];
-    esum += cnt[2 * ((int64_t)r * nch + cc) + 1];
-  }
-  uint32_t G, E;
-  tk_scan(gsum, sh, &G);
+  if (min(topk, n) == n || lo >= n) return;   // every entry taken, or nothing here
+  for (int i = threadIdx.x; i < kRtBins; i += 256) lh[i] = 0u;
   __syncthreads();
-  tk_scan(esum, sh, &E);
+  rt_hist_range<0>(scores, ld, r, lo, min(n, lo + kRtChunk), 0u, lh);
   __syncthreads();
-  const uint32_t sel_before = G + min(E, want);
-  const uint32_t quota = E >= want ? 0u : want - E;   // keys equal to t* this chunk may take
-  uint32_t k[16];
-  rt_load(scores, ld, r, lo, n, k);
-  uint32_t eq_run = 0, sel_run = sel_before;
+  for (int i = threadIdx.x; i < kRtBins; i += 256)
+    if (lh[i]) atomicAdd(&hist0[(int64_t)r * kRtBins + i], lh[i]);
+}
+
+// One workgroup selects the kk largest keys of row r (n entries) straight
+// from the score row: three histogram levels to the exact kk-th largest key
+// t*, then every key above t* and the lowest-position keys equal to t*, in
+// ascending position order.
+__device__ void rt_row_select(const float *scores, int64_t ld, int r, int n, int kk, int32_t *io, float *so,
+                              uint32_t *lh, uint32_t *sh) {
+  RtThr t{0u, 0u, (uint32_t)kk};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {   // position order: q, then thread, then e
-    uint32_t ne = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ne += k[4 * q + e] == tstar ? 1u : 0u;
-    uint32_t tot;
-    uint32_t er = eq_run + tk_scan(ne, sh, &tot);
-    eq_run += tot;
+  for (int L = 0; L < 3; ++L) {
+    for (int i = threadIdx.x; i < kRtBins; i += 256) lh[i] = 0u;
     __syncthreads();
-    bool pick[4];
-    uint32_t ns = 0;
+    if (L == 0) rt_hist_range<0>(scores, ld, r, 0, n, 0u, lh);
+    else if (L == 1) rt_hist_range<1>(scores, ld, r, 0, n, t.prefix, lh);
+    else rt_hist_range<2>(scores, ld, r, 0, n, t.prefix, lh);
+    __syncthreads();
+    t = rt_next(lh, L == 2 ? 1024 : kRtBins, L == 2 ? 10 : 11, t, sh);
+  }
+  const uint32_t tstar = t.prefix, quota = t.want;
+  uint32_t eq_run = 0, sel_run = 0;
+  for (int base = 0; base < n; base += kRtChunk) {
+    uint32_t k[16];
+    rt_load(scores, ld, r, base, n, k);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = k[4 * q + e];
-      bool p = key > tstar;
-      if (key == tstar) {
-        p = er < quota;
-        ++er;
+    for (int q = 0; q < 4; ++q) {   // position order: q, then thread, then e
+      uint32_t ne = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ne += k[4 * q + e] == tstar ? 1u : 0u;
+      uint32_t tot;
+      uint32_t er = eq_run + tk_scan(ne, sh, &tot);
+      eq_run += tot;
+      __syncthreads();
+      bool pick[4];
+      uint32_t ns = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = k[4 * q + e];
+        bool p = key > tstar;
+        if (key == tstar) {
+          p = er < quota;
+          ++er;
+        }
+        pick[e] = p;
+        ns += p ? 1u : 0u;
       }
-      pick[e] = p;
-      ns += p ? 1u : 0u;
-    }
-    uint32_t slot = sel_run + tk_scan(ns, sh, &tot);
-    sel_run += tot;
-    __syncthreads();
+      uint32_t slot = sel_run + tk_scan(ns, sh, &tot);
+      sel_run += tot;
+      __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (!pick[e]) continue;
-      const int pos = lo + 4 * ((int)threadIdx.x + 256 * q) + e;
-      io[slot] = pos;
-      if (so) so[slot] = keyf(k[4 * q + e]);
+      for (int e = 0; e < 4; ++e) {
+        if (!pick[e]) continue;
+        io[slot] = base + 4 * ((int)threadIdx.x + 256 * q) + e;
+        if (so) so[slot] = keyf(k[4 * q + e]);
+        ++slot;
+      }
+    }
+  }
+}
+
+// The kk largest of the row's M candidates (candidate i in position order is
+// slot c*cc + (i - off[c]) of the chunk c with off[c] <= i < off[c + 1]).
+// Every candidate above the level-0 bin b0 is taken (`above` of them); the
+// keys of bin b0 are refined by two more histogram levels (the next 11 and
+// the last 10 key bits) to the exact kk-th largest key t*; then the keys above
+// t* and the first `want` keys equal to t* are written in position order.
+// Thread t holds the contiguous run of candidates [t*P, t*P + P) (P >= M/256):
+// each one's chunk comes from a branch-free search of the offsets in LDS, so
+// all of its key and position loads are issued together.
+template <int P>
+__device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, const uint32_t *off, int nch, int cc, int M,
+                                int kk, uint32_t b0, uint32_t above0, uint32_t *lh, uint32_t *sh, int32_t *io,
+                                float *so) {
+  const int i0 = (int)threadIdx.x * P;
+  uint32_t k[P];
+  int32_t pos[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int i = i0 + j;
+    int a = 0;
+#pragma unroll
+    for (int step = kCandMaxChunks / 2; step > 0; step >>= 1)
+      a = (a + step < nch && (int)off[a + step] <= i) ? a + step : a;
+    const int sl = a * cc + (i - (int)off[a]);
+    k[j] = i < M ? rk[sl] : 0u;
+    pos[j] = i < M ? rp[sl] : 0;
+  }
+  // level 1: the next 11 bits of the keys in bin b0
+  RtThr t{b0, above0, (uint32_t)kk - above0};
+  for (int i = threadIdx.x; i < kRtBins; i += 256) lh[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (k[j] && (k[j] >> 21) == b0) atomicAdd(&lh[(k[j] >> 10) & 2047u], 1u);
+  __syncthreads();
+  t = rt_next(lh, kRtBins, 11, t, sh);
+  // level 2: the last 10 bits of the keys under that 22-bit prefix
+  for (int i = threadIdx.x; i < 1024; i += 256) lh[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (k[j] && (k[j] >> 10) == t.prefix) atomicAdd(&lh[k[j] & 1023u], 1u);
+  __syncthreads();
+  t = rt_next(lh, 1024, 10, t, sh);
+  const uint32_t tstar = t.prefix, quota = t.want;
+  // ordered emission: equal keys ranked in position order, then output slots
+  uint32_t ne = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) ne += k[j] == tstar ? 1u : 0u;
+  uint32_t tot;
+  uint32_t er = tk_scan(ne, sh, &tot);
+  __syncthreads();
+  uint32_t ns = 0;
+  uint64_t pick = 0ull;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    bool p = k[j] > tstar;
+    if (k[j] == tstar) {
+      p = er < quota;
+      ++er;
+    }
+    pick |= p ? 1ull << j : 0ull;
+    ns += p ? 1u : 0u;
+  }
+  uint32_t slot = tk_scan(ns, sh, &tot);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if ((pick >> j) & 1ull) {
+      io[slot] = pos[j];
+      if (so) so[slot] = keyf(k[j]);
       ++slot;
     }
+}
+
+// The picks of long row r from its candidates (or from the whole row when a
+// chunk's candidates overflowed), and the -1 tail.  Block-wide.
+struct RtFinalLds {
+  uint32_t soff[kCandMaxChunks + 1];
+  uint32_t lh[kRtBins];
+  uint32_t sh[8];
+  int over;
+};
+__device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t ld, int topk, int nch, int cc,
+                             const uint32_t *ckey, const int32_t *cpos, const uint32_t *cr, int32_t *idx_out,
+                             float *score_out, RtFinalLds &F) {
+  int32_t *io = idx_out + (int64_t)r * topk;
+  float *so = score_out ? score_out + (int64_t)r * topk : nullptr;
+  if (kk == n) {   // everything visible is taken, in order
+    for (int j = threadIdx.x; j < n; j += 256) {
+      io[j] = j;
+      if (so) so[j] = scores[(int64_t)r * ld + j];
+    }
+  } else {
+    // chunk counts -> exclusive offsets (wave 0), overflow flag
+    if (threadIdx.x < 64) {
+      const int c = threadIdx.x;
+      const uint32_t v = c < nch ? cr[c] : 0u;
+      uint32_t inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(inc, o, 64);
+        if (c >= o) inc += t;
+      }
+      F.soff[c] = inc - v;
+      if (c == 63) F.soff[kCandMaxChunks] = inc;
+      const bool over = __ballot(v > (uint32_t)cc) != 0ull;
+      if (c == 0) F.over = over ? 1 : 0;
+    }
+    __syncthreads();
+    const int M = (int)F.soff[kCandMaxChunks];
+    const uint32_t *rk = ckey + (int64_t)r * kCandSlots;
+    const int32_t *rp = cpos + (int64_t)r * kCandSlots;
+    const uint32_t b0 = cr[kCandMaxChunks], ab = cr[kCandMaxChunks + 1];
+    // more than 8192 candidates (heavy ties at the edge): the whole-row select
+    if (F.over || M > 256 * 32) rt_row_select(scores, ld, r, n, kk, io, so, F.lh, F.sh);
+    else if (M <= 256 * 8) rt_cands_select<8>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
+    else if (M <= 256 * 16) rt_cands_select<16>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
+    else rt_cands_select<32>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
   }
+  for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
+    io[j] = -1;
+    if (so) so[j] = -INFINITY;
+  }
+}
+
+// grid (T, nch), 256 threads: chunk c = positions [c*chunk, (c+1)*chunk) of
+// row r.  Candidates (keys in the level-0 bins from b0 up) go to slots
+// [c*cc, c*cc + cc) of the row's kCandSlots, in position order; the chunk's
+// true candidate count goes to ccnt[r, c], and chunk 0 records b0 and the
+// count of keys in the bins above it.
+__global__ __launch_bounds__(256) void k_rt_cand(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                 const int32_t *__restrict__ count, int m,
+                                                 const float *__restrict__ scores, int64_t ld, int topk,
+                                                 const uint32_t *__restrict__ hist0, int chunk, int cc,
+                                                 uint32_t *__restrict__ ckey, int32_t *__restrict__ cpos,
+                                                 uint32_t *__restrict__ ccnt) {
+  __shared__ uint32_t sh[8];
+  const int r = blockIdx.x, c = blockIdx.y, nch = gridDim.y;
+  const int n = n_visible(tok[r], m, count[seq[r]]);
+  const int kk = min(topk, n);
+  const int lo = c * chunk, hi = min(n, lo + chunk);
+  uint32_t total = 0, kmin_bin = 0, kmin_above = 0;
+  if (kk < n && lo < n) {
+    uint32_t k[16];
+    rt_load(scores, ld, r, lo, hi, k);   // in flight during the histogram search
+    uint32_t above;
+    const int b0 = rt_find(hist0 + (int64_t)r * kRtBins, kRtBins, (uint32_t)kk, &above, sh);
+    kmin_bin = (uint32_t)b0;
+    kmin_above = above;
+    const uint32_t kmin = (uint32_t)b0 << 21;
+    uint32_t *ok = ckey + (int64_t)r * kCandSlots + (int64_t)c * cc;
+    int32_t *op = cpos + (int64_t)r * kCandSlots + (int64_t)c * cc;
+    for (int base = lo; base < hi; base += kRtChunk) {
+      if (base != lo) rt_load(scores, ld, r, base, hi, k);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {   // position order: q, then thread, then e
+        uint32_t ne = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ne += k[4 * q + e] >= kmin ? 1u : 0u;
+        uint32_t tot;
+        uint32_t slot = total + tk_scan(ne, sh, &tot);
+        total += tot;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (k[4 * q + e] < kmin) continue;
+          if (slot < (uint32_t)cc) {
+            ok[slot] = k[4 * q + e];
+            op[slot] = base + 4 * ((int)threadIdx.x + 256 * q) + e;
+          }
+          ++slot;
+        }
+      }
+    }
+  }
+  uint32_t *cr = ccnt + (int64_t)r * kCandRow;
+  if (threadIdx.x == 0) {
+    cr[c] = total;
+    if (c == 0 && kk < n) {
+      cr[kCandMaxChunks] = kmin_bin;
+      cr[kCandMaxChunks + 1] = kmin_above;
+    }
+  }
+}
+
+// grid (T), 256 threads: the picks of each long row from its candidates
+__global__ __launch_bounds__(256) void k_rt_final(const int32_t *__restrict__ seq, const int32_t *__restrict__ tok,
+                                                  const int32_t *__restrict__ count, int m,
+                                                  const float *__restrict__ scores, int64_t ld, int topk, int nch,
+                                                  int cc, const uint32_t *__restrict__ ckey,
+                                                  const int32_t *__restrict__ cpos, const uint32_t *__restrict__ ccnt,
+                                                  int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
+  __shared__ RtFinalLds F;
+  const int r = gridDim.x - 1 - blockIdx.x;
+  const int n = n_visible(tok[r], m, count[seq[r]]);
+  rt_final_row(r, n, min(topk, n), scores, ld, topk, nch, cc, ckey, cpos, ccnt + (int64_t)r * kCandRow, idx_out,
+               score_out, F);
 }
 
 // Scratch memory of dsv4_index_topk_noalloc (the score rows, histograms,
@@ -881,13 +1043,15 @@ int index_topk_scratch(void **ptr) {
 }
 
 // Top-k plan: rows of at most 16384 entries are selected by one workgroup
-// each (k_topk_chunk, KPT keys per thread); longer rows by the radix-threshold
-// passes over chunks of kRtChunk entries.  Workspace: the score rows, then
-// (long rows) the histograms, the per-chunk counts and the thresholds.
+// each (k_topk_chunk, KPT keys per thread); longer rows by the candidate
+// path (level-0 histogram, k_rt_cand over at most kCandMaxChunks chunks of
+// `chunk` entries with cc candidate slots each, then k_rt_final).  Workspace: the
+// score rows, then (long rows) the histograms, the per-chunk candidate counts,
+// the candidate keys and their positions.
 struct TopkPlan {
   bool radix;
-  int kpt, n_chunks;
-  size_t scores_bytes, hist_bytes, cnt_bytes, thr_bytes;
+  int kpt, nch, chunk, cc;
+  size_t scores_bytes, hist_bytes, cnt_bytes, cand_bytes;
 };
 
 static int tk_kpt(int64_t n) {
@@ -903,12 +1067,17 @@ static TopkPlan plan_topk(int64_t n_rows, int64_t stride, int topk) {
   const int64_t st = stride > 0 ? stride : 1;
   p.radix = st > 16384;
   p.kpt = tk_kpt(st);
-  p.n_chunks = p.radix ? (int)((st + kRtChunk - 1) / kRtChunk) : 1;
   p.scores_bytes = align256((size_t)n_rows * (size_t)st * 4);
   if (p.radix) {
-    p.hist_bytes = align256((size_t)n_rows * sizeof(RtHist));
-    p.cnt_bytes = align256((size_t)n_rows * p.n_chunks * 8);
-    p.thr_bytes = align256((size_t)n_rows * 8);
+    int64_t nch = std::min<int64_t>(kCandMaxChunks, (st + kRtChunk - 1) / kRtChunk);
+    const int64_t chunk = ((st + nch - 1) / nch + kRtChunk - 1) / kRtChunk * kRtChunk;
+    nch = (st + chunk - 1) / chunk;
+    p.nch = (int)nch;
+    p.chunk = (int)chunk;
+    p.cc = kCandSlots / p.nch;
+    p.hist_bytes = align256((size_t)n_rows * kRtBins * 4);
+    p.cnt_bytes = align256((size_t)n_rows * kCandRow * 4);
+    p.cand_bytes = align256((size_t)n_rows * kCandSlots * 4);
   }
   (void)topk;
   return p;
@@ -916,7 +1085,7 @@ static TopkPlan plan_topk(int64_t n_rows, int64_t stride, int topk) {
 
 size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk) {
   const TopkPlan p = plan_topk(n_rows, stride, topk);
-  return p.scores_bytes + p.hist_bytes + p.cnt_bytes + p.thr_bytes + 256;
+  return p.scores_bytes + p.hist_bytes + p.cnt_bytes + 2 * p.cand_bytes + 256;
 }
 
 int index_topk_supported(int64_t stride, int topk) {
@@ -949,14 +1118,20 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
   if (T == 0) return DSV4_OK;
   const TopkPlan p = plan_topk(T, kp->seq_stride, topk);
   float *scores = (float *)ws;
-  RtHist *hist = p.radix ? (RtHist *)((char *)ws + p.scores_bytes) : nullptr;
-  const int hwords = (int)(sizeof(RtHist) / 4);
-  bool hist_clear = false;   // the scoring kernel clears the histograms
+  uint32_t *hist0 = p.radix ? (uint32_t *)((char *)ws + p.scores_bytes) : nullptr;
+  uint32_t *ccnt = p.radix ? (uint32_t *)((char *)hist0 + p.hist_bytes) : nullptr;
+  uint32_t *ckey = p.radix ? (uint32_t *)((char *)ccnt + p.cnt_bytes) : nullptr;
+  int32_t *cpos = p.radix ? (int32_t *)((char *)ckey + p.cand_bytes) : nullptr;
+  if (p.radix) {   // the level-0 histograms start at zero (a kernel, so graphs may capture it)
+    const int64_t hw = (int64_t)T * kRtBins;
+    hipLaunchKernelGGL(k_rt_zero, dim3((unsigned)((hw + 255) / 256)), dim3(256), 0, st, hist0, hw);
+  }
+  bool hist_built = false;   // the decode scoring kernel builds the level-0 histograms
   IdxQ Q{q->seq, q->tok, qv, qscale, w, H, Di};
   IdxK K{kp->data, kp->blk_scale, kp->count, kp->seq_stride, m};
   const int64_t ld = kp->seq_stride;
   // scoring kernels with one workgroup per (query row, entry chunk)
-  typedef void (*ScoreK)(IdxQ, IdxK, float, uint32_t *, int, float *, int64_t);
+  typedef void (*ScoreK)(IdxQ, IdxK, float, uint32_t *, float *, int64_t);
   ScoreK sk = nullptr;
   int eb = 1;   // entries per wave iteration / 16
   if (q_dtype == DSV4_MXFP4) {
@@ -996,9 +1171,8 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
     const int64_t blocks = (kp->seq_stride + unit - 1) / unit;
     const int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, resident_wgs((const void *)sk, 256) / T),
                                               std::max<int64_t>(1, blocks));
-    hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, (uint32_t *)hist, hwords,
-                       scores, ld);
-    hist_clear = hist != nullptr;
+    hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, hist0, scores, ld);
+    hist_built = hist0 != nullptr;
   } else {
     constexpr int QPW = 1;   // queries per wave (4 per workgroup share each key tile)
     dim3 g8((T + 4 * QPW - 1) / (4 * QPW));
@@ -1025,21 +1199,15 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
 #undef DSV4_TK1
     return check_launch("k_topk_chunk");
   }
-  uint32_t *cnt = (uint32_t *)((char *)hist + p.hist_bytes);
-  uint32_t *thr = (uint32_t *)((char *)cnt + p.cnt_bytes);
-  if (!hist_clear) {
-    const int64_t hw = (int64_t)T * hwords;
-    hipLaunchKernelGGL(k_rt_zero, dim3((unsigned)((hw + 255) / 256)), dim3(256), 0, st, (uint32_t *)hist, hw);
+  if (!hist_built) {
+    const dim3 g((unsigned)T, (unsigned)((kp->seq_stride + kRtChunk - 1) / kRtChunk));
+    hipLaunchKernelGGL(k_rt_hist0, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist0);
   }
-  const dim3 g((unsigned)T, (unsigned)p.n_chunks);
-  hipLaunchKernelGGL(k_rt_hist<0>, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist);
-  hipLaunchKernelGGL(k_rt_hist<1>, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist);
-  hipLaunchKernelGGL(k_rt_hist<2>, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist);
-  hipLaunchKernelGGL(k_rt_count, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, hist, cnt,
-                     thr);
-  hipLaunchKernelGGL(k_rt_emit, g, dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld, topk, cnt, thr,
-                     idx_out, score_out);
-  return check_launch("k_rt_emit");
+  hipLaunchKernelGGL(k_rt_cand, dim3((unsigned)T, (unsigned)p.nch), dim3(256), 0, st, q->seq, q->tok, kp->count, m,
+                     scores, ld, topk, hist0, p.chunk, p.cc, ckey, cpos, ccnt);
+  hipLaunchKernelGGL(k_rt_final, dim3((unsigned)T), dim3(256), 0, st, q->seq, q->tok, kp->count, m, scores, ld,
+                     topk, p.nch, p.cc, ckey, cpos, ccnt, idx_out, score_out);
+  return check_launch("k_rt_final");
 }
 
 }  // namespace dsv4host
