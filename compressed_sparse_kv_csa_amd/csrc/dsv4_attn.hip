@@ -482,6 +482,14 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
+// a pointer every lane holds the same value of, in scalar registers
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T *)(((uint64_t)hi << 32) | lo);
+}
+
 constexpr float kRefSlack = 15.f;   // log2 units: P <= 2^15 stays finite in fp16
 
 // FP8 rows: 448 E4M3 channels, then 64 bf16 channels
@@ -595,10 +603,10 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // the epilogue does not wait for argument reloads
   int e_ns = __builtin_amdgcn_readfirstlane(A.nsplit), e_odt = __builtin_amdgcn_readfirstlane(A.out_dtype);
   int e_H = __builtin_amdgcn_readfirstlane(A.H), e_sk = __builtin_amdgcn_readfirstlane(A.sinks != nullptr ? 1 : 0);
-  uint16_t *orow = (uint16_t *)A.out + (int64_t)r * A.H * D;
-  uint16_t *e_po = A.part_o;
-  float *e_pml = A.part_ml;
-  asm volatile("" : "+s"(orow), "+s"(e_ns), "+s"(e_odt), "+s"(e_H), "+s"(e_sk), "+s"(e_po), "+s"(e_pml));
+  uint16_t *orow = uniform_ptr((uint16_t *)A.out + (int64_t)r * A.H * D);
+  uint16_t *e_po = uniform_ptr(A.part_o);
+  float *e_pml = uniform_ptr(A.part_ml);
+  asm volatile("" : "+s"(e_ns), "+s"(e_odt), "+s"(e_H), "+s"(e_sk));
   const bool stage = DSPV && !FP8 && e_ns == 1 && e_odt != DSV4_F32;
 
   // FP8: the raw 32-row tile is 18 KB of consecutive 1 KB DMA chunks (wave w:
@@ -609,18 +617,25 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // [1024q + 16l, +16) of the tile, part of row (1024q + 16l) / 576; the row
   // ids are read from LDS up front, then each DMA is one instruction
   constexpr int CPW = (kF8Chunks + NW - 1) / NW;   // chunks per wave
+  // (the lane index is made opaque here so that the per-lane offsets are
+  // formed at each use rather than hoisted out of the tile loop, where they
+  // would hold registers for the whole loop)
   auto raw_ids = [&](int tile, int (&rk)[CPW], int &rid) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int k = 0; k < CPW; ++k) {
       const int q = wv + NW * k;
-      rk[k] = q < kF8Chunks ? row_id(32 * tile + (1024 * q + 16 * lane) / kF8Row) : 0x7fffffff;
+      rk[k] = q < kF8Chunks ? row_id(32 * tile + (1024 * q + 16 * ln) / kF8Row) : 0x7fffffff;
     }
-    rid = (wv == NW - 1 && lane < 32) ? row_id(32 * tile + lane) : 0x7fffffff;
+    rid = (wv == NW - 1 && ln < 32) ? row_id(32 * tile + ln) : 0x7fffffff;
   };
   auto raw_chunk = [&](int k, int rkk, uint8_t *R) {
     const int q = wv + NW * k;
     if (q < kF8Chunks && rkk != 0x7fffffff) {
-      const int o = 1024 * q + 16 * lane, row = o / kF8Row;
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int o = 1024 * q + 16 * ln, row = o / kF8Row;
       const uint8_t *rp = rkk >= 0 ? wbase + (int64_t)rkk * RB : pbase + (int64_t)(-1 - rkk) * RB;
       __builtin_amdgcn_global_load_lds(rp + (o - row * kF8Row), (lds_void *)(R + 1024 * q), 16, 0, 0);
     }
@@ -638,55 +653,42 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
     for (int k = 0; k < CPW; ++k) raw_chunk(k, rk[k], R);
     raw_scale(rid, Sc);
   };
-  // FP8: decode raw tile buf into the fp16 tile T
+  // FP8: decode raw tile buf into the fp16 tile T.  Thread t takes row t/8 (of
+  // 32) and its 8-channel columns t%8 + 8i: seven of E4M3 codes, one of bf16
+  // rope channels, so every LDS address is a per-thread base plus a constant.
   auto convert = [&](const uint8_t *R, const float *sc, uint16_t *T) {
-    constexpr int NI = 32 * (kF8Nope / 8), NU = (NI + NT - 1) / NT;   // items of 8 E4M3 codes
-    constexpr int NR = (32 * 8 + NT - 1) / NT;                         // items of 8 bf16 rope channels
-    constexpr int KB = 4;                                              // items read ahead per batch
+    static_assert(kF8Nope == 56 * 8, "7 E4M3 columns + 1 rope column per thread");
+    int t8 = tid;
+    asm volatile("" : "+v"(t8));   // formed at each use, not held across the tile loop
+    const int j8 = t8 & 7;
 #pragma unroll
-    for (int k0 = 0; k0 < NU; k0 += KB) {
-      u32x2 v[KB];
-      float sv[KB];
+    for (int row = t8 >> 3; row < 32; row += NT / 8) {
+      const uint8_t *rr = R + row * kF8Row + 8 * j8;
+      uint16_t *tr = T + row * KP + 8 * j8;
+      // s = m 2^e: the conversion applies 2^e exactly (E4M3 values are exact in
+      // fp16), one fp16 multiply applies m in [1, 2)
+      const float s = sc[row];
+      const _Float16 m = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+      const h2 mm = h2{m, m};
+      u32x2 v[7];
 #pragma unroll
-      for (int k = 0; k < KB; ++k) {   // the batch's LDS reads first
-        const int u = tid + NT * (k0 + k);
-        if (k0 + k < NU && u < NI) {
-          const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
-          v[k] = *reinterpret_cast<const u32x2 *>(R + row * kF8Row + 8 * c8);
-          sv[k] = sc[row];
-        }
+      for (int i = 0; i < 7; ++i) v[i] = *reinterpret_cast<const u32x2 *>(rr + 64 * i);
+      const u32x4 rv = *reinterpret_cast<const u32x4 *>(R + row * kF8Row + kF8Nope + 16 * j8);
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i].x, s, false) * mm;
+        const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i].x, s, true) * mm;
+        const h2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i].y, s, false) * mm;
+        const h2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[i].y, s, true) * mm;
+        uint32_t w[4];
+        __builtin_memcpy(&w[0], &a0, 4);
+        __builtin_memcpy(&w[1], &a1, 4);
+        __builtin_memcpy(&w[2], &a2, 4);
+        __builtin_memcpy(&w[3], &a3, 4);
+        *reinterpret_cast<u32x4 *>(tr + 64 * i) = u32x4{w[0], w[1], w[2], w[3]};
       }
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int u = tid + NT * (k0 + k);
-        if (k0 + k < NU && u < NI) {
-          const int row = u / (kF8Nope / 8), c8 = u - row * (kF8Nope / 8);
-          // s = m 2^e: the conversion applies 2^e exactly (E4M3 values are
-          // exact in fp16), one fp16 multiply applies m in [1, 2)
-          const float s = sv[k];
-          const _Float16 m = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
-          const h2 mm = h2{m, m};
-          const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].x, s, false) * mm;
-          const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].x, s, true) * mm;
-          const h2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].y, s, false) * mm;
-          const h2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[k].y, s, true) * mm;
-          uint32_t w[4];
-          __builtin_memcpy(&w[0], &a0, 4);
-          __builtin_memcpy(&w[1], &a1, 4);
-          __builtin_memcpy(&w[2], &a2, 4);
-          __builtin_memcpy(&w[3], &a3, 4);
-          *reinterpret_cast<u32x4 *>(T + row * KP + 8 * c8) = u32x4{w[0], w[1], w[2], w[3]};
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NR; ++k) {
-      const int u = tid + NT * k;
-      if (u < 32 * 8) {
-        const u32x4 rv = *reinterpret_cast<const u32x4 *>(R + (u >> 3) * kF8Row + kF8Nope + 16 * (u & 7));
-        *reinterpret_cast<u32x4 *>(T + (u >> 3) * KP + kF8Nope + 8 * (u & 7)) =
-            u32x4{bf16x2_to_f16x2(rv.x), bf16x2_to_f16x2(rv.y), bf16x2_to_f16x2(rv.z), bf16x2_to_f16x2(rv.w)};
-      }
+      *reinterpret_cast<u32x4 *>(T + row * KP + kF8Nope + 8 * j8) =
+          u32x4{bf16x2_to_f16x2(rv.x), bf16x2_to_f16x2(rv.y), bf16x2_to_f16x2(rv.z), bf16x2_to_f16x2(rv.w)};
     }
   };
 
