@@ -1055,6 +1055,473 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   }
 }
 
+// ---------------------------------------------------------------- FP8 rows, decode
+// k_attn_dec<NW, R64>: the decode form of the FP8-row path (one query row per
+// sequence, its row list split over several workgroups).  Same matrix-core
+// scheme as k_attn_f16's channel-split PV (64 heads as the MFMA N dimension,
+// S^T = K q~^T, every wave publishing its P^T fragment, O^T for all heads over
+// a D/NW channel share), with a setup and a tile pipeline made for short row
+// lists that live in HBM:
+//   * the query's picks, sinks and rope frequencies are loaded first and the
+//     query row after them, so the gathers wait for the picks only and the
+//     query row's conversion overlaps the first gathers;
+//   * no index compaction: a split keeps the picks of its own tiles, and a
+//     pick that is -1 or past the pool count is a masked row (its tile row is
+//     written as zeros, its probability is zero);
+//   * gathers into registers: thread t loads 72 bytes of tile row t/8 (seven
+//     8-byte E4M3 pieces, 16 bytes of bf16 rope channels) and the row scale,
+//     two tiles ahead, then decodes them into one of two fp16 tiles itself, so
+//     the raw rows never pass through LDS and no wave waits for another's
+//     loads; a gather past the split's last tile reads a row that exists, so
+//     every step issues the same loads and the waits stay exact;
+//   * two barriers per tile: P^T published, and the next fp16 tile written;
+//   * the splits of one query sit on one XCD (workgroups are dealt to the
+//     eight XCDs in turn), so its query row and picks come into one L2;
+//   * split partials (fp16, normalised by the split's own sum) and bf16
+//     outputs are staged in LDS, heads as rows, so each store writes a whole
+//     1 KB head row.
+// Decoding E4M3 with scale s = m 2^e: the conversion applies 2^e exactly
+// (E4M3 values are exact in fp16), one fp16 multiply applies m in [1, 2).
+template <int NW>
+struct DecRaw {
+  static constexpr int RPT = 256 / (NW * 64);   // tile rows a thread gathers
+  u32x2 v[RPT][7];
+  u32x4 rv[RPT];
+  float s[RPT];
+  uint32_t ok;   // bit q: row q of this thread is valid
+};
+
+// read in place of absent sinks (never written; the value read is not used),
+// global memory like the sinks so that the read is a global load
+__device__ float kNoSinks[64];
+
+// bits 0, 8, ..., 56 of a wave ballot (lane 8k stands for row k of 8) as 8 bits
+__device__ __forceinline__ uint32_t row_bits8(uint64_t b) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m |= (uint32_t)((b >> (8 * k)) & 1u) << k;
+  return m;
+}
+
+template <int NW, bool R64>
+__global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
+  constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
+  constexpr int RB = kF8Row;
+  constexpr int DB = NDB / NW;               // 16-channel blocks per wave (wave w: w, w+NW, ...)
+  constexpr int RPT = DecRaw<NW>::RPT;       // tile rows per thread in a gather
+  constexpr int RSTEP = NT / 8;              // between a thread's rows
+  constexpr int TH = 32 * KP;                // halfs per fp16 tile
+  constexpr int SROW = 1040;                 // staged output row pitch (bytes)
+  static_assert(NW == 1 || NW == 2 || NW == 4, "channel-split PV");
+  static_assert(RPT * RSTEP == 32, "a gather covers the tile");
+  static_assert(2 * TH * 2 >= 64 * SROW, "output staging fits in the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t TT[2 * TH];   // two fp16 tiles
+  __shared__ uint32_t vmk[4][NW];   // valid rows of tile t, slot t % 4: one field per wave
+  __shared__ int ids[kMaxSel];      // this split's picks
+  __shared__ float rc[32], rs[32];
+  __shared__ float sk[64];
+  __shared__ int rflag[3];
+  __shared__ __attribute__((aligned(16))) uint16_t PB[NW * 64 * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  int L = (int)blockIdx.x;
+  if ((gridDim.x & 7u) == 0) L = (int)((blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3));
+  const int r = (A.T - 1) - L / A.nsplit;
+  const int split = L % A.nsplit;
+
+  // the picks (clamped reads, so the count of loads is fixed), the sinks and
+  // the rope frequencies first; the query row after them
+  constexpr int IPT = (kMaxSel + NT - 1) / NT;
+  int ipre[IPT];
+  if (A.csa && A.topk > 0) {
+    const int32_t *ix = A.idx + (int64_t)r * A.topk;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) ipre[k] = ix[min(tid + NT * k, A.topk - 1)];
+  }
+  const float sink = (A.sinks ? A.sinks : kNoSinks)[min(tid, A.H - 1)];   // one unconditional load
+  const double ifq = A.inv_freq[tid & 31];
+  f16x8 qb[NJ];
+  {
+    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + 16 * wv + c) * D + 8 * g;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) qb[j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
+  }
+  RowPlan P = row_plan(A, r);
+  const int R = R64 ? 64 : A.rope_dim;
+  const int nwin = P.nwin, csa = A.csa;
+  const int pcount = A.pool.data ? A.pool.count[P.b] : 0;
+  // nominal row list: window rows, then every pick slot (CSA) or the visible entries (HCA)
+  const int nrows = nwin + (csa ? A.topk : P.nsel);
+  const int ntiles = (nrows + 31) / 32;
+  const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
+  const int tile_lo = split * tps;
+  int tile_hi = min(ntiles, tile_lo + tps);
+  const int e_lo = max(0, 32 * tile_lo - nwin), e_hi = csa ? min(A.topk, 32 * tile_hi - nwin) : 0;
+  if (csa) {
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const int e = tid + NT * k;
+      if (k * NT < A.topk && e >= e_lo && e < e_hi) ids[e - e_lo] = ipre[k];
+    }
+  }
+  const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * RB : nullptr;
+  const uint8_t *wbase = A.win.data ? A.win.data + (int64_t)P.b * A.win.stride * RB : nullptr;
+  const float *psc = A.pool.data ? A.pool.rscale + (int64_t)P.b * A.pool.stride : nullptr;
+  const float *wsc = A.win.data ? A.win.rscale + (int64_t)P.b * A.win.stride : nullptr;
+  // every invalid position reads a row that exists (its values are replaced by
+  // zeros): the first window row, else pool entry 0; with neither there is no row
+  if (!(nwin > 0 || pcount > 0)) tile_hi = tile_lo;
+  if (tid < R / 2) rope_cs_f((double)P.p, ifq, 1.f, &rc[tid], &rs[tid]);
+  if (tid < A.H) sk[tid] = A.sinks ? sink * kLog2e : -INFINITY;
+  if (tid < 3) rflag[tid] = 0;
+  lds_barrier();   // picks, angles and sinks visible; the query row may still be in flight
+
+  // row i of the list: its address and scale address, and whether it is valid
+  auto row_src = [&](int i, const uint8_t **rp, const float **sp) -> bool {
+    bool ok = i >= 0 && i < nrows;
+    int wrow = -1, pent = -1;
+    if (ok && i < nwin) wrow = win_slot(A, P, i);
+    else if (ok) {
+      pent = csa ? ids[i - nwin - e_lo] : i - nwin;
+      ok = pent >= 0 && pent < pcount;
+    }
+    if (!ok) {   // the row every invalid position reads
+      wrow = nwin > 0 ? win_slot(A, P, 0) : -1;
+      pent = nwin > 0 ? -1 : 0;
+    }
+    *rp = wrow >= 0 ? wbase + (int64_t)wrow * RB : pbase + (int64_t)pent * RB;
+    *sp = wrow >= 0 ? wsc + wrow : psc + pent;
+    return ok;
+  };
+  // gather tile t (t < 0: no tile, every row reads the stand-in row) into
+  // registers; the rows' validity goes to this wave's field of vmk
+  const int j8 = tid & 7;
+  auto gather = [&](int t, DecRaw<NW> &Rw) {
+    uint32_t wm = 0;
+    Rw.ok = 0;
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      const int row = (tid >> 3) + q * RSTEP;
+      const uint8_t *rp = nullptr;
+      const float *sp = nullptr;
+      const bool ok = row_src(t >= 0 ? 32 * t + row : -1, &rp, &sp);
+      Rw.ok |= (uint32_t)ok << q;
+      const uint8_t *p8 = rp + 8 * j8;
+#pragma unroll
+      for (int i = 0; i < 7; ++i) Rw.v[q][i] = *reinterpret_cast<const u32x2 *>(p8 + 64 * i);
+      Rw.rv[q] = *reinterpret_cast<const u32x4 *>(rp + kF8Nope + 16 * j8);
+      Rw.s[q] = *sp;
+      wm |= row_bits8(__ballot(ok)) << (8 * wv + q * RSTEP);
+    }
+    if (t >= 0 && lane == 0) vmk[t & 3][wv] = wm;
+  };
+  auto tile_mask = [&](int t) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m |= vmk[t & 3][w];
+    return m;
+  };
+  // gathered registers -> fp16 tile Tb (invalid rows become zeros)
+  auto convert = [&](const DecRaw<NW> &Rw, uint16_t *Tb) {
+#pragma unroll
+    for (int q = 0; q < RPT; ++q) {
+      const int row = (tid >> 3) + q * RSTEP;
+      uint16_t *tr = Tb + row * KP + 8 * j8;
+      uint16_t *tq = Tb + row * KP + kF8Nope + 8 * j8;
+      // the row's loads have landed on every path through the branch below,
+      // so the compiler's waits stay exact (one tile of gathers in flight)
+#pragma unroll
+      for (int i = 0; i < 7; ++i) asm volatile("" ::"v"(Rw.v[q][i]));
+      asm volatile("" ::"v"(Rw.rv[q]), "v"(Rw.s[q]));
+      if (!((Rw.ok >> q) & 1u)) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) *reinterpret_cast<u32x4 *>(tr + 64 * i) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4 *>(tq) = u32x4{0u, 0u, 0u, 0u};
+        continue;
+      }
+      const float s = Rw.s[q];
+      const _Float16 m = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+      const h2 mm = h2{m, m};
+#pragma unroll
+      for (int i = 0; i < 7; ++i) {
+        const u32x2 v = Rw.v[q][i];
+        const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, s, false) * mm;
+        const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, s, true) * mm;
+        const h2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, s, false) * mm;
+        const h2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, s, true) * mm;
+        uint32_t w[4];
+        __builtin_memcpy(&w[0], &a0, 4);
+        __builtin_memcpy(&w[1], &a1, 4);
+        __builtin_memcpy(&w[2], &a2, 4);
+        __builtin_memcpy(&w[3], &a3, 4);
+        *reinterpret_cast<u32x4 *>(tr + 64 * i) = u32x4{w[0], w[1], w[2], w[3]};
+      }
+      const u32x4 rv = Rw.rv[q];
+      *reinterpret_cast<u32x4 *>(tq) =
+          u32x4{bf16x2_to_f16x2(rv.x), bf16x2_to_f16x2(rv.y), bf16x2_to_f16x2(rv.z), bf16x2_to_f16x2(rv.w)};
+    }
+  };
+
+  DecRaw<NW> R0, R1;
+  f32x4 acc_o[NW][DB];
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+  auto clear_acc = [&]() {
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc_o[w][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // everything up to the epilogue sits in one branch, so that the compiler's
+  // load waits see a single path: the q~ conversion waits for the query row
+  // only, with the first two gathers still in flight behind it
+  if (tile_lo < tile_hi) {
+  gather(tile_lo, R0);
+  gather(tile_lo + 1 < tile_hi ? tile_lo + 1 : -1, R1);
+  // q~ = RoPE(q) * sm_scale * log2(e) in fp16 (B operand: head 16 wv + c, dims 32j + 8g .. +8)
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int d0 = 32 * j + 8 * g;
+    u32x4 raw;
+    __builtin_memcpy(&raw, &qb[j], 16);
+    float x[8];
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16_to_f32((uint16_t)(wds[k] & 0xFFFF));
+      x[2 * k + 1] = bf16_to_f32((uint16_t)(wds[k] >> 16));
+    }
+    if (d0 >= D - R) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int pi = (d0 + 2 * k - (D - R)) >> 1;
+        const float cs = rc[pi], sn = rs[pi];
+        const float a = x[2 * k] * cs - x[2 * k + 1] * sn, bb = x[2 * k] * sn + x[2 * k + 1] * cs;
+        x[2 * k] = a;
+        x[2 * k + 1] = bb;
+      }
+    }
+    const u32x4 o = u32x4{pack_f16x2(x[0] * A.scale_log2, x[1] * A.scale_log2),
+                          pack_f16x2(x[2] * A.scale_log2, x[3] * A.scale_log2),
+                          pack_f16x2(x[4] * A.scale_log2, x[5] * A.scale_log2),
+                          pack_f16x2(x[6] * A.scale_log2, x[7] * A.scale_log2)};
+    __builtin_memcpy(&qb[j], &o, 16);
+  }
+  clear_acc();
+
+  // one tile on the matrix cores (fp16 tile Tb).  A logit far above the
+  // reference sets rflag[fl].
+  auto compute = [&](const uint16_t *Tb, int tile, int fl) {
+    const uint32_t mask = tile_mask(tile);
+    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      constexpr int QD = 3;
+      const uint16_t *k0 = Tb + c * KP + 8 * g;
+      const uint16_t *k1 = k0 + 16 * KP;
+      f16x8 r0[QD], r1[QD];
+#pragma unroll
+      for (int j = 0; j < QD; ++j) {
+        r0[j] = *reinterpret_cast<const f16x8 *>(k0 + 32 * j);
+        r1[j] = *reinterpret_cast<const f16x8 *>(k1 + 32 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const f16x8 a0 = r0[j % QD], a1 = r1[j % QD];
+        if (j + QD < NJ) {
+          r0[j % QD] = *reinterpret_cast<const f16x8 *>(k0 + 32 * (j + QD));
+          r1[j % QD] = *reinterpret_cast<const f16x8 *>(k1 + 32 * (j + QD));
+        }
+        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[j], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[j], s[1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (mask != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!((mask >> (16 * mb + 4 * g + i)) & 1u)) s[mb][i] = -INFINITY;
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[mb][i]);
+    mloc = rows_max(mloc);
+    m_seen = fmaxf(m_seen, mloc);
+    if (m_ref == -INFINITY) m_ref = mloc;   // first tile with a valid row
+    const bool over = mloc > m_ref + kRefSlack;
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[4 * mb + i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[mb][i] - m_ref);
+        psum += p[4 * mb + i];
+      }
+    l_run += psum;
+    const u32x4 pw = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
+                           pack_f16x2(p[6], p[7])};
+    *reinterpret_cast<u32x4 *>(PB + (wv * 64 + lane) * 8) = pw;
+    if (__ballot(over) && lane == 0) rflag[fl] = 1;
+    asm volatile("" : "+v"(l_run), "+v"(m_seen));
+    lds_barrier();   // P^T of every wave visible
+    const uint16_t *v0p = Tb + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * wv;
+    const uint16_t *v1p = v0p + 16 * KP;
+    f16x8 pf[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) pf[w] = *reinterpret_cast<const f16x8 *>(PB + (w * 64 + lane) * 8);
+    constexpr int VD = 4;
+    v4i16 vlo[VD], vhi[VD];
+#pragma unroll
+    for (int db = 0; db < VD; ++db) {
+      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * NW * db));
+      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * NW * db));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      f16x8 a;
+      __builtin_memcpy(&a, &vlo[db % VD], 8);
+      __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &vhi[db % VD], 8);
+      if (db + VD < DB) {
+        vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * NW * (db + VD)));
+        vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * NW * (db + VD)));
+      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        acc_o[w][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[w], acc_o[w][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // tile `tile` (in fp16 tile B, its raw registers free) on the matrix cores
+  // while the gather of tile+2 is in flight, then tile+1 decoded into the other
+  // fp16 tile.  Returns whether a logit overflowed the reference.  The gather
+  // and the decode run past the last tile too (the stand-in rows decode to
+  // zeros; only the matrix work is skipped): with no branch around a load or
+  // its use, the compiler's waits for the gathers stay one step deep.
+  auto step = [&](auto Bc, int tile, int it) -> bool {
+    constexpr int B = decltype(Bc)::value;
+    DecRaw<NW> &Rc = B ? R1 : R0;
+    DecRaw<NW> &Rn = B ? R0 : R1;
+    gather(tile + 2 < tile_hi ? tile + 2 : -1, Rc);
+    if (tile < tile_hi) compute(TT + B * TH, tile, it % 3);
+    if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
+    convert(Rn, TT + (1 - B) * TH);
+    lds_barrier();   // next fp16 tile written, this one and P^T free, flags visible
+    return rflag[it % 3] != 0;
+  };
+
+  // one pass over the split's tiles, its first two gathers issued; returns
+  // whether a logit far above the reference asks for another pass.  Tiles go
+  // in pairs (an odd count ends with a step that only gathers and decodes),
+  // so the loop has one exit point and every path back to its head has
+  // passed both steps' waits.
+  auto pass = [&]() __attribute__((always_inline)) -> bool {
+    convert(R0, TT);
+    lds_barrier();
+    for (int tile = tile_lo, it = 0;; tile += 2, it += 2) {
+      const bool o0 = step(std::integral_constant<int, 0>{}, tile, it);
+      const bool o1 = step(std::integral_constant<int, 1>{}, tile + 1, it + 1);
+      if (o0 || o1) return true;
+      if (tile + 2 >= tile_hi) return false;
+    }
+  };
+  // the first pass is a copy of its own, so its waits are not merged with
+  // the restart path's
+  if (pass()) {
+    do {   // restart with the reference raised to the largest logit seen
+      lds_barrier();
+      if (tid < 3) rflag[tid] = 0;
+      m_ref = m_seen;
+      lds_barrier();
+      l_run = 0.f;
+      clear_acc();
+      gather(tile_lo, R0);
+      gather(tile_lo + 1 < tile_hi ? tile_lo + 1 : -1, R1);
+    } while (pass());
+  }
+  } else {
+    clear_acc();
+  }
+
+  // the head-owning waves' (reference, sum) pairs through LDS
+  float *shml = reinterpret_cast<float *>(PB);
+  {
+    const float lr = rows_sum(l_run);
+    if (g == 0) {
+      shml[2 * (16 * wv + c)] = m_ref;
+      shml[2 * (16 * wv + c) + 1] = lr;
+    }
+    lds_barrier();
+  }
+  // MODE 0: split partial (fp16, staged), 1: fp32 output (direct), 2: bf16 output (staged)
+  auto finish = [&](auto Mc) {
+    constexpr int MODE = decltype(Mc)::value;
+    const int ns = A.nsplit;
+    const int dlo = 16 * wv;
+#pragma unroll
+    for (int hb = 0; hb < NW; ++hb) {
+      const int h = 16 * hb + c;
+      const float mr = shml[2 * h], lr = shml[2 * h + 1];
+      float f = 1.f, den = lr;
+      if (MODE != 0 && A.sinks) {   // the sink joins the denominator (exponents <= 0)
+        const float sg = sk[h];
+        const float M = lr > 0.f ? fmaxf(mr, sg) : sg;
+        f = lr > 0.f ? __builtin_amdgcn_exp2f(mr - M) : 0.f;
+        den = lr * f + __builtin_amdgcn_exp2f(sg - M);
+      }
+      // split partials: normalised by the split's own sum, so fp16 holds them
+      const float inv = den > 0.f ? f * __builtin_amdgcn_rcpf(den) : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        float o[4];
+        const int d0 = dlo + 16 * NW * db + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
+        if (MODE != 0 && dlo + 16 * NW * db >= D - R) {   // the output's rope slice turns back by -p
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int pi = (d0 + 2 * k - (D - R)) >> 1;
+            const float cs = rc[pi], sn = rs[pi];
+            const float a = o[2 * k] * cs + o[2 * k + 1] * sn, bb = -o[2 * k] * sn + o[2 * k + 1] * cs;
+            o[2 * k] = a;
+            o[2 * k + 1] = bb;
+          }
+        }
+        if (MODE == 1) {
+          const int64_t oe = ((int64_t)r * A.H + h) * D + d0;
+          *reinterpret_cast<f32x4 *>((float *)A.out + oe) = f32x4{o[0], o[1], o[2], o[3]};
+        } else {
+          const u32x2 v = MODE == 0 ? u32x2{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])}
+                                    : u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(TT) + h * SROW + 2 * d0) = v;
+        }
+      }
+      if (MODE == 0 && g == 0 && hb == wv) {
+        const int64_t pr = ((int64_t)r * ns + split) * A.H + h;
+        A.part_ml[2 * pr] = lr > 0.f ? mr : -INFINITY;
+        A.part_ml[2 * pr + 1] = lr;
+      }
+    }
+    if (MODE != 1) {
+      lds_barrier();
+      // wave w writes the rows of heads 16w .. 16w+15: lane l carries channels 8l .. 8l+7
+      uint16_t *orow = MODE == 0 ? A.part_o + (((int64_t)r * ns + split) * A.H) * D
+                                 : (uint16_t *)A.out + (int64_t)r * A.H * D;
+#pragma unroll 4
+      for (int k = 0; k < 16; ++k) {
+        const int h = 16 * wv + k;
+        *reinterpret_cast<u32x4 *>(orow + (int64_t)h * D + 8 * lane) =
+            *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(TT) + h * SROW + 16 * lane);
+      }
+    }
+  };
+  if (A.nsplit > 1) finish(std::integral_constant<int, 0>{});
+  else if (A.out_dtype == DSV4_F32) finish(std::integral_constant<int, 1>{});
+  else finish(std::integral_constant<int, 2>{});
+}
+
 // Merge split partials: grid (T * H), block D/2 threads (one channel pair each).
 // Every load that does not depend on another (the channel pair of every split,
 // the splits' (max, sum)) is issued first, so the merge costs about one memory
@@ -1359,6 +1826,21 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   // FP8 rows in the 448 E4M3 + 64 bf16 layout take the DMA-staged path too
   const bool fp8fast = fp8 && D == 512 && (W > 0 ? win->tail == 64 : true) && (pool ? pool->tail == 64 : true);
   dim3 grid((unsigned)((int64_t)T * ns));
+  if (fp8fast && (H == 16 || H == 32 || H == 64)) {
+#define DSV4_DECK(NW)                                                                           \
+  if (rope_dim == 64) hipLaunchKernelGGL((k_attn_dec<NW, true>), grid, dim3(NW * 64), 0, st, A); \
+  else hipLaunchKernelGGL((k_attn_dec<NW, false>), grid, dim3(NW * 64), 0, st, A);
+    switch (H) {
+    case 16: DSV4_DECK(1) break;
+    case 32: DSV4_DECK(2) break;
+    default: DSV4_DECK(4) break;
+    }
+#undef DSV4_DECK
+    int rc = check_launch("k_attn_dec");
+    if (rc || ns == 1) return rc;
+    launch_combine(A, T, H, st);
+    return check_launch("k_attn_combine");
+  }
   if (f16 || fp8fast) {
 #define DSV4_F16K(NW)                                                                                 \
   if (f16 && rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, NW, false, true>), grid, dim3(NW * 64), 0, st, A); \
