@@ -1056,24 +1056,34 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 }
 
 // ---------------------------------------------------------------- FP8 rows, decode
-// k_attn_dec<NW, R64>: the decode form of the FP8-row path (one query row per
-// sequence, its row list split over several workgroups).  Same matrix-core
-// scheme as k_attn_f16's channel-split PV (64 heads as the MFMA N dimension,
-// S^T = K q~^T, every wave publishing its P^T fragment, O^T for all heads over
-// a D/NW channel share), with a setup and a tile pipeline made for short row
-// lists that live in HBM:
+// k_attn_dec<NHB, R64>: the decode form of the FP8-row path (one query row per
+// sequence, its row list split over several workgroups), for H = 16 NHB heads.
+// Two waves per SIMD: 2 NHB waves, wave w = (head block w % NHB, row half
+// w / NHB).  Per 32-row tile:
+//   * S^T = K q~^T: each wave scores its 16 rows against its 16 heads (the K
+//     fragments it reads from LDS are half a tile, so the tile's LDS reads are
+//     spread over twice the waves);
+//   * the fixed-reference softmax: both row halves of a head share one
+//     reference, taken from the first tile with a valid row through one LDS
+//     exchange; each wave publishes its 16-row half of the head block's P^T
+//     fragment;
+//   * O^T = V^T P^T with the channels split over all waves (wave w owns the
+//     16-channel blocks w, w + 2 NHB, ...), every P^T fragment read by every
+//     wave, so each V^T fragment read from LDS feeds NHB products.
+// Around it, a pipeline made for short row lists that live in HBM:
 //   * the query's picks, sinks and rope frequencies are loaded first and the
-//     query row after them, so the gathers wait for the picks only and the
-//     query row's conversion overlaps the first gathers;
+//     query row after them, so the gathers wait for the picks only; the query
+//     row is converted to q~ once per workgroup (each thread 1/NT of it) and
+//     handed to the waves through LDS, overlapping the first gathers;
 //   * no index compaction: a split keeps the picks of its own tiles, and a
 //     pick that is -1 or past the pool count is a masked row (its tile row is
 //     written as zeros, its probability is zero);
-//   * gathers into registers: thread t loads 72 bytes of tile row t/8 (seven
-//     8-byte E4M3 pieces, 16 bytes of bf16 rope channels) and the row scale,
-//     two tiles ahead, then decodes them into one of two fp16 tiles itself, so
-//     the raw rows never pass through LDS and no wave waits for another's
-//     loads; a gather past the split's last tile reads a row that exists, so
-//     every step issues the same loads and the waits stay exact;
+//   * gathers into registers, two tiles ahead: sixteen threads per row, each
+//     loading 28 bytes of E4M3 codes, 8 bytes of bf16 rope channels and the
+//     row scale, then decoding them into one of two fp16 tiles itself, so the
+//     raw rows never pass through LDS and no wave waits on another's loads; a
+//     gather past the split's last tile reads a row that exists, so every step
+//     issues the same loads and the compiler's waits stay exact;
 //   * two barriers per tile: P^T published, and the next fp16 tile written;
 //   * the splits of one query sit on one XCD (workgroups are dealt to the
 //     eight XCDs in turn), so its query row and picks come into one L2;
@@ -1082,49 +1092,61 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 //     1 KB head row.
 // Decoding E4M3 with scale s = m 2^e: the conversion applies 2^e exactly
 // (E4M3 values are exact in fp16), one fp16 multiply applies m in [1, 2).
-template <int NW>
+template <int NHB>
 struct DecRaw {
-  static constexpr int RPT = 256 / (NW * 64);   // tile rows a thread gathers
-  u32x2 v[RPT][7];
-  u32x4 rv[RPT];
+  static constexpr int NT = 128 * NHB;
+  static constexpr int RPT = 512 / NT;   // tile rows a thread gathers (16 threads per row)
+  u32x4 a[RPT];                          // E4M3 bytes [28p, 28p + 16) of the row
+  u32x2 b[RPT];                          // [28p + 16, 28p + 24)
+  uint32_t c[RPT];                       // [28p + 24, 28p + 28)
+  u32x2 rp[RPT];                         // rope bytes [448 + 8p, +8): four bf16 channels
   float s[RPT];
-  uint32_t ok;   // bit q: row q of this thread is valid
+  uint32_t ok;                           // bit q: row q of this thread is valid
 };
 
 // read in place of absent sinks (never written; the value read is not used),
 // global memory like the sinks so that the read is a global load
 __device__ float kNoSinks[64];
 
-// bits 0, 8, ..., 56 of a wave ballot (lane 8k stands for row k of 8) as 8 bits
-__device__ __forceinline__ uint32_t row_bits8(uint64_t b) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) m |= (uint32_t)((b >> (8 * k)) & 1u) << k;
-  return m;
+// an unaligned global load of a T (the addresses here are 4-byte aligned)
+template <class T>
+__device__ __forceinline__ T ldg_u(const uint8_t *p) {
+  T v;
+  __builtin_memcpy(&v, p, sizeof(T));
+  return v;
 }
 
-template <int NW, bool R64>
-__global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
-  constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16, NT = NW * 64;
+// bits 0, 16, 32, 48 of a wave ballot (lane 16k stands for row k of 4) as 4 bits
+__device__ __forceinline__ uint32_t row_bits4(uint64_t b) {
+  return (uint32_t)(b & 1u) | (uint32_t)((b >> 15) & 2u) | (uint32_t)((b >> 30) & 4u) | (uint32_t)((b >> 45) & 8u);
+}
+
+template <int NHB, bool R64>
+__global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
+  constexpr int D = 512, KP = D + 16, NJ = D / 32, NDB = D / 16;
+  constexpr int NWV = 2 * NHB, NT = 64 * NWV;   // waves, threads
   constexpr int RB = kF8Row;
-  constexpr int DB = NDB / NW;               // 16-channel blocks per wave (wave w: w, w+NW, ...)
-  constexpr int RPT = DecRaw<NW>::RPT;       // tile rows per thread in a gather
-  constexpr int RSTEP = NT / 8;              // between a thread's rows
-  constexpr int TH = 32 * KP;                // halfs per fp16 tile
-  constexpr int SROW = 1040;                 // staged output row pitch (bytes)
-  static_assert(NW == 1 || NW == 2 || NW == 4, "channel-split PV");
+  constexpr int DBW = NDB / NWV;                // 16-channel blocks per wave in PV
+  constexpr int RPT = DecRaw<NHB>::RPT;
+  constexpr int RSTEP = NT / 16;                // between a thread's rows
+  constexpr int TH = 32 * KP;                   // halfs per fp16 tile
+  constexpr int QP = D + 8;                     // staged q~ row pitch (halfs)
+  constexpr int SROW = 1040;                    // staged output row pitch (bytes)
+  static_assert(NHB == 1 || NHB == 2 || NHB == 4, "16, 32 or 64 heads");
   static_assert(RPT * RSTEP == 32, "a gather covers the tile");
-  static_assert(2 * TH * 2 >= 64 * SROW, "output staging fits in the tile buffers");
+  static_assert(2 * TH * 2 >= 16 * NHB * SROW && 2 * TH >= 16 * NHB * QP, "staging fits in the tile buffers");
   __shared__ __attribute__((aligned(16))) uint16_t TT[2 * TH];   // two fp16 tiles
-  __shared__ uint32_t vmk[4][NW];   // valid rows of tile t, slot t % 4: one field per wave
-  __shared__ int ids[kMaxSel];      // this split's picks
+  __shared__ uint32_t vmk[4][NWV];   // valid rows of tile t, slot t % 4: one field per wave
+  __shared__ int ids[kMaxSel];       // this split's picks
   __shared__ float rc[32], rs[32];
   __shared__ float sk[64];
+  __shared__ float xm[2][64];        // per row half: a head's tile maximum, then its sum
   __shared__ int rflag[3];
-  __shared__ __attribute__((aligned(16))) uint16_t PB[NW * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t PB[NHB * 64 * 8];
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
+  const int hb = wv % NHB, rh = wv / NHB;   // this wave's head block and row half
   int L = (int)blockIdx.x;
   if ((gridDim.x & 7u) == 0) L = (int)((blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3));
   const int r = (A.T - 1) - L / A.nsplit;
@@ -1141,11 +1163,20 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
   }
   const float sink = (A.sinks ? A.sinks : kNoSinks)[min(tid, A.H - 1)];   // one unconditional load
   const double ifq = A.inv_freq[tid & 31];
-  f16x8 qb[NJ];
+  // the query row in 8-channel chunks: thread t holds plain chunks t + NT i
+  // (i < 7, numbered over the 56 non-rope chunks of each head) and the rope
+  // chunk t (head t / 8, channels 448 + 8 (t % 8)), so that every wave does
+  // the same work for every chunk it converts
+  static_assert(16 * NHB * (D / 8) == 8 * NT, "eight chunks per thread");
+  f16x8 qb[8];
   {
-    const uint16_t *qr = (const uint16_t *)A.q + ((int64_t)r * A.H + 16 * wv + c) * D + 8 * g;
+    const uint16_t *qr = (const uint16_t *)A.q + (int64_t)r * A.H * D;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) qb[j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
+    for (int i = 0; i < 7; ++i) {
+      const int k = tid + NT * i;
+      qb[i] = *reinterpret_cast<const f16x8 *>(qr + (k / 56) * D + 8 * (k % 56));
+    }
+    qb[7] = *reinterpret_cast<const f16x8 *>(qr + (tid >> 3) * D + (D - 64) + 8 * (tid & 7));
   }
   RowPlan P = row_plan(A, r);
   const int R = R64 ? 64 : A.rope_dim;
@@ -1158,11 +1189,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
   const int tile_lo = split * tps;
   int tile_hi = min(ntiles, tile_lo + tps);
   const int e_lo = max(0, 32 * tile_lo - nwin), e_hi = csa ? min(A.topk, 32 * tile_hi - nwin) : 0;
-  if (csa) {
+  if (csa && A.topk > 0) {
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int e = tid + NT * k;
-      if (k * NT < A.topk && e >= e_lo && e < e_hi) ids[e - e_lo] = ipre[k];
+      if (e >= e_lo && e < e_hi) ids[e - e_lo] = ipre[k];
     }
   }
   const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * RB : nullptr;
@@ -1196,81 +1227,74 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
   };
   // gather tile t (t < 0: no tile, every row reads the stand-in row) into
   // registers; the rows' validity goes to this wave's field of vmk
-  const int j8 = tid & 7;
-  auto gather = [&](int t, DecRaw<NW> &Rw) {
+  const int p16 = tid & 15;
+  auto gather = [&](int t, DecRaw<NHB> &Rw) {
     uint32_t wm = 0;
     Rw.ok = 0;
 #pragma unroll
     for (int q = 0; q < RPT; ++q) {
-      const int row = (tid >> 3) + q * RSTEP;
+      const int row = (tid >> 4) + q * RSTEP;
       const uint8_t *rp = nullptr;
       const float *sp = nullptr;
       const bool ok = row_src(t >= 0 ? 32 * t + row : -1, &rp, &sp);
       Rw.ok |= (uint32_t)ok << q;
-      const uint8_t *p8 = rp + 8 * j8;
-#pragma unroll
-      for (int i = 0; i < 7; ++i) Rw.v[q][i] = *reinterpret_cast<const u32x2 *>(p8 + 64 * i);
-      Rw.rv[q] = *reinterpret_cast<const u32x4 *>(rp + kF8Nope + 16 * j8);
+      const uint8_t *p8 = rp + 28 * p16;
+      Rw.a[q] = ldg_u<u32x4>(p8);
+      Rw.b[q] = ldg_u<u32x2>(p8 + 16);
+      Rw.c[q] = ldg_u<uint32_t>(p8 + 24);
+      Rw.rp[q] = ldg_u<u32x2>(rp + kF8Nope + 8 * p16);
       Rw.s[q] = *sp;
-      wm |= row_bits8(__ballot(ok)) << (8 * wv + q * RSTEP);
+      wm |= row_bits4(__ballot(ok)) << (4 * wv + q * RSTEP);
     }
     if (t >= 0 && lane == 0) vmk[t & 3][wv] = wm;
   };
   auto tile_mask = [&](int t) {
     uint32_t m = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) m |= vmk[t & 3][w];
+    for (int w = 0; w < NWV; ++w) m |= vmk[t & 3][w];
     return m;
   };
   // gathered registers -> fp16 tile Tb (invalid rows become zeros)
-  auto convert = [&](const DecRaw<NW> &Rw, uint16_t *Tb) {
+  auto convert = [&](const DecRaw<NHB> &Rw, uint16_t *Tb) {
 #pragma unroll
     for (int q = 0; q < RPT; ++q) {
-      const int row = (tid >> 3) + q * RSTEP;
-      uint16_t *tr = Tb + row * KP + 8 * j8;
-      uint16_t *tq = Tb + row * KP + kF8Nope + 8 * j8;
+      const int row = (tid >> 4) + q * RSTEP;
+      uint16_t *tr = Tb + row * KP + 28 * p16;
+      uint16_t *tq = Tb + row * KP + kF8Nope + 4 * p16;
       // the row's loads have landed on every path through the branch below,
       // so the compiler's waits stay exact (one tile of gathers in flight)
-#pragma unroll
-      for (int i = 0; i < 7; ++i) asm volatile("" ::"v"(Rw.v[q][i]));
-      asm volatile("" ::"v"(Rw.rv[q]), "v"(Rw.s[q]));
+      asm volatile("" ::"v"(Rw.a[q]), "v"(Rw.b[q]), "v"(Rw.c[q]), "v"(Rw.rp[q]), "v"(Rw.s[q]));
       if (!((Rw.ok >> q) & 1u)) {
 #pragma unroll
-        for (int i = 0; i < 7; ++i) *reinterpret_cast<u32x4 *>(tr + 64 * i) = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4 *>(tq) = u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < 7; ++i) *reinterpret_cast<u32x2 *>(tr + 4 * i) = u32x2{0u, 0u};
+        *reinterpret_cast<u32x2 *>(tq) = u32x2{0u, 0u};
         continue;
       }
       const float s = Rw.s[q];
       const _Float16 m = (_Float16)__uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
       const h2 mm = h2{m, m};
+      const uint32_t wd[7] = {Rw.a[q].x, Rw.a[q].y, Rw.a[q].z, Rw.a[q].w, Rw.b[q].x, Rw.b[q].y, Rw.c[q]};
 #pragma unroll
       for (int i = 0; i < 7; ++i) {
-        const u32x2 v = Rw.v[q][i];
-        const h2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, s, false) * mm;
-        const h2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.x, s, true) * mm;
-        const h2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, s, false) * mm;
-        const h2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v.y, s, true) * mm;
-        uint32_t w[4];
-        __builtin_memcpy(&w[0], &a0, 4);
-        __builtin_memcpy(&w[1], &a1, 4);
-        __builtin_memcpy(&w[2], &a2, 4);
-        __builtin_memcpy(&w[3], &a3, 4);
-        *reinterpret_cast<u32x4 *>(tr + 64 * i) = u32x4{w[0], w[1], w[2], w[3]};
+        const h2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd[i], s, false) * mm;
+        const h2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd[i], s, true) * mm;
+        uint32_t w0, w1;
+        __builtin_memcpy(&w0, &lo, 4);
+        __builtin_memcpy(&w1, &hi, 4);
+        *reinterpret_cast<u32x2 *>(tr + 4 * i) = u32x2{w0, w1};
       }
-      const u32x4 rv = Rw.rv[q];
-      *reinterpret_cast<u32x4 *>(tq) =
-          u32x4{bf16x2_to_f16x2(rv.x), bf16x2_to_f16x2(rv.y), bf16x2_to_f16x2(rv.z), bf16x2_to_f16x2(rv.w)};
+      *reinterpret_cast<u32x2 *>(tq) = u32x2{bf16x2_to_f16x2(Rw.rp[q].x), bf16x2_to_f16x2(Rw.rp[q].y)};
     }
   };
 
-  DecRaw<NW> R0, R1;
-  f32x4 acc_o[NW][DB];
+  DecRaw<NHB> R0, R1;
+  f32x4 acc_o[NHB][DBW];
   float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
   auto clear_acc = [&]() {
 #pragma unroll
-    for (int w = 0; w < NW; ++w)
+    for (int h = 0; h < NHB; ++h)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc_o[w][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < DBW; ++db) acc_o[h][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
   // everything up to the epilogue sits in one branch, so that the compiler's
   // load waits see a single path: the q~ conversion waits for the query row
@@ -1278,12 +1302,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
   if (tile_lo < tile_hi) {
   gather(tile_lo, R0);
   gather(tile_lo + 1 < tile_hi ? tile_lo + 1 : -1, R1);
-  // q~ = RoPE(q) * sm_scale * log2(e) in fp16 (B operand: head 16 wv + c, dims 32j + 8g .. +8)
+  // q~ = RoPE(q) * sm_scale * log2(e) in fp16, staged in the tile buffers as
+  // head rows; then each wave takes its B operand (head 16 hb + c, dims 32j + 8g .. +8)
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int d0 = 32 * j + 8 * g;
+  for (int i = 0; i < 8; ++i) {
+    const int k = tid + NT * i;
+    const int h = i < 7 ? k / 56 : tid >> 3, d0 = i < 7 ? 8 * (k % 56) : (D - 64) + 8 * (tid & 7);
     u32x4 raw;
-    __builtin_memcpy(&raw, &qb[j], 16);
+    __builtin_memcpy(&raw, &qb[i], 16);
     float x[8];
     const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -1291,7 +1317,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
       x[2 * k] = bf16_to_f32((uint16_t)(wds[k] & 0xFFFF));
       x[2 * k + 1] = bf16_to_f32((uint16_t)(wds[k] >> 16));
     }
-    if (d0 >= D - R) {
+    if (i == 7 && d0 >= D - R) {   // the rope chunk (R <= 64)
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int pi = (d0 + 2 * k - (D - R)) >> 1;
@@ -1301,96 +1327,90 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
         x[2 * k + 1] = bb;
       }
     }
-    const u32x4 o = u32x4{pack_f16x2(x[0] * A.scale_log2, x[1] * A.scale_log2),
-                          pack_f16x2(x[2] * A.scale_log2, x[3] * A.scale_log2),
-                          pack_f16x2(x[4] * A.scale_log2, x[5] * A.scale_log2),
-                          pack_f16x2(x[6] * A.scale_log2, x[7] * A.scale_log2)};
-    __builtin_memcpy(&qb[j], &o, 16);
+    *reinterpret_cast<u32x4 *>(TT + h * QP + d0) =
+        u32x4{pack_f16x2(x[0] * A.scale_log2, x[1] * A.scale_log2), pack_f16x2(x[2] * A.scale_log2, x[3] * A.scale_log2),
+              pack_f16x2(x[4] * A.scale_log2, x[5] * A.scale_log2), pack_f16x2(x[6] * A.scale_log2, x[7] * A.scale_log2)};
   }
+  lds_barrier();
+  f16x8 qf[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) qf[j] = *reinterpret_cast<const f16x8 *>(TT + (16 * hb + c) * QP + 32 * j + 8 * g);
+  lds_barrier();   // every wave holds its q~ fragments: the tile buffers are free
   clear_acc();
 
+  bool ref_set = false;   // the reference of this pass is taken (uniform over the workgroup)
   // one tile on the matrix cores (fp16 tile Tb).  A logit far above the
   // reference sets rflag[fl].
   auto compute = [&](const uint16_t *Tb, int tile, int fl) {
     const uint32_t mask = tile_mask(tile);
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;   // even and odd k-steps: two MFMA chains
     {
-      constexpr int QD = 3;
-      const uint16_t *k0 = Tb + c * KP + 8 * g;
-      const uint16_t *k1 = k0 + 16 * KP;
-      f16x8 r0[QD], r1[QD];
+      constexpr int QD = 4;
+      const uint16_t *k0 = Tb + (16 * rh + c) * KP + 8 * g;
+      f16x8 r0[QD];
 #pragma unroll
-      for (int j = 0; j < QD; ++j) {
-        r0[j] = *reinterpret_cast<const f16x8 *>(k0 + 32 * j);
-        r1[j] = *reinterpret_cast<const f16x8 *>(k1 + 32 * j);
-      }
+      for (int j = 0; j < QD; ++j) r0[j] = *reinterpret_cast<const f16x8 *>(k0 + 32 * j);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const f16x8 a0 = r0[j % QD], a1 = r1[j % QD];
-        if (j + QD < NJ) {
-          r0[j % QD] = *reinterpret_cast<const f16x8 *>(k0 + 32 * (j + QD));
-          r1[j % QD] = *reinterpret_cast<const f16x8 *>(k1 + 32 * (j + QD));
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qb[j], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qb[j], s[1], 0, 0, 0);
+        const f16x8 a0 = r0[j % QD];
+        if (j + QD < NJ) r0[j % QD] = *reinterpret_cast<const f16x8 *>(k0 + 32 * (j + QD));
+        if (j & 1) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[j], s1, 0, 0, 0);
+        else s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[j], s0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    float sv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = s0[i] + s1[i];
     if (mask != 0xFFFFFFFFu) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (!((mask >> (16 * mb + 4 * g + i)) & 1u)) s[mb][i] = -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (!((mask >> (16 * rh + 4 * g + i)) & 1u)) sv[i] = -INFINITY;
     }
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[mb][i]);
+    float mloc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mloc = rows_max(mloc);
     m_seen = fmaxf(m_seen, mloc);
-    if (m_ref == -INFINITY) m_ref = mloc;   // first tile with a valid row
+    if (!ref_set && mask != 0u) {   // the first tile with a valid row: both halves' maximum
+      if (g == 0) xm[rh][16 * hb + c] = mloc;
+      lds_barrier();
+      m_ref = fmaxf(mloc, xm[1 - rh][16 * hb + c]);
+      ref_set = true;
+    }
     const bool over = mloc > m_ref + kRefSlack;
-    float p[8], psum = 0.f;
+    float p[4], psum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[4 * mb + i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[mb][i] - m_ref);
-        psum += p[4 * mb + i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_ref);
+      psum += p[i];
+    }
     l_run += psum;
-    const u32x4 pw = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
-                           pack_f16x2(p[6], p[7])};
-    *reinterpret_cast<u32x4 *>(PB + (wv * 64 + lane) * 8) = pw;
+    *reinterpret_cast<u32x2 *>(PB + (hb * 64 + lane) * 8 + 4 * rh) = u32x2{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])};
     if (__ballot(over) && lane == 0) rflag[fl] = 1;
     asm volatile("" : "+v"(l_run), "+v"(m_seen));
     lds_barrier();   // P^T of every wave visible
     const uint16_t *v0p = Tb + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * wv;
     const uint16_t *v1p = v0p + 16 * KP;
-    f16x8 pf[NW];
+    f16x8 pf[NHB];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) pf[w] = *reinterpret_cast<const f16x8 *>(PB + (w * 64 + lane) * 8);
-    constexpr int VD = 4;
+    for (int h = 0; h < NHB; ++h) pf[h] = *reinterpret_cast<const f16x8 *>(PB + (h * 64 + lane) * 8);
+    constexpr int VD = DBW < 4 ? DBW : 4;
     v4i16 vlo[VD], vhi[VD];
 #pragma unroll
     for (int db = 0; db < VD; ++db) {
-      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * NW * db));
-      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * NW * db));
+      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * NWV * db));
+      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * NWV * db));
     }
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int db = 0; db < DBW; ++db) {
       f16x8 a;
       __builtin_memcpy(&a, &vlo[db % VD], 8);
       __builtin_memcpy(reinterpret_cast<char *>(&a) + 8, &vhi[db % VD], 8);
-      if (db + VD < DB) {
-        vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * NW * (db + VD)));
-        vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * NW * (db + VD)));
+      if (db + VD < DBW) {
+        vlo[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v0p + 16 * NWV * (db + VD)));
+        vhi[db % VD] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(lds_u16 *)(v1p + 16 * NWV * (db + VD)));
       }
 #pragma unroll
-      for (int w = 0; w < NW; ++w)
-        acc_o[w][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[w], acc_o[w][db], 0, 0, 0);
+      for (int h = 0; h < NHB; ++h) acc_o[h][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pf[h], acc_o[h][db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1402,8 +1422,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
   // its use, the compiler's waits for the gathers stay one step deep.
   auto step = [&](auto Bc, int tile, int it) -> bool {
     constexpr int B = decltype(Bc)::value;
-    DecRaw<NW> &Rc = B ? R1 : R0;
-    DecRaw<NW> &Rn = B ? R0 : R1;
+    DecRaw<NHB> &Rc = B ? R1 : R0;
+    DecRaw<NHB> &Rn = B ? R0 : R1;
     gather(tile + 2 < tile_hi ? tile + 2 : -1, Rc);
     if (tile < tile_hi) compute(TT + B * TH, tile, it % 3);
     if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
@@ -1411,7 +1431,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
     lds_barrier();   // next fp16 tile written, this one and P^T free, flags visible
     return rflag[it % 3] != 0;
   };
-
   // one pass over the split's tiles, its first two gathers issued; returns
   // whether a logit far above the reference asks for another pass.  Tiles go
   // in pairs (an odd count ends with a step that only gathers and decodes),
@@ -1430,10 +1449,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
   // the first pass is a copy of its own, so its waits are not merged with
   // the restart path's
   if (pass()) {
-    do {   // restart with the reference raised to the largest logit seen
+    do {   // restart with the reference raised to the largest logit seen (both halves)
+      if (g == 0) xm[rh][16 * hb + c] = m_seen;
       lds_barrier();
       if (tid < 3) rflag[tid] = 0;
-      m_ref = m_seen;
+      m_ref = fmaxf(m_seen, xm[1 - rh][16 * hb + c]);
+      ref_set = true;
       lds_barrier();
       l_run = 0.f;
       clear_acc();
@@ -1445,25 +1466,26 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
     clear_acc();
   }
 
-  // the head-owning waves' (reference, sum) pairs through LDS
-  float *shml = reinterpret_cast<float *>(PB);
+  // every head's (reference, sum over both row halves) through LDS
   {
     const float lr = rows_sum(l_run);
-    if (g == 0) {
-      shml[2 * (16 * wv + c)] = m_ref;
-      shml[2 * (16 * wv + c) + 1] = lr;
-    }
+    if (g == 0) xm[rh][16 * hb + c] = lr;
     lds_barrier();
   }
+  float *shm = reinterpret_cast<float *>(PB);
+  if (rh == 0 && g == 0) {
+    shm[2 * (16 * hb + c)] = m_ref;
+    shm[2 * (16 * hb + c) + 1] = xm[0][16 * hb + c] + xm[1][16 * hb + c];
+  }
+  lds_barrier();
   // MODE 0: split partial (fp16, staged), 1: fp32 output (direct), 2: bf16 output (staged)
   auto finish = [&](auto Mc) {
     constexpr int MODE = decltype(Mc)::value;
     const int ns = A.nsplit;
-    const int dlo = 16 * wv;
 #pragma unroll
-    for (int hb = 0; hb < NW; ++hb) {
-      const int h = 16 * hb + c;
-      const float mr = shml[2 * h], lr = shml[2 * h + 1];
+    for (int hh = 0; hh < NHB; ++hh) {
+      const int h = 16 * hh + c;
+      const float mr = shm[2 * h], lr = shm[2 * h + 1];
       float f = 1.f, den = lr;
       if (MODE != 0 && A.sinks) {   // the sink joins the denominator (exponents <= 0)
         const float sg = sk[h];
@@ -1474,12 +1496,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
       // split partials: normalised by the split's own sum, so fp16 holds them
       const float inv = den > 0.f ? f * __builtin_amdgcn_rcpf(den) : 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int db = 0; db < DBW; ++db) {
         float o[4];
-        const int d0 = dlo + 16 * NW * db + 4 * g;
+        const int cb = wv + NWV * db, d0 = 16 * cb + 4 * g;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = acc_o[hb][db][i] * inv;
-        if (MODE != 0 && dlo + 16 * NW * db >= D - R) {   // the output's rope slice turns back by -p
+        for (int i = 0; i < 4; ++i) o[i] = acc_o[hh][db][i] * inv;
+        if (MODE != 0 && 16 * cb >= D - R) {   // the output's rope slice turns back by -p
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             const int pi = (d0 + 2 * k - (D - R)) >> 1;
@@ -1498,7 +1520,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
           *reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(TT) + h * SROW + 2 * d0) = v;
         }
       }
-      if (MODE == 0 && g == 0 && hb == wv) {
+      if (MODE == 0 && g == 0 && hh == hb && rh == 0) {
         const int64_t pr = ((int64_t)r * ns + split) * A.H + h;
         A.part_ml[2 * pr] = lr > 0.f ? mr : -INFINITY;
         A.part_ml[2 * pr + 1] = lr;
@@ -1506,12 +1528,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_attn_dec(AttnArgs A) {
     }
     if (MODE != 1) {
       lds_barrier();
-      // wave w writes the rows of heads 16w .. 16w+15: lane l carries channels 8l .. 8l+7
+      // wave w writes the head rows w, w + NWV, ...: lane l carries channels 8l .. 8l+7
       uint16_t *orow = MODE == 0 ? A.part_o + (((int64_t)r * ns + split) * A.H) * D
                                  : (uint16_t *)A.out + (int64_t)r * A.H * D;
-#pragma unroll 4
-      for (int k = 0; k < 16; ++k) {
-        const int h = 16 * wv + k;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int h = wv + NWV * k;
         *reinterpret_cast<u32x4 *>(orow + (int64_t)h * D + 8 * lane) =
             *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint8_t *>(TT) + h * SROW + 16 * lane);
       }
@@ -1827,9 +1849,9 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   const bool fp8fast = fp8 && D == 512 && (W > 0 ? win->tail == 64 : true) && (pool ? pool->tail == 64 : true);
   dim3 grid((unsigned)((int64_t)T * ns));
   if (fp8fast && (H == 16 || H == 32 || H == 64)) {
-#define DSV4_DECK(NW)                                                                           \
-  if (rope_dim == 64) hipLaunchKernelGGL((k_attn_dec<NW, true>), grid, dim3(NW * 64), 0, st, A); \
-  else hipLaunchKernelGGL((k_attn_dec<NW, false>), grid, dim3(NW * 64), 0, st, A);
+#define DSV4_DECK(NHB)                                                                              \
+  if (rope_dim == 64) hipLaunchKernelGGL((k_attn_dec<NHB, true>), grid, dim3(NHB * 128), 0, st, A); \
+  else hipLaunchKernelGGL((k_attn_dec<NHB, false>), grid, dim3(NHB * 128), 0, st, A);
     switch (H) {
     case 16: DSV4_DECK(1) break;
     case 32: DSV4_DECK(2) break;
