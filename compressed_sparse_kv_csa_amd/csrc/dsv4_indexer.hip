@@ -78,14 +78,21 @@ __device__ __forceinline__ float keyf(uint32_t k) {
 // The key loads of iteration it+1 are issued before the MFMAs of iteration it
 // (two register stages), so each wave keeps 2*EB*16 key rows in flight: the
 // decode scan is one pass over a large pool and is bound by how many bytes
-// are outstanding, not by the matrix cores.  With hist0 set (rows that take
-// the long-row top-k) every stored score is also counted in an LDS histogram
-// of its key's top 11 bits, added to the row's histogram at the end.
+// are outstanding, not by the matrix cores.  The loop issues loads only: the
+// scores are staged in LDS and written out after it (a store in the loop would
+// count in the same in-order counter as the loads, and the wait for one stage
+// would then also wait for the stores behind it).  A workgroup handles at most
+// kScoreStage / (64 EB) - 1 super-blocks (the launcher sizes the grid so).
+// With hist0 set (rows that take the long-row top-k) every score is also
+// counted in an LDS histogram of its key's top 11 bits, added to the row's
+// histogram at the end.
 constexpr int kHistBins = 2048;
+constexpr int kScoreStage = 4096;   // staged scores per workgroup
 template <int NHB, int KS, bool FP4, int EB>
 __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float scale, uint32_t *hist0,
                                                            float *__restrict__ scores, int64_t ld) {
   __shared__ uint32_t lh[kHistBins];
+  __shared__ float sbuf[kScoreStage];
   const int r = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
       }
     }
   };
-  auto comp = [&](int e0, const Frag &f) {
+  auto comp = [&](int e0, const Frag &f, int slot) {
 #pragma unroll
     for (int eb = 0; eb < EB; ++eb) {
       float s = 0.f;
@@ -161,27 +168,46 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
       // sum over the four lane groups (heads 4g..4g+3 of every head block)
       s = rows_sum(s);
       const int e = e0 + 16 * eb + c;
-      if (g == 0 && e < hi) {
+      if (g == 0) {
         const float v = s * scale;
-        scores[(int64_t)r * ld + e] = v;
-        if (hist0) atomicAdd(&lh[fkey(v) >> 21], 1u);
+        sbuf[slot * STEP + 16 * EB * wv + 16 * eb + c] = v;
+        if (hist0 && e < hi) atomicAdd(&lh[fkey(v) >> 21], 1u);
       }
     }
   };
   const int gstride = (int)gridDim.y * STEP;
+  const int sb_lo = (int)blockIdx.y * STEP;   // this workgroup's first super-block
+  const int nsb = (hi - sb_lo + gstride - 1) / gstride;
   Frag f0, f1;
-  int e0 = (int)blockIdx.y * STEP + 16 * EB * wv;
-  if (e0 < hi) load(e0, f0);
-  for (; e0 < hi; e0 += 2 * gstride) {
-    const int e1 = e0 + gstride;
-    if (e1 < hi) load(e1, f1);
-    comp(e0, f0);
-    if (e1 >= hi) break;
-    if (e1 + gstride < hi) load(e1 + gstride, f0);
-    comp(e1, f1);
+  const int ew = 16 * EB * wv;
+  // super-blocks go in pairs (an odd count ends with a stage past the end);
+  // the stage loads are unconditional (load() clamps rows past the end to the
+  // last one) and the loop has one exit point, so with no branch around a
+  // load the compiler's wait before a stage's products leaves the other
+  // stage's loads in flight; the scheduling barriers keep that program order
+  load(sb_lo + ew, f0);
+  load(sb_lo + gstride + ew, f1);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int k = 0;; k += 2) {
+    const int e0 = sb_lo + k * gstride + ew;
+    comp(e0, f0, k);
+    __builtin_amdgcn_sched_barrier(0);
+    load(e0 + 2 * gstride, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    comp(e0 + gstride, f1, k + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(e0 + 3 * gstride, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (k + 2 >= nsb) break;
+  }
+  __syncthreads();
+  // the staged scores out, super-block by super-block (contiguous entries)
+  float *srow = scores + (int64_t)r * ld;
+  for (int i = threadIdx.x; i < nsb * STEP; i += 256) {
+    const int e = sb_lo + (i / STEP) * gstride + i % STEP;
+    if (e < hi) srow[e] = sbuf[i];
   }
   if (hist0) {
-    __syncthreads();
     for (int i = threadIdx.x; i < kHistBins; i += 256)
       if (lh[i]) atomicAdd(&hist0[(int64_t)r * kHistBins + i], lh[i]);
   }
@@ -1169,8 +1195,11 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
     // runs as one wave of workgroups with no partly filled second round
     const int64_t unit = 64LL * eb;   // entries per super-block
     const int64_t blocks = (kp->seq_stride + unit - 1) / unit;
-    const int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, resident_wgs((const void *)sk, 256) / T),
-                                              std::max<int64_t>(1, blocks));
+    int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, resident_wgs((const void *)sk, 256) / T),
+                                        std::max<int64_t>(1, blocks));
+    // at most kScoreStage / unit - 1 super-blocks per workgroup (its LDS staging)
+    const int64_t cap = kScoreStage / unit - 1;
+    per_row = std::max<int64_t>(per_row, (blocks + cap - 1) / cap);
     hipLaunchKernelGGL(sk, dim3(T, (unsigned)per_row), dim3(256), 0, st, Q, K, scale, hist0, scores, ld);
     hist_built = hist0 != nullptr;
   } else {
