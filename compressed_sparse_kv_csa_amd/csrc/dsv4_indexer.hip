@@ -839,8 +839,11 @@ __device__ void rt_row_select(const float *scores, int64_t ld, int r, int n, int
 // the last 10 key bits) to the exact kk-th largest key t*; then the keys above
 // t* and the first `want` keys equal to t* are written in position order.
 // Thread t holds the contiguous run of candidates [t*P, t*P + P) (P >= M/256):
-// each one's chunk comes from a branch-free search of the offsets in LDS, so
-// all of its key and position loads are issued together.
+// each one's chunk comes from a search of the offsets in LDS with no branch
+// (off[c] = M for every chunk c >= nch, so no chunk past the last is chosen
+// for i < M), and every key and position load is issued unconditionally (the
+// slot clamped into the row's range, the value dropped for i >= M), so all of
+// a thread's loads are in flight together.
 template <int P>
 __device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, const uint32_t *off, int nch, int cc, int M,
                                 int kk, uint32_t b0, uint32_t above0, uint32_t *lh, uint32_t *sh, int32_t *io,
@@ -853,11 +856,12 @@ __device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, const uin
     const int i = i0 + j;
     int a = 0;
 #pragma unroll
-    for (int step = kCandMaxChunks / 2; step > 0; step >>= 1)
-      a = (a + step < nch && (int)off[a + step] <= i) ? a + step : a;
-    const int sl = a * cc + (i - (int)off[a]);
-    k[j] = i < M ? rk[sl] : 0u;
-    pos[j] = i < M ? rp[sl] : 0;
+    for (int step = kCandMaxChunks / 2; step > 0; step >>= 1) a = (int)off[a + step] <= i ? a + step : a;
+    const int sl = min(a * cc + (i - (int)off[a]), kCandSlots - 1);
+    const uint32_t kv = rk[sl];
+    const int32_t pv = rp[sl];
+    k[j] = i < M ? kv : 0u;
+    pos[j] = i < M ? pv : 0;
   }
   // level 1: the next 11 bits of the keys in bin b0
   RtThr t{b0, above0, (uint32_t)kk - above0};
