@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdsv4.so")
+# DSV4_LIB names another build of the library (the host sanitizer build of
+# build.build_sanitized is loaded this way); the in-tree libdsv4.so otherwise
+LIB_PATH = os.environ.get("DSV4_LIB") or os.path.join(HERE, "libdsv4.so")
 
 DSV4_F32, DSV4_BF16, DSV4_FP8R, DSV4_MXFP4, DSV4_F16 = 0, 1, 2, 3, 4
 DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, -4

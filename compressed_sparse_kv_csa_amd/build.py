@@ -67,5 +67,38 @@ def _wait(item, verbose):
         print("\n".join(lines))
 
 
+def sanitizer_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime (ASan and UBSan handlers) that a
+    host process must preload to load a sanitizer build, or '' if absent."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/lib/llvm/bin/clang"
+    try:
+        out = subprocess.check_output([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], text=True).strip()
+    except (OSError, subprocess.CalledProcessError):
+        return ""
+    return out if os.path.isabs(out) and os.path.exists(out) else ""
+
+
+def build_sanitized(outdir: str) -> str:
+    """A copy of libdsv4.so whose host C-ABI layer (argument validation, workspace
+    sizing, dispatch: dsv4_api.cpp) is built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, linked with the device objects of build().  The
+    sanitizers apply to host code only (-Xarch_host); the GPU code is the same.
+    Load it by setting DSV4_LIB, with sanitizer_runtime() preloaded."""
+    objdir = os.path.join(HERE, "_build")
+    dev = [os.path.join(objdir, s + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in dev):
+        build()
+    os.makedirs(outdir, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+    api = os.path.join(outdir, "dsv4_api_san.o")
+    subprocess.check_call([HIPCC, "-O1", "-g", "-std=c++17", "-fPIC", "-fno-omit-frame-pointer"] + san +
+                          [f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, "dsv4_api.cpp"), "-o", api])
+    lib = os.path.join(outdir, "libdsv4_san.so")
+    subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + san + ["-shared-libsan", "-o", lib, api] + dev)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -44,6 +44,20 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(outdir: str) -> str:
+    """The oracle built with clang's AddressSanitizer and UndefinedBehaviorSanitizer
+    (the runtime shared with the library's sanitizer build, so one process can
+    load both).  Load it by setting DSV4_ORACLE_LIB."""
+    clang = "/opt/rocm/lib/llvm/bin/clang"
+    os.makedirs(outdir, exist_ok=True)
+    out = os.path.join(outdir, "liboracle_san.so")
+    libdir = "/opt/rocm/lib/llvm/lib"
+    subprocess.check_call([clang, "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                           "-shared-libsan", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-o", out, _SRC,
+                           "-lm", f"-L{libdir}", f"-Wl,-rpath,{libdir}"])
+    return out
+
+
 class _Rows(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("row_scale", ctypes.c_void_p),
                 ("blk_scale", ctypes.c_void_p), ("dtype", ctypes.c_int32),
@@ -58,7 +72,8 @@ _lib = None
 def _L():
     global _lib
     if _lib is None:
-        _lib = ctypes.CDLL(build())
+        # DSV4_ORACLE_LIB names another build (the sanitizer build of build_sanitized)
+        _lib = ctypes.CDLL(os.environ.get("DSV4_ORACLE_LIB") or build())
         P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         _lib.or_decode.argtypes = [P, I, I64, I, I, P, P, P]
         _lib.or_rope.argtypes = [P, I64, I, I, P, D, I]
