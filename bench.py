@@ -152,6 +152,21 @@ class CsaPrefill:
         return self.S
 
 
+class CsaPrefillSkewed(CsaPrefill):
+    """The CSA prefill step with the compressor's candidate input scaled by
+    POOL_SCALE: the pooled K=V rows (a convex combination of the candidates) get
+    logits far above the window rows', so the attention's fixed softmax
+    reference, taken from a query's first (window) tile, is passed by more than
+    2^15, repeatedly, and raised inside the tile each time.  Ordinary finite
+    inputs (pool values of a few tens); measures what those raises cost."""
+    name = "flash_csa_prefill_S8192_skewed_pool"
+    POOL_SCALE = 16.0
+
+    def __init__(self, torch, K, S_, **kw):
+        super().__init__(torch, K, S_, **kw)
+        self.c = (self.c.float() * self.POOL_SCALE).to(self.c.dtype)
+
+
 class HcaPrefill:
     """Flash-shaped HCA layer prefill (batch 1, seq 65536, m'=128, bf16)."""
     name = "flash_hca_prefill_S65536"
@@ -432,7 +447,7 @@ class CsaBlock(CsaPrefill):
 
 
 WORKLOADS = {"csa_prefill": CsaPrefill, "hca_prefill": HcaPrefill, "csa_decode": CsaDecode,
-             "mixed_decode": MixedDecode, "csa_block": CsaBlock}
+             "mixed_decode": MixedDecode, "csa_block": CsaBlock, "csa_prefill_skewed": CsaPrefillSkewed}
 
 
 def time_steps(torch, wl, steps, warmup):
@@ -839,7 +854,7 @@ def main():
         legs = {}
         del wl
         torch.cuda.empty_cache()
-        for name in ("hca_prefill", "csa_decode", "mixed_decode", "csa_block"):
+        for name in ("hca_prefill", "csa_decode", "mixed_decode", "csa_block", "csa_prefill_skewed"):
             log("leg", name)
             lw = WORKLOADS[name](torch, K, S_)
             torch.cuda.synchronize()
@@ -856,6 +871,20 @@ def main():
                               "projection_gflop": round(lw.gemm_flop / 1e9, 1),
                               "q_b_gemm_ms": round(lk, 3), "q_b_gemm_tflops": round(ach, 1),
                               "q_b_gemm_frac_mfma_peak": round(ach / PEAK_MFMA_F16, 4)}
+            elif isinstance(lw, CsaPrefillSkewed):
+                prev = K.dsv4_set_diagnostics(True)
+                try:
+                    K.dsv4_read_diagnostics(reset=True)
+                    lw.step()
+                    diag = K.dsv4_read_diagnostics(reset=True)
+                finally:
+                    K.dsv4_set_diagnostics(prev)
+                legs[name] = {"workload": lw.name, "pool_value_scale": lw.POOL_SCALE,
+                              "tokens_per_s": round(lw.tokens() / (lms / 1e3), 1), "ms_per_step": round(lms, 3),
+                              "softmax_ref_raises": diag["ref_raises"],
+                              "ref_raises_per_query": round(diag["ref_raises"] / lw.tokens(), 3),
+                              "attn_kernel_ms": round(lk, 3), "attn_kernel_ms_unskewed": round(kern_ms, 3),
+                              "raise_cost": round(lk / kern_ms - 1.0, 3)}
             elif isinstance(lw, HcaPrefill):
                 ach = lw.counts["attn_flop"] / (lk / 1e3) / 1e12
                 legs[name] = {"workload": lw.name, "tokens_per_s": round(lw.tokens() / (lms / 1e3), 1),

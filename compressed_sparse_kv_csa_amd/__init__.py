@@ -24,7 +24,7 @@ DSV4_F32, DSV4_BF16, DSV4_FP8R, DSV4_MXFP4, DSV4_F16 = 0, 1, 2, 3, 4
 DSV4_OK, DSV4_EINVAL, DSV4_ENOTSUP, DSV4_EHIP, DSV4_EWORKSPACE = 0, -1, -2, -3, -4
 
 EXPORTS = ["dsv4_compress", "dsv4_rope", "dsv4_index_topk_workspace", "dsv4_index_topk",
-           "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant",
+           "dsv4_attn_workspace", "dsv4_sparse_attn", "dsv4_hca_attn", "dsv4_set_batch_invariant", "dsv4_set_diagnostics", "dsv4_read_diagnostics",
            "dsv4_quantize", "dsv4_cache_append", "dsv4_linear", "dsv4_last_error", "dsv4_version",
            "dsv4_index_topk_noalloc"]
 NOALLOC_SCRATCH_BYTES = 16 << 20   # DSV4_NOALLOC_SCRATCH_BYTES in include/dsv4.h
@@ -88,6 +88,8 @@ def lib():
         L.dsv4_sparse_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, P, I32, P, F, I32, D, P, I32, P, SZ, P]
         L.dsv4_hca_attn.argtypes = [P, P, I32, I32, I32, P, I32, P, I32, P, F, I32, D, P, I32, P, SZ, P]
         L.dsv4_set_batch_invariant.argtypes = [I32]
+        L.dsv4_set_diagnostics.argtypes = [I32]
+        L.dsv4_read_diagnostics.argtypes = [P, I32]
         L.dsv4_quantize.argtypes = [P, I32, I64, I32, I32, P, P, P, I32, P]
         L.dsv4_cache_append.argtypes = [P, I32, P, P, P, P, P, P, I32, P]
         L.dsv4_linear.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, I32, I32, I64, I64, I64, P]
@@ -459,6 +461,22 @@ def dsv4_set_batch_invariant(on: bool) -> bool:
     """Fixed per-query reduction order whatever the batch (see include/dsv4.h).
     Returns the previous setting."""
     return bool(lib().dsv4_set_batch_invariant(int(bool(on))))
+
+
+DSV4_DIAG_REF_RAISES, DSV4_DIAG_BAD_PICKS, DSV4_DIAG_COUNT = 0, 1, 4
+
+
+def dsv4_set_diagnostics(on: bool) -> bool:
+    """Count softmax reference raises and out-of-range picks in the attention calls
+    (see include/dsv4.h).  Returns the previous setting."""
+    return bool(lib().dsv4_set_diagnostics(int(bool(on))))
+
+
+def dsv4_read_diagnostics(reset: bool = False) -> dict:
+    """The current GPU's counters after its queued work: {"ref_raises", "bad_picks"}."""
+    buf = (ctypes.c_uint64 * DSV4_DIAG_COUNT)()
+    _check(lib().dsv4_read_diagnostics(ctypes.addressof(buf), int(bool(reset))))
+    return {"ref_raises": int(buf[DSV4_DIAG_REF_RAISES]), "bad_picks": int(buf[DSV4_DIAG_BAD_PICKS])}
 
 
 def dsv4_last_error() -> str:

@@ -43,6 +43,8 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
 int attn_nsplit(int T, int64_t max_rows);
 size_t attn_ws(int T, int H, int D, int64_t max_rows);
 int set_batch_invariant(bool on);
+int set_diagnostics(bool on);
+int read_diagnostics(uint64_t *out, bool reset);
 int launch_cache_append(const dsv4_cache *C, int n, const int32_t *n_new, const void *kv, const void *kv_c,
                         const void *kv_z, const void *idx_c, const void *idx_z, int in_dtype, hipStream_t st);
 int launch_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, void *y, int64_t ldy, int y_dtype, int M,
@@ -199,6 +201,14 @@ int dsv4_linear(const void *x, int64_t ldx, const void *w, int64_t ldw, void *y,
 }
 
 int dsv4_set_batch_invariant(int32_t on) { return dsv4host::set_batch_invariant(on != 0); }
+
+int dsv4_set_diagnostics(int32_t on) { return dsv4host::set_diagnostics(on != 0); }
+
+int dsv4_read_diagnostics(uint64_t *out, int32_t reset) {
+  if (!out) return fail(DSV4_EINVAL, "read_diagnostics: NULL output");
+  const int rc = dsv4host::read_diagnostics(out, reset != 0);
+  return rc ? rc : ok();
+}
 
 int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *pos_bias, int32_t n_seq,
                   int32_t seq_len, int32_t dim, int32_t m, int32_t overlap, int32_t rope_dim, double rope_theta,

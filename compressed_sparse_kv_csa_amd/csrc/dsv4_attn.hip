@@ -72,7 +72,13 @@ struct AttnArgs {
   int nsplit;
   uint16_t *part_o;   // [T*nsplit*H, D] fp16: each split's output normalised by its own sum
   float *part_ml;     // [T*nsplit*H, 2]: the split's reference maximum (log2 units) and sum
+  int diag;           // count into g_diag (dsv4_set_diagnostics)
 };
+
+// Diagnostic counters of this GPU (DSV4_DIAG_*), added to only while
+// dsv4_set_diagnostics is on: raises of the fixed softmax reference inside a
+// tile, and pick entries that are neither -1 nor below the pool count.
+__device__ unsigned long long g_diag[DSV4_DIAG_COUNT];
 
 constexpr int kMaxSel = 2048;
 
@@ -138,11 +144,18 @@ __device__ __forceinline__ IdxPre<NT> load_idx(const AttnArgs &A, int r) {
 // preserving order.  Block-wide, one barrier; returns the count (sel[] is
 // visible after the caller's next barrier).  sh_cnt holds kMaxSel/64 ints.
 template <int NT>
-__device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int b, int *sel, int *sh_cnt) {
+__device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int b, int *sel, int *sh_cnt,
+                           bool count_bad = false) {
   constexpr int NWV = NT / 64, PER = kMaxSel / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int cnt = A.pool.count[b];
   const int nq = (A.topk + NT - 1) / NT;
+  if (A.diag && count_bad) {   // entries past the row's end load as -1
+    unsigned long long nb = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) nb += (q < nq && pre.v[q] != -1 && !(pre.v[q] >= 0 && pre.v[q] < cnt)) ? 1ull : 0ull;
+    if (nb) atomicAdd(&g_diag[DSV4_DIAG_BAD_PICKS], nb);
+  }
   unsigned long long bal[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
@@ -165,8 +178,8 @@ __device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int b, int 
   return total;
 }
 template <int NT>
-__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cnt) {
-  return compact_idx<NT>(A, load_idx<NT>(A, r), b, sel, sh_cnt);
+__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cnt, bool count_bad = false) {
+  return compact_idx<NT>(A, load_idx<NT>(A, r), b, sel, sh_cnt, count_bad);
 }
 
 // storage row (within its sequence) of window row i of a query
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
     for (int j = 0; j < NJ; ++j) qb[j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
   }
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_cnt);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_cnt, blockIdx.x % A.nsplit == 0);
   const int nrows = P.nwin + P.nsel;
   const int ntiles = (nrows + 31) / 32;
   const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
@@ -522,6 +535,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   __shared__ float sk[64];   // the heads' sinks (log2 units), loaded with the setup
   __shared__ int sh_cnt[kMaxSel / 64];
   __shared__ int rflag[3];   // overflow flags of tiles it mod 3: a flag is cleared two tiles after its last read
+  __shared__ float fsh[DSPV ? 64 : 1];   // per-head factors of a reference raise
   __shared__ __attribute__((aligned(16))) uint16_t PB[DSPV ? NW * 64 * 8 : 8];   // P^T fragments, wave-major
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -587,7 +601,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   const bool early = !FP8 && A.nsplit == 1 && (csa ? nwin >= 32 : nrows > 0);
   if (early) gather(0, T0);
   if (csa && A.topk > 0) {
-    P.nsel = compact_idx<NT>(A, ipre, P.b, sel, sh_cnt);
+    P.nsel = compact_idx<NT>(A, ipre, P.b, sel, sh_cnt, split == 0);
     nrows = nwin + P.nsel;
   }
   const int ntiles = (nrows + 31) / 32;
@@ -731,13 +745,13 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 #pragma unroll
   for (int hb = 0; hb < NHB; ++hb) { m_ref[hb] = -INFINITY; m_seen[hb] = -INFINITY; }
 
-  // one tile: scores, probabilities against m_ref, PV.  Returns true if a
-  // logit of this wave overflowed the reference.
+  // one tile: scores, probabilities against m_ref (raised within the tile when
+  // a logit passes it by more than 2^15), PV.
   // Tn/idn: the next tile's buffer and row ids (Tn == nullptr: nothing to
   // gather); its DMAs are spread over the k-steps of S^T so that their issue
   // (the texture path moves 64 B per clock per CU) overlaps the matrix cores
   auto compute = [&](const uint16_t *__restrict__ T, int tile, uint16_t *__restrict__ Tn, uint64_t idn,
-                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile, int fl) -> bool {
+                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile, int fl) {
     const int base = 32 * tile;
     // FP8 rows: the next raw tile's gather is issued during this tile's
     // matrix work (its buffer is disjoint from T), one DMA per few k-steps
@@ -794,8 +808,24 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    // probabilities of head block hb against its reference, packed as the P^T fragment
+    auto probs = [&](int hb, f16x8 &pf) -> float {
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[4 * mb + i] = __builtin_amdgcn_exp2f(s[hb][mb][i] - m_ref[hb]);
+          psum += p[4 * mb + i];
+        }
+      const u32x4 pw = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
+                             pack_f16x2(p[6], p[7])};
+      __builtin_memcpy(&pf, &pw, 16);
+      return psum;
+    };
     bool over = false;
     f16x8 pb[NHB];
+    float ps[NHB];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       if (base + 32 > nrows) {   // only the last tile holds positions past the list
@@ -812,28 +842,31 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s[hb][mb][i]);
       mloc = rows_max(mloc);
       m_seen[hb] = fmaxf(m_seen[hb], mloc);
-      if (m_ref[hb] == -INFINITY) m_ref[hb] = mloc;   // first tile of this pass
-      over = over || (mloc > m_ref[hb] + kRefSlack);
-      float p[8], psum = 0.f;
+      if (m_ref[hb] == -INFINITY) m_ref[hb] = mloc;   // first tile
+      const bool ov = mloc > m_ref[hb] + kRefSlack;
+      if constexpr (!DSPV) {
+        // the wave owns its heads' whole tile: a logit more than 2^15 above the
+        // reference raises the reference to the largest logit seen, and the
+        // running sum and the accumulators follow by 2^(old - new)
+        if (__ballot(ov)) {
+          const float f = __builtin_amdgcn_exp2f(m_ref[hb] - m_seen[hb]);
+          m_ref[hb] = m_seen[hb];
+          l_run[hb] *= f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[4 * mb + i] = __builtin_amdgcn_exp2f(s[hb][mb][i] - m_ref[hb]);
-          psum += p[4 * mb + i];
+          for (int db = 0; db < DB; ++db) acc_o[hb][db] = acc_o[hb][db] * f;
+          if (A.diag && lane == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
         }
-      l_run[hb] += psum;
-      const u32x4 pw = u32x4{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
-                             pack_f16x2(p[6], p[7])};
-      __builtin_memcpy(&pb[hb], &pw, 16);
+      } else {
+        over = over || ov;
+      }
+      ps[hb] = probs(hb, pb[hb]);
+      if constexpr (!DSPV) l_run[hb] += ps[hb];
     }
     if constexpr (DSPV) {
       // every wave's P^T fragment to LDS (PB was last read before the previous
       // tile's closing barrier), then O^T[this wave's channels, all heads]
       *reinterpret_cast<f16x8 *>(PB + (wv * 64 + lane) * 8) = pb[0];
-      if (__ballot(over) && lane == 0) rflag[fl] = 1;   // raised before the barrier: nothing live across PV
-      // the running sum and maximum settled here, so no probability stays live across PV
-      asm volatile("" : "+v"(l_run[0]), "+v"(m_seen[0]));
+      if (__ballot(over) && lane == 0) rflag[fl] = 1;   // raised before the barrier
       // the next tile's gather: issued where the wave would wait for the others'
       // scores anyway (its buffer was released by the previous tile's closing barrier)
       if (!FP8 && Tn) {
@@ -841,6 +874,29 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         for (int k = 0; k < RPW; ++k) dma_row(idn, k, Tn);
       }
       lds_barrier();   // P^T of every wave visible; the next tile's DMAs stay in flight
+      if (rflag[fl]) {
+        // a logit more than 2^15 above its head's reference: every head's
+        // reference rises to its largest logit seen so far, this tile's P^T is
+        // taken again, and the running sums and every wave's accumulators (all
+        // heads) scale by 2^(old - new); nothing of this tile has been summed yet
+        const float f = __builtin_amdgcn_exp2f(m_ref[0] - m_seen[0]);
+        m_ref[0] = m_seen[0];
+        l_run[0] *= f;
+        if (g == 0) fsh[16 * wv + c] = f;
+        ps[0] = probs(0, pb[0]);
+        *reinterpret_cast<f16x8 *>(PB + (wv * 64 + lane) * 8) = pb[0];
+        if (A.diag && tid == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
+        lds_barrier();   // the factors and the new P^T visible
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const float fw = fsh[16 * w + c];
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc_o[w][db] = acc_o[w][db] * fw;
+        }
+      }
+      l_run[0] += ps[0];
+      // the running sum and maximum settled here, so no probability stays live across PV
+      asm volatile("" : "+v"(l_run[0]), "+v"(m_seen[0]));
       // head blocks in groups of HG (P^T fragments live: HG; V^T read NW/HG times)
       constexpr int HG = NW;
       const uint16_t *v0p = T + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * wv;
@@ -872,7 +928,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      return false;
+      return;
     }
     // O^T += V^T P^T; V^T fragments by transposing reads of the row-major tile,
     // pipelined VD 16-dim blocks deep
@@ -899,32 +955,28 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         if constexpr (!DSPV) acc_o[hb][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[hb], acc_o[hb][db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    return over;
   };
 
-  for (int pass = 0;; ++pass) {
+  {
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) l_run[hb] = 0.f;
 #pragma unroll
     for (int ah = 0; ah < AH; ++ah)
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc_o[ah][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool restart = false;
     int it = 0;
     if constexpr (!FP8) {
-      if (tile_lo < tile_hi && !(early && pass == 0)) gather(tile_lo, T0);
+      if (tile_lo < tile_hi && !early) gather(tile_lo, T0);
       vm_wait_all();     // this wave's rows of the first tile landed ...
       __syncthreads();   // ... and every wave's
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool odd = it & 1;
         const bool more = tile + 1 < tile_hi;
-        const bool over = compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_addr(tile + 1) : 0,
-                                  nullptr, nullptr, 0, it % 3);
-        if (__ballot(over) && lane == 0) rflag[it % 3] = 1;
-        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
+        compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_addr(tile + 1) : 0, nullptr,
+                nullptr, 0, it % 3);
+        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the P barrier of tile it-2
         vm_wait_all();     // this wave's rows of the next tile landed ...
-        __syncthreads();   // ... and every wave's; this one fully read, flags visible
-        if (rflag[it % 3]) { restart = true; break; }
+        __syncthreads();   // ... and every wave's; this one fully read
       }
     } else {
       // one raw buffer and one fp16 tile (two workgroups share a CU, so one's
@@ -937,22 +989,14 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       lds_barrier();
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool more = tile + 1 < tile_hi;
-        const bool over = compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1, it % 3);
-        if (__ballot(over) && lane == 0) rflag[it % 3] = 1;
-        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
+        compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1, it % 3);
+        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the P barrier of tile it-2
         vm_wait_all();     // this wave's part of raw tile+1 landed ...
-        __syncthreads();   // ... and every wave's; the tile fully read, flags visible
-        if (rflag[it % 3]) { restart = true; break; }
+        __syncthreads();   // ... and every wave's; the tile fully read
         if (more) convert(RW, RSC, T0);
         lds_barrier();
       }
     }
-    if (!restart) break;
-    __syncthreads();
-    if (tid < 3) rflag[tid] = 0;
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) m_ref[hb] = m_seen[hb];
-    __syncthreads();
   }
 
   // DSPV: the head-owning waves' (reference, sum) pairs through LDS
@@ -1065,8 +1109,9 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 //     spread over twice the waves);
 //   * the fixed-reference softmax: both row halves of a head share one
 //     reference, taken from the first tile with a valid row through one LDS
-//     exchange; each wave publishes its 16-row half of the head block's P^T
-//     fragment;
+//     exchange (and raised inside a tile, with the partial sums and the
+//     accumulators rescaled, when a logit passes it by more than 2^15); each
+//     wave publishes its 16-row half of the head block's P^T fragment;
 //   * O^T = V^T P^T with the channels split over all waves (wave w owns the
 //     16-channel blocks w, w + 2 NHB, ...), every P^T fragment read by every
 //     wave, so each V^T fragment read from LDS feeds NHB products.
@@ -1141,6 +1186,7 @@ __global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
   __shared__ float rc[32], rs[32];
   __shared__ float sk[64];
   __shared__ float xm[2][64];        // per row half: a head's tile maximum, then its sum
+  __shared__ float fsh[64];          // per-head factors of a reference raise
   __shared__ int rflag[3];
   __shared__ __attribute__((aligned(16))) uint16_t PB[NHB * 64 * 8];
 
@@ -1190,11 +1236,16 @@ __global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
   int tile_hi = min(ntiles, tile_lo + tps);
   const int e_lo = max(0, 32 * tile_lo - nwin), e_hi = csa ? min(A.topk, 32 * tile_hi - nwin) : 0;
   if (csa && A.topk > 0) {
+    unsigned long long nb = 0;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
       const int e = tid + NT * k;
-      if (e >= e_lo && e < e_hi) ids[e - e_lo] = ipre[k];
+      if (e >= e_lo && e < e_hi) {
+        ids[e - e_lo] = ipre[k];
+        nb += (ipre[k] != -1 && !(ipre[k] >= 0 && ipre[k] < pcount)) ? 1ull : 0ull;
+      }
     }
+    if (A.diag && nb) atomicAdd(&g_diag[DSV4_DIAG_BAD_PICKS], nb);
   }
   const uint8_t *pbase = A.pool.data ? A.pool.data + (int64_t)P.b * A.pool.stride * RB : nullptr;
   const uint8_t *wbase = A.win.data ? A.win.data + (int64_t)P.b * A.win.stride * RB : nullptr;
@@ -1377,17 +1428,45 @@ __global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
       ref_set = true;
     }
     const bool over = mloc > m_ref + kRefSlack;
-    float p[4], psum = 0.f;
+    // this wave's 16-row half of the head block's P^T fragment, against the reference
+    auto probs = [&]() -> float {
+      float p[4], psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_ref);
-      psum += p[i];
+      for (int i = 0; i < 4; ++i) {
+        p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_ref);
+        psum += p[i];
+      }
+      *reinterpret_cast<u32x2 *>(PB + (hb * 64 + lane) * 8 + 4 * rh) = u32x2{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])};
+      return psum;
+    };
+    float psum = probs();
+    if (__ballot(over) && lane == 0) rflag[fl] = 1;
+    lds_barrier();   // P^T of every wave visible
+    if (rflag[fl]) {
+      // a logit more than 2^15 above its head's reference: every head's
+      // reference rises to its largest logit seen so far (both row halves),
+      // this tile's P^T is taken again, and the running sums and every wave's
+      // accumulators (all heads) scale by 2^(old - new); nothing of this tile
+      // has been summed yet
+      if (g == 0) xm[rh][16 * hb + c] = m_seen;
+      lds_barrier();
+      const float mn = fmaxf(m_seen, xm[1 - rh][16 * hb + c]);
+      const float f = __builtin_amdgcn_exp2f(m_ref - mn);
+      m_ref = mn;
+      l_run *= f;
+      if (g == 0 && rh == 0) fsh[16 * hb + c] = f;
+      psum = probs();
+      if (A.diag && tid == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
+      lds_barrier();   // the factors and the new P^T visible
+#pragma unroll
+      for (int h = 0; h < NHB; ++h) {
+        const float fh = fsh[16 * h + c];
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) acc_o[h][db] = acc_o[h][db] * fh;
+      }
     }
     l_run += psum;
-    *reinterpret_cast<u32x2 *>(PB + (hb * 64 + lane) * 8 + 4 * rh) = u32x2{pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])};
-    if (__ballot(over) && lane == 0) rflag[fl] = 1;
     asm volatile("" : "+v"(l_run), "+v"(m_seen));
-    lds_barrier();   // P^T of every wave visible
     const uint16_t *v0p = Tb + (4 * g + (c >> 2)) * KP + 4 * (c & 3) + 16 * wv;
     const uint16_t *v1p = v0p + 16 * KP;
     f16x8 pf[NHB];
@@ -1416,51 +1495,30 @@ __global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
   };
   // tile `tile` (in fp16 tile B, its raw registers free) on the matrix cores
   // while the gather of tile+2 is in flight, then tile+1 decoded into the other
-  // fp16 tile.  Returns whether a logit overflowed the reference.  The gather
-  // and the decode run past the last tile too (the stand-in rows decode to
-  // zeros; only the matrix work is skipped): with no branch around a load or
-  // its use, the compiler's waits for the gathers stay one step deep.
-  auto step = [&](auto Bc, int tile, int it) -> bool {
+  // fp16 tile.  The gather and the decode run past the last tile too (the
+  // stand-in rows decode to zeros; only the matrix work is skipped): with no
+  // branch around a load or its use, the compiler's waits for the gathers stay
+  // one step deep.
+  auto step = [&](auto Bc, int tile, int it) {
     constexpr int B = decltype(Bc)::value;
     DecRaw<NHB> &Rc = B ? R1 : R0;
     DecRaw<NHB> &Rn = B ? R0 : R1;
     gather(tile + 2 < tile_hi ? tile + 2 : -1, Rc);
     if (tile < tile_hi) compute(TT + B * TH, tile, it % 3);
-    if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the barrier of tile it-2
+    if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the P barrier of tile it-2
     convert(Rn, TT + (1 - B) * TH);
-    lds_barrier();   // next fp16 tile written, this one and P^T free, flags visible
-    return rflag[it % 3] != 0;
+    lds_barrier();   // next fp16 tile written, this one and P^T free
   };
-  // one pass over the split's tiles, its first two gathers issued; returns
-  // whether a logit far above the reference asks for another pass.  Tiles go
-  // in pairs (an odd count ends with a step that only gathers and decodes),
-  // so the loop has one exit point and every path back to its head has
-  // passed both steps' waits.
-  auto pass = [&]() __attribute__((always_inline)) -> bool {
-    convert(R0, TT);
-    lds_barrier();
-    for (int tile = tile_lo, it = 0;; tile += 2, it += 2) {
-      const bool o0 = step(std::integral_constant<int, 0>{}, tile, it);
-      const bool o1 = step(std::integral_constant<int, 1>{}, tile + 1, it + 1);
-      if (o0 || o1) return true;
-      if (tile + 2 >= tile_hi) return false;
-    }
-  };
-  // the first pass is a copy of its own, so its waits are not merged with
-  // the restart path's
-  if (pass()) {
-    do {   // restart with the reference raised to the largest logit seen (both halves)
-      if (g == 0) xm[rh][16 * hb + c] = m_seen;
-      lds_barrier();
-      if (tid < 3) rflag[tid] = 0;
-      m_ref = fmaxf(m_seen, xm[1 - rh][16 * hb + c]);
-      ref_set = true;
-      lds_barrier();
-      l_run = 0.f;
-      clear_acc();
-      gather(tile_lo, R0);
-      gather(tile_lo + 1 < tile_hi ? tile_lo + 1 : -1, R1);
-    } while (pass());
+  // the split's tiles, the first two gathers issued.  Tiles go in pairs (an
+  // odd count ends with a step that only gathers and decodes), so the loop
+  // has one exit point and every path back to its head has passed both
+  // steps' waits.
+  convert(R0, TT);
+  lds_barrier();
+  for (int tile = tile_lo, it = 0;; tile += 2, it += 2) {
+    step(std::integral_constant<int, 0>{}, tile, it);
+    step(std::integral_constant<int, 1>{}, tile + 1, it + 1);
+    if (tile + 2 >= tile_hi) break;
   }
   } else {
     clear_acc();
@@ -1627,7 +1685,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs A, int D) {
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_cnt);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_cnt, true);
   const int nrows = P.nwin + P.nsel;
   const int R = A.rope_dim;
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
@@ -1766,6 +1824,23 @@ static std::atomic<int> g_batch_invariant{0};
 
 int set_batch_invariant(bool on) { return g_batch_invariant.exchange(on ? 1 : 0); }
 
+static std::atomic<int> g_diag_on{0};
+
+int set_diagnostics(bool on) { return g_diag_on.exchange(on ? 1 : 0); }
+
+// The current device's counters to out (after every queued kernel finished),
+// cleared if reset.
+int read_diagnostics(uint64_t *out, bool reset) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_diag), sizeof(uint64_t) * DSV4_DIAG_COUNT, 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && reset) {
+    static const uint64_t zero[DSV4_DIAG_COUNT] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_diag), zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return fail(DSV4_EHIP, "read_diagnostics: %s", hipGetErrorString(e));
+  return DSV4_OK;
+}
+
 // Splits per query (decode): enough workgroups to occupy the chip, but at least
 // four 32-row tiles per split, because every split writes a 64 x 512 fp16
 // partial (normalised by its own sum) plus fp32 (max, sum) per head that the
@@ -1830,6 +1905,7 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   for (int i = 0; i < 32; ++i) A.inv_freq[i] = (i < rope_dim / 2) ? pow(theta, -2.0 * i / (double)rope_dim) : 0.0;
   A.out = out;
   A.out_dtype = out_dtype;
+  A.diag = g_diag_on.load(std::memory_order_relaxed);
   if (q_dtype == DSV4_F32) {
     A.nsplit = 1;
     const size_t lds = ((size_t)H * D + 32 * (size_t)D + 32 * (size_t)H + 3 * (size_t)H) * 4;

@@ -252,6 +252,33 @@ int dsv4_quantize(const void *x, int32_t x_dtype, int64_t n_rows, int32_t dim, i
  * Returns the previous setting. */
 int dsv4_set_batch_invariant(int32_t on);
 
+/* dsv4_set_diagnostics / dsv4_read_diagnostics -- a debugging aid, off by
+ * default.  While on, the attention calls (dsv4_sparse_attn, dsv4_hca_attn)
+ * count into process-wide counters held on each GPU:
+ *   DSV4_DIAG_REF_RAISES -- times a workgroup (a wave, where waves own whole
+ *       heads) raised its fixed softmax reference inside a tile because a
+ *       logit passed it by more than 2^15: the reference becomes the largest
+ *       logit seen, the partial sums and accumulators scale by the power of two
+ *       between the two references and the tile's probabilities are taken
+ *       again (the result is the same either way; the count measures the
+ *       extra work, one softmax and two barriers per raise);
+ *   DSV4_DIAG_BAD_PICKS -- idx entries that are neither the -1 sentinel nor a
+ *       pool entry below the sequence's count (HF DeepSeek-V4 page, "Attention
+ *       mask layout": only -1 marks an unused slot); attention treats such an
+ *       entry like -1, and this counter is how a caller finds them.
+ * Each pick entry is counted once per call whatever the split of its query.
+ * Counting adds no work per row: the checks already run, and a workgroup adds
+ * to a counter only when it has something to add.  Concurrent calls on one GPU
+ * add to the same counters.  dsv4_set_diagnostics affects calls made after it
+ * and returns the previous setting.  dsv4_read_diagnostics waits for the
+ * current device's queued work, copies its DSV4_DIAG_COUNT counters to out
+ * (host memory) and clears them if reset != 0; returns DSV4_OK or DSV4_EHIP. */
+#define DSV4_DIAG_REF_RAISES 0
+#define DSV4_DIAG_BAD_PICKS 1
+#define DSV4_DIAG_COUNT 4
+int dsv4_set_diagnostics(int32_t on);
+int dsv4_read_diagnostics(uint64_t *out, int32_t reset);
+
 /* ---- decode caches: streaming maintenance ----
  * HF DeepSeek-V4 page, "Cache layers": every compressed-attention layer carries
  * its compressor (and indexer) state from one forward call to the next -- a

@@ -152,6 +152,19 @@ def test_batch_invariant_switch(K):
         K.dsv4_set_batch_invariant(prev)
 
 
+def test_diagnostics_switch(K):
+    """The diagnostics switch returns the previous setting; reading the counters
+    into a NULL buffer is rejected before any device call."""
+    prev = K.dsv4_set_diagnostics(True)
+    try:
+        assert K.dsv4_set_diagnostics(False) is True
+        assert K.dsv4_set_diagnostics(False) is False
+        assert K.lib().dsv4_read_diagnostics(None, 0) == K.DSV4_EINVAL
+        assert "NULL" in K.dsv4_last_error()
+    finally:
+        K.dsv4_set_diagnostics(prev)
+
+
 def test_quantize_rejects_bad_args(K):
     L = K.lib()
     fake = ctypes.c_void_p(0x1000)

@@ -1,14 +1,17 @@
 """The fp16 attention kernels take each head's probabilities against a fixed
-reference, the first tile's maximum logit, and start the query over with the
-largest logit seen so far as the new reference when a later tile passes the
-reference by more than 15 in log2 units (so no probability can leave fp16's
-range).  These cases force one and two such restarts: every query shares a
+reference, the first tile's maximum logit.  When a later tile passes the
+reference by more than 15 in log2 units (so no probability could stay inside
+fp16's range), the reference is raised inside that tile to the largest logit
+seen so far: the partial sums and the accumulators scale by the power of two
+between the two references and the tile's probabilities are taken again.
+These cases force one and two such raises per query: every query shares a
 common direction c, the rows of the first tiles are small noise (logits near
 0), and chosen picks are rows along c with natural-log logits of about 12, 22
 and 24, placed in successive tiles.  Checked against the oracle's exact
 softmax on the fp16 prefill path, the FP8 decode path (split over several
-workgroups) and the generic bf16 path.  The test also checks, on the CPU, that
-the inputs really take the logit spread past the restart threshold."""
+workgroups) and the generic bf16 path, and the number of raises against the
+rule run on the CPU.  The test also checks, on the CPU, that the inputs
+really take the logit spread past the threshold."""
 import numpy as np
 import pytest
 import torch
@@ -82,12 +85,52 @@ def test_prefill_restart(K, rows, H):
     assert np.all(s[:, 32:].max(1) > s[:, :32].max(1) + 15.5)
     sinks = rng.standard_normal(H).astype(np.float32)
     Q = K.QueryRows(dev(seq), dev(tok), None, 1)
-    out = K.dsv4_sparse_attn(Q, tensor_of(q, "bf16"), upload_rows(wset), W, upload_rows(pset), dev(idx),
-                             dev(sinks), 1 / np.sqrt(D), R, theta, out_dtype=torch.float32)
-    torch.cuda.synchronize()
+    prev = K.dsv4_set_diagnostics(True)
+    try:
+        K.dsv4_read_diagnostics(reset=True)
+        out = K.dsv4_sparse_attn(Q, tensor_of(q, "bf16"), upload_rows(wset), W, upload_rows(pset), dev(idx),
+                                 dev(sinks), 1 / np.sqrt(D), R, theta, out_dtype=torch.float32)
+        diag = K.dsv4_read_diagnostics(reset=True)
+    finally:
+        K.dsv4_set_diagnostics(prev)
     ref = O.attn(seq, tok, np.zeros(1, np.int64), S.bf16_bits(q), "bf16", wset, W, pset, "csa", idx=idx,
                  sinks=sinks, sm_scale=1 / np.sqrt(D), rope_dim=R, theta=theta)
-    assert_close(out.cpu().numpy(), ref, "bf16", "attention across softmax restarts")
+    assert_close(out.cpu().numpy(), ref, "bf16", "attention across softmax reference raises")
+    # the raise counter against the rule run on the CPU over every query whose
+    # picks hold a jump entry (the others' logits stay near 0): thresholds a
+    # little either side of 15 bound the fp16 rounding of q~ and the rows
+    lo = hi = 0
+    jump_rows = {e for e, _ in jumps.values()}
+    for t in range(Sx):
+        if not jump_rows & set(idx[t][idx[t] >= 0].tolist()):
+            continue
+        rows_t = np.concatenate([win[max(0, t - W + 1):t + 1], pool[idx[t][idx[t] >= 0]]])
+        lg = q[t].astype(np.float64) @ rows_t.T / np.sqrt(D) * LOG2E
+        lo += count_raises(lg, 15.05)
+        hi += count_raises(lg, 14.95)
+    say("reference raises", diag["ref_raises"], "expected", lo, "..", hi)
+    if rows == "f16":   # the fixed-reference kernel
+        assert lo >= forced and lo <= diag["ref_raises"] <= hi
+    else:               # the generic kernel keeps a running maximum: it never raises
+        assert diag["ref_raises"] == 0
+    assert diag["bad_picks"] == 0
+
+
+def count_raises(lg, thr):
+    """The fixed-reference rule on one workgroup's logits (heads x rows, log2
+    units, rows in list order): 32-row tiles; the first tile's maximum is each
+    head's reference; a tile whose maximum passes a reference by more than thr
+    raises every head's reference to its largest logit seen so far."""
+    ref, seen, count = None, np.full(lg.shape[0], -np.inf), 0
+    for a in range(0, lg.shape[1], 32):
+        m = lg[:, a:a + 32].max(1)
+        seen = np.maximum(seen, m)
+        if ref is None:
+            ref = m.copy()
+        elif np.any(m > ref + thr):
+            count += 1
+            ref = seen.copy()
+    return count
 
 
 def test_decode_restart_fp8_split(K):
@@ -105,7 +148,7 @@ def test_decode_restart_fp8_split(K):
     idx = np.empty((B, k), np.int32)
     for b in range(B):
         pick = rng.choice(np.arange(8, N), k, replace=False)
-        # restarts in the pool tiles near the end of the list, and in the middle
+        # raises in the pool tiles near the end of the list, and in the middle
         for pos, e, lg in ((200, 2, 12.0), (300, 3, 22.0), (505, 4, 24.0)):
             pools[b, e] = along(c, lg, D, rng)
             pick[pos] = e
@@ -121,4 +164,4 @@ def test_decode_restart_fp8_split(K):
     torch.cuda.synchronize()
     ref = O.attn(seq, tok, np.zeros(B, np.int64), S.bf16_bits(q), "bf16", wset, W, pset, "csa", idx=idx,
                  sinks=sinks, sm_scale=1 / np.sqrt(D), rope_dim=R, theta=theta)
-    assert_close(out.cpu().numpy(), ref, "bf16", "FP8 decode across softmax restarts")
+    assert_close(out.cpu().numpy(), ref, "bf16", "FP8 decode across softmax reference raises")
