@@ -534,8 +534,8 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   __shared__ float rc[32], rs[32];
   __shared__ float sk[64];   // the heads' sinks (log2 units), loaded with the setup
   __shared__ int sh_cnt[kMaxSel / 64];
-  __shared__ int rflag[3];   // overflow flags of tiles it mod 3: a flag is cleared two tiles after its last read
-  __shared__ float fsh[DSPV ? 64 : 1];   // per-head factors of a reference raise
+  __shared__ uint32_t rfl;   // DSPV: byte w = wave w raised its heads' reference in this tile
+  __shared__ float fsh[DSPV ? 64 : 1];   // the raise factors of those heads
   __shared__ __attribute__((aligned(16))) uint16_t PB[DSPV ? NW * 64 * 8 : 8];   // P^T fragments, wave-major
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -611,7 +611,6 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
 
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
   if (tid < A.H) sk[tid] = A.sinks ? A.sinks[tid] * kLog2e : -INFINITY;
-  if (tid < 3) rflag[tid] = 0;
   __syncthreads();
   // the epilogue's output row and mode, formed now and held in scalars so that
   // the epilogue does not wait for argument reloads
@@ -751,7 +750,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   // gather); its DMAs are spread over the k-steps of S^T so that their issue
   // (the texture path moves 64 B per clock per CU) overlaps the matrix cores
   auto compute = [&](const uint16_t *__restrict__ T, int tile, uint16_t *__restrict__ Tn, uint64_t idn,
-                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile, int fl) {
+                     uint8_t *__restrict__ Rn, float *__restrict__ Sn, int ntile) {
     const int base = 32 * tile;
     // FP8 rows: the next raw tile's gather is issued during this tile's
     // matrix work (its buffer is disjoint from T), one DMA per few k-steps
@@ -823,7 +822,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       __builtin_memcpy(&pf, &pw, 16);
       return psum;
     };
-    bool over = false;
+    uint32_t raised = 0;
     f16x8 pb[NHB];
     float ps[NHB];
 #pragma unroll
@@ -843,30 +842,32 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       mloc = rows_max(mloc);
       m_seen[hb] = fmaxf(m_seen[hb], mloc);
       if (m_ref[hb] == -INFINITY) m_ref[hb] = mloc;   // first tile
-      const bool ov = mloc > m_ref[hb] + kRefSlack;
-      if constexpr (!DSPV) {
-        // the wave owns its heads' whole tile: a logit more than 2^15 above the
-        // reference raises the reference to the largest logit seen, and the
-        // running sum and the accumulators follow by 2^(old - new)
-        if (__ballot(ov)) {
-          const float f = __builtin_amdgcn_exp2f(m_ref[hb] - m_seen[hb]);
-          m_ref[hb] = m_seen[hb];
-          l_run[hb] *= f;
+      // the wave owns its heads' whole tile: a logit more than 2^15 above the
+      // reference raises the reference to the largest logit seen, and the
+      // running sum and the accumulators follow by 2^(old - new) (DSPV: the
+      // accumulators of these heads are spread over every wave, so the factor
+      // goes to the others through LDS with the P^T fragment)
+      if (__ballot(mloc > m_ref[hb] + kRefSlack)) {
+        const float f = __builtin_amdgcn_exp2f(m_ref[hb] - m_seen[hb]);
+        m_ref[hb] = m_seen[hb];
+        l_run[hb] *= f;
+        if constexpr (!DSPV) {
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc_o[hb][db] = acc_o[hb][db] * f;
-          if (A.diag && lane == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
+        } else {
+          if (g == 0) fsh[16 * wv + c] = f;
+          raised = 1;
         }
-      } else {
-        over = over || ov;
+        if (A.diag && lane == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
       }
       ps[hb] = probs(hb, pb[hb]);
-      if constexpr (!DSPV) l_run[hb] += ps[hb];
+      l_run[hb] += ps[hb];
     }
     if constexpr (DSPV) {
       // every wave's P^T fragment to LDS (PB was last read before the previous
       // tile's closing barrier), then O^T[this wave's channels, all heads]
       *reinterpret_cast<f16x8 *>(PB + (wv * 64 + lane) * 8) = pb[0];
-      if (__ballot(over) && lane == 0) rflag[fl] = 1;   // raised before the barrier
+      if (lane == 0) reinterpret_cast<uint8_t *>(&rfl)[wv] = (uint8_t)raised;   // read after the barrier
       // the next tile's gather: issued where the wave would wait for the others'
       // scores anyway (its buffer was released by the previous tile's closing barrier)
       if (!FP8 && Tn) {
@@ -874,27 +875,18 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         for (int k = 0; k < RPW; ++k) dma_row(idn, k, Tn);
       }
       lds_barrier();   // P^T of every wave visible; the next tile's DMAs stay in flight
-      if (rflag[fl]) {
-        // a logit more than 2^15 above its head's reference: every head's
-        // reference rises to its largest logit seen so far, this tile's P^T is
-        // taken again, and the running sums and every wave's accumulators (all
-        // heads) scale by 2^(old - new); nothing of this tile has been summed yet
-        const float f = __builtin_amdgcn_exp2f(m_ref[0] - m_seen[0]);
-        m_ref[0] = m_seen[0];
-        l_run[0] *= f;
-        if (g == 0) fsh[16 * wv + c] = f;
-        ps[0] = probs(0, pb[0]);
-        *reinterpret_cast<f16x8 *>(PB + (wv * 64 + lane) * 8) = pb[0];
-        if (A.diag && tid == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
-        lds_barrier();   // the factors and the new P^T visible
+      // the accumulators of heads whose reference rose in this tile follow it
+      // (the flags and P^T are rewritten only after the tile's closing barrier)
+      if (const uint32_t fl = rfl) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          const float fw = fsh[16 * w + c];
+          if ((fl >> (8 * w)) & 0xffu) {
+            const float fw = fsh[16 * w + c];
 #pragma unroll
-          for (int db = 0; db < DB; ++db) acc_o[w][db] = acc_o[w][db] * fw;
+            for (int db = 0; db < DB; ++db) acc_o[w][db] = acc_o[w][db] * fw;
+          }
         }
       }
-      l_run[0] += ps[0];
       // the running sum and maximum settled here, so no probability stays live across PV
       asm volatile("" : "+v"(l_run[0]), "+v"(m_seen[0]));
       // head blocks in groups of HG (P^T fragments live: HG; V^T read NW/HG times)
@@ -973,8 +965,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
         const bool odd = it & 1;
         const bool more = tile + 1 < tile_hi;
         compute(odd ? T1 : T0, tile, more ? (odd ? T0 : T1) : nullptr, more ? tile_addr(tile + 1) : 0, nullptr,
-                nullptr, 0, it % 3);
-        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the P barrier of tile it-2
+                nullptr, 0);
         vm_wait_all();     // this wave's rows of the next tile landed ...
         __syncthreads();   // ... and every wave's; this one fully read
       }
@@ -989,8 +980,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
       lds_barrier();
       for (int tile = tile_lo; tile < tile_hi; ++tile, ++it) {
         const bool more = tile + 1 < tile_hi;
-        compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1, it % 3);
-        if (tid == 0) rflag[(it + 1) % 3] = 0;   // last read after the P barrier of tile it-2
+        compute(T0, tile, nullptr, 0, more ? RW : nullptr, RSC, tile + 1);
         vm_wait_all();     // this wave's part of raw tile+1 landed ...
         __syncthreads();   // ... and every wave's; the tile fully read
         if (more) convert(RW, RSC, T0);
@@ -1456,7 +1446,7 @@ __global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
       l_run *= f;
       if (g == 0 && rh == 0) fsh[16 * hb + c] = f;
       psum = probs();
-      if (A.diag && tid == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], 1ull);
+      if (A.diag && tid == 0) atomicAdd(&g_diag[DSV4_DIAG_REF_RAISES], (unsigned long long)NHB);   // every head block rose
       lds_barrier();   // the factors and the new P^T visible
 #pragma unroll
       for (int h = 0; h < NHB; ++h) {

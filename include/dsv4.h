@@ -255,13 +255,15 @@ int dsv4_set_batch_invariant(int32_t on);
 /* dsv4_set_diagnostics / dsv4_read_diagnostics -- a debugging aid, off by
  * default.  While on, the attention calls (dsv4_sparse_attn, dsv4_hca_attn)
  * count into process-wide counters held on each GPU:
- *   DSV4_DIAG_REF_RAISES -- times a workgroup (a wave, where waves own whole
- *       heads) raised its fixed softmax reference inside a tile because a
- *       logit passed it by more than 2^15: the reference becomes the largest
- *       logit seen, the partial sums and accumulators scale by the power of two
- *       between the two references and the tile's probabilities are taken
- *       again (the result is the same either way; the count measures the
- *       extra work, one softmax and two barriers per raise);
+ *   DSV4_DIAG_REF_RAISES -- times a block of 16 heads raised its fixed
+ *       softmax reference inside a tile because a logit passed it by more than
+ *       2^15: the block's references become their heads' largest logits seen,
+ *       the partial sums and accumulators scale by the power of two between
+ *       the two references and the tile's probabilities are taken with the new
+ *       ones (the result is the same either way; the count measures the extra
+ *       work, about one softmax of the block per raise).  The prefill kernels
+ *       raise each wave's 16 heads on their own; the FP8 decode kernel raises
+ *       every head of a workgroup together and counts each block;
  *   DSV4_DIAG_BAD_PICKS -- idx entries that are neither the -1 sentinel nor a
  *       pool entry below the sequence's count (HF DeepSeek-V4 page, "Attention
  *       mask layout": only -1 marks an unused slot); attention treats such an
