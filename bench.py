@@ -45,11 +45,12 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(summary):
-    """HBM bytes per launch of a kernel from its committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE runs scaled by a plain copy's counts),
-    or None when the summary is missing or the kernel's sources changed since
-    the counters were taken (sha256 of the listed source files)."""
+def measured_traffic(summary, key="traffic_bytes_per_launch"):
+    """HBM bytes per launch of a kernel (or of one call's kernels, `key`) from
+    its committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE runs
+    scaled by a plain copy's counts), or None when the summary is missing or
+    the kernels' sources changed since the counters were taken (sha256 of the
+    listed source files)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", summary)
     try:
@@ -59,7 +60,7 @@ def measured_traffic(summary):
             h.update(open(os.path.join(ROOT, "compressed_sparse_kv_csa_amd", "csrc", f), "rb").read())
         if h.hexdigest() != kv["source_sha256"].strip():
             return None
-        return int(float(kv["traffic_bytes_per_launch"]))
+        return int(float(kv[key]))
     except (OSError, KeyError, ValueError):
         return None
 
@@ -236,6 +237,7 @@ class CsaDecode:
     """CSA decode: 32 sequences x 1 query at 131072 tokens (32768 FP8 entries, bf16
     indexer keys, window 128, top-k 512)."""
     name = "csa_decode_B32_L131072"
+    hbm_summary = "k_attn_dec_csa_decode_B32_L131072_hbm.txt"
 
     def __init__(self, torch, K, S_, seed=1004, B=32, L=131072, H=64, D=512, R=64, W=128, Hi=64, Di=128, k=512,
                  m=4, copies=3):
@@ -308,6 +310,7 @@ class MixedDecode:
     top-k 1024, MXFP4 indexer keys/queries, FP8 KV) + one HCA layer (m'=128, 8192
     FP8 entries, dense), window 128 each."""
     name = "mixed_decode_B8_L1048576"
+    hbm_summary = "k_attn_dec_mixed_decode_B8_L1048576_hbm.txt"
 
     def __init__(self, torch, K, S_, seed=1005, B=8, L=1048576, H=64, D=512, R=64, W=128, Hi=64, Di=128, k=1024,
                  copies=3):
@@ -488,7 +491,8 @@ def decode_attn_roofline(torch, wl, reps=10):
         ms = float(np.median(t))
         out[name] = {"ms_median": round(ms, 4), "algorithmic_bytes": int(alg), "GB_per_s": round(alg / ms / 1e6, 1),
                      "frac_hbm_peak": round(alg / ms / 1e6 / PEAK_HBM, 4), "split_partial_bytes": int(part),
-                     "GB_per_s_with_partials": round((alg + part) / ms / 1e6, 1)}
+                     "GB_per_s_with_partials": round((alg + part) / ms / 1e6, 1),
+                     "traffic": measured_traffic(wl.hbm_summary, f"traffic_bytes_per_launch_{name}")}
     return {"attention": out}
 
 
@@ -834,7 +838,8 @@ def main():
         kb = wl.bytes["index_keys"]
         ach = kb / (kern_ms / 1e3) / 1e9
         rec["roofline"] = {"bound": "hbm", "kernel": "dsv4_index_topk (key scan + top-k)", "achieved": round(ach, 1),
-                           "peak": PEAK_HBM, "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4), "traffic": None,
+                           "peak": PEAK_HBM, "unit": "GB/s", "frac": round(ach / PEAK_HBM, 4),
+                           "traffic": measured_traffic(wl.hbm_summary, "traffic_bytes_per_launch_index_topk"),
                            "kernel_ms_mean": round(kern_ms, 4), "kernel_ms_events": pcts(kern_all)}
         rec["config"] = {"workload": wl.name, "bytes_per_step": wl.bytes}
         if not args.no_cpu:
