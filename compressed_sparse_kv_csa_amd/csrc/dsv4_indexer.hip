@@ -838,20 +838,30 @@ __device__ void rt_row_select(const float *scores, int64_t ld, int r, int n, int
 // keys of bin b0 are refined by two more histogram levels (the next 11 and
 // the last 10 key bits) to the exact kk-th largest key t*; then the keys above
 // t* and the first `want` keys equal to t* are written in position order.
-// The candidates are staged in LDS in position order (ck, cp: M <= 8192 of
-// each) by the caller.  Thread t holds the contiguous run of candidates
-// [t*P, t*P + P) (P >= M/256).
+// Thread t holds the contiguous run of candidates [t*P, t*P + P) (P >= M/256):
+// each one's chunk comes from a search of the offsets in LDS with no branch
+// (off[c] = M for every chunk c >= nch, so no chunk past the last is chosen
+// for i < M), and every key and position load is issued unconditionally (the
+// slot clamped into the row's range, the value dropped for i >= M), so all of
+// a thread's loads are in flight together.
 template <int P>
-__device__ void rt_cands_select(int M, int kk, uint32_t b0, uint32_t above0, uint32_t *lh, uint32_t *sh,
-                                const uint32_t *ck, const int32_t *cp, int32_t *io, float *so) {
+__device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, const uint32_t *off, int nch, int cc, int M,
+                                int kk, uint32_t b0, uint32_t above0, uint32_t *lh, uint32_t *sh, int32_t *io,
+                                float *so) {
   const int i0 = (int)threadIdx.x * P;
   uint32_t k[P];
   int32_t pos[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int i = i0 + j;
-    k[j] = i < M ? ck[i] : 0u;
-    pos[j] = i < M ? cp[i] : 0;
+    int a = 0;
+#pragma unroll
+    for (int step = kCandMaxChunks / 2; step > 0; step >>= 1) a = (int)off[a + step] <= i ? a + step : a;
+    const int sl = min(a * cc + (i - (int)off[a]), kCandSlots - 1);
+    const uint32_t kv = rk[sl];
+    const int32_t pv = rp[sl];
+    k[j] = i < M ? kv : 0u;
+    pos[j] = i < M ? pv : 0;
   }
   // level 1: the next 11 bits of the keys in bin b0
   RtThr t{b0, above0, (uint32_t)kk - above0};
@@ -903,39 +913,15 @@ __device__ void rt_cands_select(int M, int kk, uint32_t b0, uint32_t above0, uin
 
 // The picks of long row r from its candidates (or from the whole row when a
 // chunk's candidates overflowed), and the -1 tail.  Block-wide.
-constexpr int kCandSelMax = 256 * 32;   // candidates one workgroup selects from
-// The first kCandSpec candidate slots of every chunk, loaded before the chunk
-// counts are known (they arrive with them): thread t holds items t + 256 j,
-// item = chunk * kCandSpec + slot; chunks past the row's last read its last.
-constexpr int kCandSpec = 128;
-constexpr int kCandSpecPT = kCandMaxChunks * kCandSpec / 256;
-struct CandSpec {
-  uint32_t k[kCandSpecPT];
-  int32_t p[kCandSpecPT];
-};
-__device__ __forceinline__ CandSpec cand_spec_load(const uint32_t *rk, const int32_t *rp, int nch, int cc) {
-  CandSpec s;
-#pragma unroll
-  for (int j = 0; j < kCandSpecPT; ++j) {
-    const int item = (int)threadIdx.x + 256 * j;
-    const int c = min(item / kCandSpec, nch - 1), q = item % kCandSpec;
-    s.k[j] = rk[c * cc + q];
-    s.p[j] = rp[c * cc + q];
-  }
-  return s;
-}
 struct RtFinalLds {
   uint32_t soff[kCandMaxChunks + 1];
   uint32_t lh[kRtBins];
   uint32_t sh[8];
   int over;
-  uint32_t maxc;
-  uint32_t ck[kCandSelMax];
-  int32_t cp[kCandSelMax];
 };
 __device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t ld, int topk, int nch, int cc,
-                             const uint32_t *ckey, const int32_t *cpos, const uint32_t *cr, const CandSpec &spec,
-                             int32_t *idx_out, float *score_out, RtFinalLds &F) {
+                             const uint32_t *ckey, const int32_t *cpos, const uint32_t *cr, int32_t *idx_out,
+                             float *score_out, RtFinalLds &F) {
   int32_t *io = idx_out + (int64_t)r * topk;
   float *so = score_out ? score_out + (int64_t)r * topk : nullptr;
   if (kk == n) {   // everything visible is taken, in order
@@ -957,13 +943,7 @@ __device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t 
       F.soff[c] = inc - v;
       if (c == 63) F.soff[kCandMaxChunks] = inc;
       const bool over = __ballot(v > (uint32_t)cc) != 0ull;
-      uint32_t mx = v;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-      if (c == 0) {
-        F.over = over ? 1 : 0;
-        F.maxc = mx;
-      }
+      if (c == 0) F.over = over ? 1 : 0;
     }
     __syncthreads();
     const int M = (int)F.soff[kCandMaxChunks];
@@ -971,60 +951,10 @@ __device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t 
     const int32_t *rp = cpos + (int64_t)r * kCandSlots;
     const uint32_t b0 = cr[kCandMaxChunks], ab = cr[kCandMaxChunks + 1];
     // more than 8192 candidates (heavy ties at the edge): the whole-row select
-    if (F.over || M > kCandSelMax) {
-      rt_row_select(scores, ld, r, n, kk, io, so, F.lh, F.sh);
-    } else {
-      // the candidates into LDS in position order: first the preloaded slots,
-      // then (chunks holding more than kCandSpec) the rest, wave w copying
-      // chunks w, w + 4, ..., lane l their slots base + l, every load of a
-      // round issued unconditionally (slot and chunk clamped into the row's
-      // range, the value dropped past the chunk's count)
-      // (every chunk's offsets read first, with no branch between the reads:
-      // chunks past the row's last have no candidates, off = M for them)
-      int so_[kCandSpecPT], sn_[kCandSpecPT];
-#pragma unroll
-      for (int j = 0; j < kCandSpecPT; ++j) {
-        const int c = ((int)threadIdx.x + 256 * j) / kCandSpec;
-        so_[j] = (int)F.soff[c];
-        sn_[j] = (int)F.soff[c + 1];
-      }
-#pragma unroll
-      for (int j = 0; j < kCandSpecPT; ++j) {
-        const int q = ((int)threadIdx.x + 256 * j) % kCandSpec;
-        if (q < sn_[j] - so_[j]) {
-          F.ck[so_[j] + q] = spec.k[j];
-          F.cp[so_[j] + q] = spec.p[j];
-        }
-      }
-      constexpr int CW = kCandMaxChunks / 4;   // chunks per wave
-      const int wv = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
-      for (int base = kCandSpec; base < (int)F.maxc; base += 64) {
-        uint32_t kv[CW];
-        int32_t pv[CW];
-        const int kq = min(base + lane, cc - 1);
-#pragma unroll
-        for (int q = 0; q < CW; ++q) {
-          const int c = min(wv + 4 * q, nch - 1);
-          kv[q] = rk[c * cc + kq];
-          pv[q] = rp[c * cc + kq];
-        }
-#pragma unroll
-        for (int q = 0; q < CW; ++q) {
-          const int c = wv + 4 * q;
-          if (c < nch) {
-            const int o = (int)F.soff[c], cnt = (int)F.soff[c + 1] - o;
-            if (base + lane < cnt) {
-              F.ck[o + base + lane] = kv[q];
-              F.cp[o + base + lane] = pv[q];
-            }
-          }
-        }
-      }
-      __syncthreads();
-      if (M <= 256 * 8) rt_cands_select<8>(M, kk, b0, ab, F.lh, F.sh, F.ck, F.cp, io, so);
-      else if (M <= 256 * 16) rt_cands_select<16>(M, kk, b0, ab, F.lh, F.sh, F.ck, F.cp, io, so);
-      else rt_cands_select<32>(M, kk, b0, ab, F.lh, F.sh, F.ck, F.cp, io, so);
-    }
+    if (F.over || M > 256 * 32) rt_row_select(scores, ld, r, n, kk, io, so, F.lh, F.sh);
+    else if (M <= 256 * 8) rt_cands_select<8>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
+    else if (M <= 256 * 16) rt_cands_select<16>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
+    else rt_cands_select<32>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
   }
   for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
     io[j] = -1;
@@ -1100,16 +1030,10 @@ __global__ __launch_bounds__(256) void k_rt_final(const int32_t *__restrict__ se
                                                   const int32_t *__restrict__ cpos, const uint32_t *__restrict__ ccnt,
                                                   int32_t *__restrict__ idx_out, float *__restrict__ score_out) {
   __shared__ RtFinalLds F;
-  // longest rows first; with a multiple of 8 rows, in groups of eight that keep
-  // row r on the XCD that ran its candidate chunks (block r + T*c of k_rt_cand)
-  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
-  const int r = nb % 8 == 0 ? (nb / 8 - 1 - b / 8) * 8 + b % 8 : nb - 1 - b;
-  // the candidates' loads first: they are in flight during the row's count
-  // and chunk-count loads
-  const CandSpec spec = cand_spec_load(ckey + (int64_t)r * kCandSlots, cpos + (int64_t)r * kCandSlots, nch, cc);
+  const int r = gridDim.x - 1 - blockIdx.x;
   const int n = n_visible(tok[r], m, count[seq[r]]);
-  rt_final_row(r, n, min(topk, n), scores, ld, topk, nch, cc, ckey, cpos, ccnt + (int64_t)r * kCandRow, spec,
-               idx_out, score_out, F);
+  rt_final_row(r, n, min(topk, n), scores, ld, topk, nch, cc, ckey, cpos, ccnt + (int64_t)r * kCandRow, idx_out,
+               score_out, F);
 }
 
 // Scratch memory of dsv4_index_topk_noalloc (the score rows, histograms,
