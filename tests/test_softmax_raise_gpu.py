@@ -44,8 +44,8 @@ def along(c, logit, D, rng):
 
 
 @pytest.mark.parametrize("rows,H", [("f16", 64), ("bf16", 64), ("f16", 16)])
-def test_prefill_restart(K, rows, H):
-    say("prefill restart", rows, H)
+def test_prefill_raise(K, rows, H):
+    say("prefill reference raise", rows, H)
     D, R, W, theta = 512, 0, 128, 1e4     # no rope channels: logits are plain dot products
     rng = np.random.default_rng(99)
     Sx, m, k = 900, 4, 64
@@ -137,8 +137,8 @@ def count_raises(lg, thr, group=16):
     return count
 
 
-def test_decode_restart_fp8_split(K):
-    say("decode restart, FP8 rows, split")
+def test_decode_raise_fp8_split(K):
+    say("decode reference raise, FP8 rows, split")
     D, R, W, H, k, theta = 512, 64, 128, 64, 512, 1.6e5
     rng = np.random.default_rng(98)
     B, L = 3, 8000
