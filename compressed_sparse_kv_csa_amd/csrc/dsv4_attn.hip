@@ -1931,15 +1931,18 @@ int launch_attn(const dsv4_queries *q, const void *qv, int q_dtype, int H, int D
   }
   if (f16 || fp8fast) {
 #define DSV4_F16K(NW)                                                                                 \
-  if (f16 && rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, NW, false, true>), grid, dim3(NW * 64), 0, st, A); \
-  else if (f16) hipLaunchKernelGGL((k_attn_f16<1, NW, false, false>), grid, dim3(NW * 64), 0, st, A);       \
-  else if (rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, NW, true, true>), grid, dim3(NW * 64), 0, st, A); \
-  else hipLaunchKernelGGL((k_attn_f16<1, NW, true, false>), grid, dim3(NW * 64), 0, st, A);
-    switch (H) {
-    case 16: DSV4_F16K(1) break;
-    case 32: DSV4_F16K(2) break;
-    case 48: DSV4_F16K(3) break;
-    default: DSV4_F16K(4) break;
+  if (rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, NW, false, true>), grid, dim3(NW * 64), 0, st, A); \
+  else hipLaunchKernelGGL((k_attn_f16<1, NW, false, false>), grid, dim3(NW * 64), 0, st, A);
+    if (fp8fast) {   // FP8 rows with 16, 32 or 64 heads took k_attn_dec above: 48 heads
+      if (rope_dim == 64) hipLaunchKernelGGL((k_attn_f16<1, 3, true, true>), grid, dim3(3 * 64), 0, st, A);
+      else hipLaunchKernelGGL((k_attn_f16<1, 3, true, false>), grid, dim3(3 * 64), 0, st, A);
+    } else {
+      switch (H) {
+      case 16: DSV4_F16K(1) break;
+      case 32: DSV4_F16K(2) break;
+      case 48: DSV4_F16K(3) break;
+      default: DSV4_F16K(4) break;
+      }
     }
 #undef DSV4_F16K
     int rc = check_launch("k_attn_f16");
