@@ -230,7 +230,7 @@ int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *p
 
 int dsv4_rope(const void *x, int32_t x_dtype, void *y, int32_t y_dtype, int64_t n_rows, int32_t dim,
               int32_t rope_dim, const int64_t *pos, double rope_theta, int32_t inverse, hipStream_t stream) {
-  if (!x || !y || (!pos && n_rows > 0)) return fail(DSV4_EINVAL, "rope: NULL pointer");
+  if (n_rows > 0 && (!x || !y || !pos)) return fail(DSV4_EINVAL, "rope: NULL pointer");   // no rows: may be NULL
   if (n_rows < 0) return fail(DSV4_EINVAL, "rope: n_rows %lld", (long long)n_rows);
   if (dim < 2 || (dim & 1) || dim > 4096) return fail(DSV4_ENOTSUP, "rope: dim %d (even, 2..4096)", dim);
   if (rope_dim < 0 || (rope_dim & 1) || rope_dim > dim || rope_dim > 64)
@@ -256,7 +256,7 @@ static int index_topk_check(const dsv4_queries *q, const void *q_idx, const uint
                             int32_t topk, float score_scale, int32_t *idx_out, size_t *need) {
   int rc = check_queries(q);
   if (rc) return rc;
-  if (!q_idx || !w || !idx_out) return fail(DSV4_EINVAL, "index_topk: NULL tensor pointer");
+  if (q->n_rows > 0 && (!q_idx || !w || !idx_out)) return fail(DSV4_EINVAL, "index_topk: NULL tensor pointer");
   if (m < 1 || topk < 1 || topk > 2048) return fail(DSV4_EINVAL, "index_topk: m %d topk %d (1..2048)", m, topk);
   if ((rc = check_rows(k_pool, "index_topk: k_pool", head_dim))) return rc;
   if (k_pool->ring) return fail(DSV4_EINVAL, "index_topk: k_pool cannot be a ring");
@@ -273,7 +273,7 @@ static int index_topk_check(const dsv4_queries *q, const void *q_idx, const uint
     if (n_heads < 16 || n_heads > 64 || n_heads % 16 || head_dim != 128)
       return fail(DSV4_ENOTSUP, "index_topk: MXFP4 path needs n_heads in {16,32,48,64} and head_dim 128 (%d, %d)",
                   n_heads, head_dim);
-    if (!q_idx_scale) return fail(DSV4_EINVAL, "index_topk: MXFP4 queries need q_idx_scale");
+    if (q->n_rows > 0 && !q_idx_scale) return fail(DSV4_EINVAL, "index_topk: MXFP4 queries need q_idx_scale");
   } else {
     return fail(DSV4_ENOTSUP, "index_topk: query dtype %d", q_dtype);
   }
@@ -327,7 +327,7 @@ static int attn_common(const char *who, const dsv4_queries *q, const void *qv, i
                        int32_t rope_dim, double rope_theta, void *out, int32_t out_dtype) {
   int rc = check_queries(q);
   if (rc) return rc;
-  if (!qv || !out) return fail(DSV4_EINVAL, "%s: NULL q/out", who);
+  if (q->n_rows > 0 && (!qv || !out)) return fail(DSV4_EINVAL, "%s: NULL q/out", who);   // no rows: may be NULL
   if (W < 0) return fail(DSV4_EINVAL, "%s: W %d", who, W);
   if (W > 0 && (rc = check_rows(window, "window", dim))) return rc;
   if (W > 0 && !window->first_tok) return fail(DSV4_EINVAL, "%s: window rows need first_tok", who);

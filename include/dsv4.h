@@ -14,10 +14,14 @@
  *     contiguous as described per argument.  The library allocates nothing,
  *     keeps no pointer after the call returns (apart from work already queued)
  *     and holds no global state beyond its code objects, a thread-local error
- *     string, the batch-invariant switch and the static scratch array of
+ *     string, the batch-invariant and diagnostics switches, the per-GPU
+ *     diagnostic counters and the static scratch array of
  *     dsv4_index_topk_noalloc (with its per-device address).
  *   - Every call validates its arguments on the host first; a call that returns
  *     an error has launched nothing.  dsv4_last_error() describes the failure.
+ *   - A call with nothing to do (no query rows, no rows to rotate or quantise,
+ *     no entry to pool, an empty product) queues nothing and returns DSV4_OK;
+ *     its tensor pointers may then be NULL.
  *   - Work is queued on `stream` (a hipStream_t; 0 = the null stream) with no
  *     host synchronisation.  A kernel fault surfaces at the caller's next
  *     synchronisation, or as DSV4_EHIP from a later call.

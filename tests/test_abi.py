@@ -275,3 +275,30 @@ def test_index_topk_noalloc_rejects_bad_args(K):
     assert L.dsv4_index_topk_workspace(4, 1 << 21, 8) > K.NOALLOC_SCRATCH_BYTES
     assert _rc(L.dsv4_index_topk_noalloc(*args(kp=big))) == K.DSV4_EWORKSPACE
     assert "scratch" in K.dsv4_last_error()
+
+
+def test_empty_calls_queue_nothing(K):
+    """A call with nothing to do returns DSV4_OK and accepts NULL data
+    pointers (no kernel is launched, so this runs without a GPU)."""
+    L = K.lib()
+    empty_q = K.Queries(0, 1, None, None, None)
+    win = _rows(K, K.DSV4_BF16, 512, first_tok=0x1000)
+    pool = _rows(K, K.DSV4_BF16, 512)
+    assert _rc(L.dsv4_sparse_attn(ctypes.byref(empty_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
+                                  ctypes.byref(pool), None, 0, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
+                                  None)) == K.DSV4_OK
+    assert _rc(L.dsv4_hca_attn(ctypes.byref(empty_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
+                               ctypes.byref(pool), 128, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
+                               None)) == K.DSV4_OK
+    assert _rc(L.dsv4_rope(None, K.DSV4_BF16, None, K.DSV4_BF16, 0, 512, 64, None, 1.6e5, 0, None)) == K.DSV4_OK
+    assert _rc(L.dsv4_compress(None, None, K.DSV4_BF16, None, 1, 3, 512, 4, 1, 64, 1.6e5, None, None,
+                               K.DSV4_BF16, None)) == K.DSV4_OK   # seq_len < m: no entry
+    kp = _rows(K, K.DSV4_BF16, 128)
+    assert _rc(L.dsv4_index_topk(ctypes.byref(empty_q), None, None, K.DSV4_BF16, None, 64, 128, ctypes.byref(kp),
+                                 4, 512, 0.01, None, None, None, 0, None)) == K.DSV4_OK
+    # with rows to do, the same NULL pointers are errors
+    one_q = K.Queries(1, 1, 0x1000, 0x1000, None)
+    assert _rc(L.dsv4_sparse_attn(ctypes.byref(one_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
+                                  ctypes.byref(pool), None, 0, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
+                                  None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_rope(None, K.DSV4_BF16, None, K.DSV4_BF16, 4, 512, 64, None, 1.6e5, 0, None)) == K.DSV4_EINVAL
