@@ -363,10 +363,10 @@ int dsv4_sparse_attn(const dsv4_queries *q, const void *qv, int32_t q_dtype, int
                      const float *sinks, float sm_scale, int32_t rope_dim, double rope_theta, void *out,
                      int32_t out_dtype, void *ws, size_t ws_bytes, hipStream_t stream) {
   if (topk < 0 || topk > 2048) return fail(DSV4_EINVAL, "sparse_attn: topk %d (0..2048)", topk);
-  if (topk > 0 && !idx) return fail(DSV4_EINVAL, "sparse_attn: idx is NULL");
   int rc = attn_common("sparse_attn", q, qv, q_dtype, n_heads, dim, window, W, pool, topk > 0, rope_dim, rope_theta,
                        out, out_dtype);
   if (rc) return rc;
+  if (q->n_rows > 0 && topk > 0 && !idx) return fail(DSV4_EINVAL, "sparse_attn: idx is NULL");
   const int64_t max_rows = (int64_t)W + topk;
   const size_t need = attn_ws(q->n_rows, n_heads, dim, max_rows);
   if (q_dtype != DSV4_F32 && need > 0 && (!ws || ws_bytes < need))

@@ -1839,7 +1839,7 @@ int attn_nsplit(int T, int64_t max_rows) {
   const int64_t tiles = (max_rows + 31) / 32;
   // batch-invariant mode: one workgroup reduces a query's rows in one order
   if (g_batch_invariant.load(std::memory_order_relaxed)) return 1;
-  if (T >= 512 || tiles < 8) return 1;
+  if (T < 1 || T >= 512 || tiles < 8) return 1;
   int64_t want = (256 + T - 1) / T;
   const int64_t cap = tiles / 4;
   if (want > cap) want = cap;

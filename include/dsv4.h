@@ -19,9 +19,15 @@
  *     dsv4_index_topk_noalloc (with its per-device address).
  *   - Every call validates its arguments on the host first; a call that returns
  *     an error has launched nothing.  dsv4_last_error() describes the failure.
+ *   - The host checks pointers, sizes and formats, not the contents of device
+ *     arrays (seq, tok, pos0, count, first_tok, picks): a pick outside
+ *     [0, count[b]) is a masked row (-1 is the sentinel; the diagnostics count
+ *     the others), and every other value must lie in its documented range, or
+ *     the kernels may read outside the caller's buffers.
  *   - A call with nothing to do (no query rows, no rows to rotate or quantise,
  *     no entry to pool, an empty product) queues nothing and returns DSV4_OK;
- *     its tensor pointers may then be NULL.
+ *     its tensor pointers may then be NULL (the row descriptors and scalar
+ *     arguments are still checked).
  *   - Work is queued on `stream` (a hipStream_t; 0 = the null stream) with no
  *     host synchronisation.  A kernel fault surfaces at the caller's next
  *     synchronisation, or as DSV4_EHIP from a later call.

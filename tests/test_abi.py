@@ -134,6 +134,7 @@ def test_attention_rejects_bad_args(K):
 def test_workspace_sizes(K):
     L = K.lib()
     assert L.dsv4_attn_workspace(8192, 64, 512, 640) == 0          # prefill: no split partials
+    assert L.dsv4_attn_workspace(0, 64, 512, 640) == 0             # no query rows
     assert L.dsv4_attn_workspace(8, 64, 512, 8320) > 8 * 64 * 512 * 4
     assert L.dsv4_index_topk_workspace(8, 262144, 1024) >= 8 * 262144 * 4
 
@@ -287,6 +288,9 @@ def test_empty_calls_queue_nothing(K):
     assert _rc(L.dsv4_sparse_attn(ctypes.byref(empty_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
                                   ctypes.byref(pool), None, 0, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
                                   None)) == K.DSV4_OK
+    assert _rc(L.dsv4_sparse_attn(ctypes.byref(empty_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
+                                  ctypes.byref(pool), None, 512, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
+                                  None)) == K.DSV4_OK   # picks expected, no idx: nothing to pick for
     assert _rc(L.dsv4_hca_attn(ctypes.byref(empty_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
                                ctypes.byref(pool), 128, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
                                None)) == K.DSV4_OK
@@ -301,4 +305,7 @@ def test_empty_calls_queue_nothing(K):
     assert _rc(L.dsv4_sparse_attn(ctypes.byref(one_q), None, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
                                   ctypes.byref(pool), None, 0, None, 0.04, 64, 1.6e5, None, K.DSV4_BF16, None, 0,
                                   None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_sparse_attn(ctypes.byref(one_q), 0x1000, K.DSV4_BF16, 64, 512, ctypes.byref(win), 128,
+                                  ctypes.byref(pool), None, 512, None, 0.04, 64, 1.6e5, 0x1000, K.DSV4_BF16, None, 0,
+                                  None)) == K.DSV4_EINVAL   # picks expected, idx NULL
     assert _rc(L.dsv4_rope(None, K.DSV4_BF16, None, K.DSV4_BF16, 4, 512, 64, None, 1.6e5, 0, None)) == K.DSV4_EINVAL
