@@ -214,6 +214,7 @@ int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *p
                   int32_t seq_len, int32_t dim, int32_t m, int32_t overlap, int32_t rope_dim, double rope_theta,
                   const int64_t *pos0, void *pool, int32_t out_dtype, hipStream_t stream) {
   if (n_seq < 0 || seq_len < 0 || m < 1) return fail(DSV4_EINVAL, "compress: n_seq %d seq_len %d m %d", n_seq, seq_len, m);
+  if (n_seq > 65535) return fail(DSV4_ENOTSUP, "compress: n_seq %d (at most 65535)", n_seq);
   const bool empty = n_seq == 0 || seq_len / m == 0;   // nothing to pool: pointers may be NULL
   if (!empty && (!c || !z || !pos_bias || !pool)) return fail(DSV4_EINVAL, "compress: NULL tensor pointer");
   if (dim < 2 || (dim & 1) || dim > 4096) return fail(DSV4_ENOTSUP, "compress: dim %d (even, 2..4096)", dim);
@@ -278,7 +279,7 @@ static int index_topk_check(const dsv4_queries *q, const void *q_idx, const uint
     return fail(DSV4_ENOTSUP, "index_topk: query dtype %d", q_dtype);
   }
   if (!index_topk_supported(k_pool->seq_stride, topk))
-    return fail(DSV4_ENOTSUP, "index_topk: pool stride %lld (at most 65535 chunks of 4096 entries)",
+    return fail(DSV4_ENOTSUP, "index_topk: pool stride %lld (at most 65535 * 1024 entries)",
                 (long long)k_pool->seq_stride);
   *need = index_topk_ws(q->n_rows, k_pool->seq_stride, topk);
   return DSV4_OK;

@@ -1119,8 +1119,10 @@ size_t index_topk_ws(int64_t n_rows, int64_t stride, int topk) {
 }
 
 int index_topk_supported(int64_t stride, int topk) {
-  // grid.y of the radix passes holds the chunks of a row
-  return (stride + kRtChunk - 1) / kRtChunk <= 65535 && topk >= 1;
+  // grid.y holds a row's chunks: 1024-entry chunks of the fp32 scoring kernel
+  // (the most of any pass: the radix passes take 4096, the MFMA scans at least
+  // 31 * 128 entries per workgroup)
+  return (stride + 1023) / 1024 <= 65535 && topk >= 1;
 }
 
 // Workgroups of `kernel` (`block` threads, no dynamic LDS) that the current

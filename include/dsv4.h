@@ -119,7 +119,7 @@ typedef struct {
  *   c, z     : [n_seq, seq_len, dim], in_dtype DSV4_F32 or DSV4_BF16
  *   pos_bias : [2m or m, dim] float32
  *   pool     : [n_seq, seq_len / m, dim], out_dtype DSV4_F32, DSV4_BF16 or DSV4_F16
- * Partial trailing windows are not pooled.  dim even, <= 4096. */
+ * Partial trailing windows are not pooled.  dim even, <= 4096; n_seq <= 65535. */
 int dsv4_compress(const void *c, const void *z, int32_t in_dtype, const float *pos_bias,
                   int32_t n_seq, int32_t seq_len, int32_t dim, int32_t m, int32_t overlap,
                   int32_t rope_dim, double rope_theta, const int64_t *pos0, void *pool,
@@ -154,7 +154,7 @@ int dsv4_rope(const void *x, int32_t x_dtype, void *y, int32_t y_dtype, int64_t 
  *   score_out   : [T, topk] float32 scores of the picks (or -inf), may be NULL
  *   ws          : scratch of at least dsv4_index_topk_workspace(...) bytes
  * Supported: head_dim 128 (bf16: multiple of 32), n_heads multiple of 16 and
- * <= 64, 1 <= topk <= 2048, m >= 1, pool_seq_stride <= 65535 * 4096. */
+ * <= 64, 1 <= topk <= 2048, m >= 1, pool_seq_stride <= 65535 * 1024. */
 size_t dsv4_index_topk_workspace(int32_t n_rows, int64_t pool_seq_stride, int32_t topk);
 int dsv4_index_topk(const dsv4_queries *q, const void *q_idx, const uint8_t *q_idx_scale,
                     int32_t q_dtype, const float *w, int32_t n_heads, int32_t head_dim,

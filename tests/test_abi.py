@@ -53,6 +53,7 @@ def test_compress_rejects_bad_args(K):
     assert _rc(L.dsv4_compress(fake, fake, 1, fake, 1, 8, 8, 0, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_EINVAL
     assert _rc(L.dsv4_compress(fake, fake, 7, fake, 1, 8, 8, 4, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_ENOTSUP
     assert _rc(L.dsv4_compress(fake, fake, 1, fake, 1, 8, 8, 4, 1, 3, 1e4, None, fake, 1, None)) == K.DSV4_EINVAL
+    assert _rc(L.dsv4_compress(fake, fake, 1, fake, 65536, 8, 8, 4, 1, 0, 1e4, None, fake, 1, None)) == K.DSV4_ENOTSUP
 
 
 def test_rope_rejects_bad_args(K):
@@ -100,8 +101,9 @@ def test_index_topk_rejects_bad_args(K):
     assert _rc(L.dsv4_index_topk(*args(qdt=K.DSV4_MXFP4, kp=_rows(K, K.DSV4_MXFP4, 128)))) == K.DSV4_EINVAL
     bad_q = K.Queries(4, 0, fake.value, fake.value, None)
     assert _rc(L.dsv4_index_topk(*args(q=bad_q))) == K.DSV4_EINVAL
-    huge = _rows(K, K.DSV4_BF16, 128, seq_stride=1 << 29)   # more than 65535 chunks of 4096 entries
-    assert _rc(L.dsv4_index_topk(*args(kp=huge, k=2048, ws=fake, wsb=1 << 62))) == K.DSV4_ENOTSUP
+    for stride in (1 << 29, 65535 * 1024 + 1):   # more than 65535 * 1024 entries per sequence
+        huge = _rows(K, K.DSV4_BF16, 128, seq_stride=stride)
+        assert _rc(L.dsv4_index_topk(*args(kp=huge, k=2048, ws=fake, wsb=1 << 62))) == K.DSV4_ENOTSUP
 
 
 def test_attention_rejects_bad_args(K):
