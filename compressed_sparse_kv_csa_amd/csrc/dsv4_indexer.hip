@@ -336,6 +336,10 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
       for (int qq = 0; qq < QPW; ++qq)
 #pragma unroll
         for (int eb = 0; eb < 4; ++eb) sacc[qq][eb] = rows_sum(sacc[qq][eb]);
+      // the next tile into LDS before this tile's scores go out: the wait for
+      // the staged key loads then leaves the score stores in flight (vmcnt
+      // counts stores and loads in issue order; 151 -> 144 us at S = 8192)
+      if (tile + 1 < ntile) store(buf ^ 1, stg);
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
         if (!mine[qq] || g != 0) continue;
@@ -345,7 +349,6 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
           if (e < nq[qq]) scores[(int64_t)(r0 + QPW * wv + qq) * ld + e] = sacc[qq][eb] * scale;
         }
       }
-      if (tile + 1 < ntile) store(buf ^ 1, stg);
       __syncthreads();
     }
   }
