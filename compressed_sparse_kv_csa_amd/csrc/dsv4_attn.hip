@@ -85,35 +85,46 @@ constexpr int kMaxSel = 2048;
 // Rows of one query: window part [0, nwin) then pool part.
 struct RowPlan {
   int b, t, nwin, nsel, wlo;
+  int pcount;   // the sequence's pool entries (0 without a pool)
   int64_t p;
 };
 
+// read in place of absent per-sequence arrays (never written)
+__device__ int32_t kZeroI32[1];
+__device__ int64_t kZeroI64[1];
+
+// The plan's loads go out in two rounds: the row's (sequence, token), then the
+// sequence's pos0, window first token and count, and pool count.  An absent
+// array reads a zero stand-in, so that no load waits behind a branch on an
+// argument (each such branch cost a scalar round trip).
 __device__ __forceinline__ RowPlan row_plan(const AttnArgs &A, int r) {
+  const int b = A.seq[r];
+  const int t = A.tok[r];
+  const bool win = A.W > 0, pool = A.pool.data != nullptr;
+  const int64_t p0 = *(A.pos0 ? A.pos0 + b : kZeroI64);
+  const int ft = *(win && A.win.first_tok ? A.win.first_tok + b : kZeroI32);
+  const int wc = *(win ? A.win.count + b : kZeroI32);
+  const int pc = *(pool ? A.pool.count + b : kZeroI32);
+  // every value needed here: the compiler would otherwise sink each load into
+  // the branch that uses it, one round trip after another (r is uniform, so
+  // are they)
+  asm volatile("" ::"s"(t), "s"(p0), "s"(ft), "s"(wc), "s"(pc));
   RowPlan P;
-  P.b = A.seq[r];
-  P.t = A.tok[r];
-  P.p = (A.pos0 ? A.pos0[P.b] : 0) + P.t;
+  P.b = b;
+  P.t = t;
+  P.p = p0 + t;
+  P.pcount = pc;
   P.nwin = 0;
   P.wlo = 0;
-  if (A.W > 0) {
-    const int ft = A.win.first_tok ? A.win.first_tok[P.b] : 0;
-    const int wc = A.win.count[P.b];
-    int lo = P.t - A.W + 1;
-    lo = lo < ft ? ft : lo;
-    lo = lo < 0 ? 0 : lo;
-    int hi = P.t;
-    hi = hi > ft + wc - 1 ? ft + wc - 1 : hi;
+  if (win) {
+    const int lo = max(max(t - A.W + 1, ft), 0);
+    const int hi = min(t, ft + wc - 1);
     // storage row of the first window token; the rows of the later ones
     // follow it, wrapping at the stride (only a ring ever wraps)
     P.wlo = A.win.ring ? (int)(lo % A.win.stride) : lo - ft;
     P.nwin = hi >= lo ? hi - lo + 1 : 0;
   }
-  P.nsel = 0;
-  if (!A.csa && A.pool.data) {
-    const int n = (P.t + 1) / A.m;
-    const int c = A.pool.count[P.b];
-    P.nsel = n < c ? n : c;
-  }
+  P.nsel = !A.csa && pool ? min((t + 1) / A.m, pc) : 0;
   return P;
 }
 
@@ -144,11 +155,10 @@ __device__ __forceinline__ IdxPre<NT> load_idx(const AttnArgs &A, int r) {
 // preserving order.  Block-wide, one barrier; returns the count (sel[] is
 // visible after the caller's next barrier).  sh_cnt holds kMaxSel/64 ints.
 template <int NT>
-__device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int b, int *sel, int *sh_cnt,
+__device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int cnt, int *sel, int *sh_cnt,
                            bool count_bad = false) {
   constexpr int NWV = NT / 64, PER = kMaxSel / NT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int cnt = A.pool.count[b];
   const int nq = (A.topk + NT - 1) / NT;
   if (A.diag && count_bad) {   // entries past the row's end load as -1
     unsigned long long nb = 0;
@@ -178,8 +188,8 @@ __device__ int compact_idx(const AttnArgs &A, const IdxPre<NT> &pre, int b, int 
   return total;
 }
 template <int NT>
-__device__ int compact_idx(const AttnArgs &A, int r, int b, int *sel, int *sh_cnt, bool count_bad = false) {
-  return compact_idx<NT>(A, load_idx<NT>(A, r), b, sel, sh_cnt, count_bad);
+__device__ int compact_idx(const AttnArgs &A, int r, int cnt, int *sel, int *sh_cnt, bool count_bad = false) {
+  return compact_idx<NT>(A, load_idx<NT>(A, r), cnt, sel, sh_cnt, count_bad);
 }
 
 // storage row (within its sequence) of window row i of a query
@@ -249,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs A) {
     for (int j = 0; j < NJ; ++j) qb[j] = *reinterpret_cast<const f16x8 *>(qr + 32 * j);
   }
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.b, sel, sh_cnt, blockIdx.x % A.nsplit == 0);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<NT>(A, r, P.pcount, sel, sh_cnt, blockIdx.x % A.nsplit == 0);
   const int nrows = P.nwin + P.nsel;
   const int ntiles = (nrows + 31) / 32;
   const int tps = (ntiles + A.nsplit - 1) / A.nsplit;
@@ -601,7 +611,7 @@ __global__ __launch_bounds__(NW * 64, FP8 ? 1 : 2) void k_attn_f16(AttnArgs A) {
   const bool early = !FP8 && A.nsplit == 1 && (csa ? nwin >= 32 : nrows > 0);
   if (early) gather(0, T0);
   if (csa && A.topk > 0) {
-    P.nsel = compact_idx<NT>(A, ipre, P.b, sel, sh_cnt, split == 0);
+    P.nsel = compact_idx<NT>(A, ipre, P.pcount, sel, sh_cnt, split == 0);
     nrows = nwin + P.nsel;
   }
   const int ntiles = (nrows + 31) / 32;
@@ -1217,7 +1227,7 @@ __global__ __launch_bounds__(128 * NHB, 1) void k_attn_dec(AttnArgs A) {
   RowPlan P = row_plan(A, r);
   const int R = R64 ? 64 : A.rope_dim;
   const int nwin = P.nwin, csa = A.csa;
-  const int pcount = A.pool.data ? A.pool.count[P.b] : 0;
+  const int pcount = P.pcount;
   // nominal row list: window rows, then every pick slot (CSA) or the visible entries (HCA)
   const int nrows = nwin + (csa ? A.topk : P.nsel);
   const int ntiles = (nrows + 31) / 32;
@@ -1675,7 +1685,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(AttnArgs A, int D) {
   const int tid = threadIdx.x;
   const int r = blockIdx.x;
   RowPlan P = row_plan(A, r);
-  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.b, sel, sh_cnt, true);
+  if (A.csa && A.topk > 0) P.nsel = compact_idx<256>(A, r, P.pcount, sel, sh_cnt, true);
   const int nrows = P.nwin + P.nsel;
   const int R = A.rope_dim;
   if (tid < R / 2) rope_cs_f((double)P.p, A.inv_freq[tid], 1.f, &rc[tid], &rs[tid]);
