@@ -835,93 +835,119 @@ __device__ void rt_row_select(const float *scores, int64_t ld, int r, int n, int
   }
 }
 
+constexpr int kRtMapWords = 256;   // bitmap words over at most 8192 candidates
+struct RtFinalLds {
+  uint32_t soff[kCandMaxChunks + 1];
+  uint32_t lh[kRtBins];
+  uint32_t bm[2][kRtMapWords];   // candidate bitmaps in position order: keys equal to t*, picks
+  uint32_t wpre[kRtMapWords];    // exclusive prefix popcount per bitmap word
+  uint32_t sh[8];
+  int over;
+};
+
+// bm[0, nw) -> wpre (nw <= 256 words); ends with a barrier
+__device__ __forceinline__ void rt_word_prefix(const uint32_t *bm, uint32_t *wpre, int nw, uint32_t *sh4) {
+  const int w = (int)threadIdx.x;
+  const uint32_t c = w < nw ? (uint32_t)__popc(bm[w]) : 0u;
+  uint32_t tot;
+  const uint32_t run = tk_scan(c, sh4, &tot);
+  if (w < nw) wpre[w] = run;
+  __syncthreads();
+}
+
 // The kk largest of the row's M candidates (candidate i in position order is
 // slot c*cc + (i - off[c]) of the chunk c with off[c] <= i < off[c + 1]).
 // Every candidate above the level-0 bin b0 is taken (`above` of them); the
 // keys of bin b0 are refined by two more histogram levels (the next 11 and
 // the last 10 key bits) to the exact kk-th largest key t*; then the keys above
 // t* and the first `want` keys equal to t* are written in position order.
-// Thread t holds the contiguous run of candidates [t*P, t*P + P) (P >= M/256):
-// each one's chunk comes from a search of the offsets in LDS with no branch
-// (off[c] = M for every chunk c >= nch, so no chunk past the last is chosen
-// for i < M), and every key and position load is issued unconditionally (the
-// slot clamped into the row's range, the value dropped for i >= M), so all of
-// a thread's loads are in flight together.
+// Candidate i (the row's candidates concatenated chunk by chunk, which is
+// position order) goes to thread i mod 256, so each wave's key and position
+// loads read consecutive slots; its chunk comes from a search of the offsets
+// in LDS with no branch (off[c] = M for every chunk c >= nch), and every load
+// is issued unconditionally (the slot clamped into the row's range, the value
+// dropped for i >= M).  Output slots come from bitmaps over i and their
+// prefix popcounts: the picks', and (only when t* has more equal keys than
+// are wanted) the equal keys' to rank them.
 template <int P>
-__device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, const uint32_t *off, int nch, int cc, int M,
-                                int kk, uint32_t b0, uint32_t above0, uint32_t *lh, uint32_t *sh, int32_t *io,
-                                float *so) {
-  const int i0 = (int)threadIdx.x * P;
+__device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, int nch, int cc, int M, int kk, uint32_t b0,
+                                uint32_t above0, RtFinalLds &F, int32_t *io, float *so) {
+  const int tid = (int)threadIdx.x;
   uint32_t k[P];
   int32_t pos[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    const int i = i0 + j;
+    const int i = tid + 256 * j;
     int a = 0;
 #pragma unroll
-    for (int step = kCandMaxChunks / 2; step > 0; step >>= 1) a = (int)off[a + step] <= i ? a + step : a;
-    const int sl = min(a * cc + (i - (int)off[a]), kCandSlots - 1);
+    for (int step = kCandMaxChunks / 2; step > 0; step >>= 1) a = (int)F.soff[a + step] <= i ? a + step : a;
+    const int sl = min(a * cc + (i - (int)F.soff[a]), kCandSlots - 1);
     const uint32_t kv = rk[sl];
     const int32_t pv = rp[sl];
     k[j] = i < M ? kv : 0u;
     pos[j] = i < M ? pv : 0;
   }
-  // level 1: the next 11 bits of the keys in bin b0
+  // level 1: the next 11 bits of the keys in bin b0 (the bitmaps cleared alongside)
   RtThr t{b0, above0, (uint32_t)kk - above0};
-  for (int i = threadIdx.x; i < kRtBins; i += 256) lh[i] = 0u;
+  for (int i = tid; i < kRtBins; i += 256) F.lh[i] = 0u;
+  for (int i = tid; i < 2 * kRtMapWords; i += 256) (&F.bm[0][0])[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < P; ++j)
-    if (k[j] && (k[j] >> 21) == b0) atomicAdd(&lh[(k[j] >> 10) & 2047u], 1u);
+    if (k[j] && (k[j] >> 21) == b0) atomicAdd(&F.lh[(k[j] >> 10) & 2047u], 1u);
   __syncthreads();
-  t = rt_next(lh, kRtBins, 11, t, sh);
+  t = rt_next(F.lh, kRtBins, 11, t, F.sh);
   // level 2: the last 10 bits of the keys under that 22-bit prefix
-  for (int i = threadIdx.x; i < 1024; i += 256) lh[i] = 0u;
+  for (int i = tid; i < 1024; i += 256) F.lh[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < P; ++j)
-    if (k[j] && (k[j] >> 10) == t.prefix) atomicAdd(&lh[k[j] & 1023u], 1u);
+    if (k[j] && (k[j] >> 10) == t.prefix) atomicAdd(&F.lh[k[j] & 1023u], 1u);
   __syncthreads();
-  t = rt_next(lh, 1024, 10, t, sh);
+  t = rt_next(F.lh, 1024, 10, t, F.sh);
   const uint32_t tstar = t.prefix, quota = t.want;
-  // ordered emission: equal keys ranked in position order, then output slots
-  uint32_t ne = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) ne += k[j] == tstar ? 1u : 0u;
-  uint32_t tot;
-  uint32_t er = tk_scan(ne, sh, &tot);
-  __syncthreads();
-  uint32_t ns = 0;
+  const uint32_t neq = F.lh[tstar & 1023u];   // every key equal to t* was counted in its level-2 bin
+  const int nw = (M + 31) / 32;
   uint64_t pick = 0ull;
+  if (neq > quota) {   // ties at t*: the equal keys lowest in position order
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int i = tid + 256 * j;
+      if (k[j] == tstar) atomicOr(&F.bm[0][i >> 5], 1u << (i & 31));
+    }
+    __syncthreads();
+    rt_word_prefix(F.bm[0], F.wpre, nw, F.sh);
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int i = tid + 256 * j, w = i >> 5;
+      if (k[j] == tstar && F.wpre[w] + __popc(F.bm[0][w] & ((1u << (i & 31)) - 1u)) < quota) pick |= 1ull << j;
+    }
+    __syncthreads();   // F.wpre is rewritten below
+  } else {
+#pragma unroll
+    for (int j = 0; j < P; ++j) pick |= k[j] == tstar ? 1ull << j : 0ull;
+  }
 #pragma unroll
   for (int j = 0; j < P; ++j) {
-    bool p = k[j] > tstar;
-    if (k[j] == tstar) {
-      p = er < quota;
-      ++er;
-    }
-    pick |= p ? 1ull << j : 0ull;
-    ns += p ? 1u : 0u;
+    const int i = tid + 256 * j;
+    if (k[j] > tstar) pick |= 1ull << j;
+    if ((pick >> j) & 1ull) atomicOr(&F.bm[1][i >> 5], 1u << (i & 31));
   }
-  uint32_t slot = tk_scan(ns, sh, &tot);
   __syncthreads();
+  rt_word_prefix(F.bm[1], F.wpre, nw, F.sh);
 #pragma unroll
   for (int j = 0; j < P; ++j)
     if ((pick >> j) & 1ull) {
+      const int i = tid + 256 * j, w = i >> 5;
+      const uint32_t slot = F.wpre[w] + __popc(F.bm[1][w] & ((1u << (i & 31)) - 1u));
       io[slot] = pos[j];
       if (so) so[slot] = keyf(k[j]);
-      ++slot;
     }
 }
 
 // The picks of long row r from its candidates (or from the whole row when a
 // chunk's candidates overflowed), and the -1 tail.  Block-wide.
-struct RtFinalLds {
-  uint32_t soff[kCandMaxChunks + 1];
-  uint32_t lh[kRtBins];
-  uint32_t sh[8];
-  int over;
-};
+
 __device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t ld, int topk, int nch, int cc,
                              const uint32_t *ckey, const int32_t *cpos, const uint32_t *cr, int32_t *idx_out,
                              float *score_out, RtFinalLds &F) {
@@ -955,9 +981,9 @@ __device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t 
     const uint32_t b0 = cr[kCandMaxChunks], ab = cr[kCandMaxChunks + 1];
     // more than 8192 candidates (heavy ties at the edge): the whole-row select
     if (F.over || M > 256 * 32) rt_row_select(scores, ld, r, n, kk, io, so, F.lh, F.sh);
-    else if (M <= 256 * 8) rt_cands_select<8>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
-    else if (M <= 256 * 16) rt_cands_select<16>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
-    else rt_cands_select<32>(rk, rp, F.soff, nch, cc, M, kk, b0, ab, F.lh, F.sh, io, so);
+    else if (M <= 256 * 8) rt_cands_select<8>(rk, rp, nch, cc, M, kk, b0, ab, F, io, so);
+    else if (M <= 256 * 16) rt_cands_select<16>(rk, rp, nch, cc, M, kk, b0, ab, F, io, so);
+    else rt_cands_select<32>(rk, rp, nch, cc, M, kk, b0, ab, F, io, so);
   }
   for (int j = kk + (int)threadIdx.x; j < topk; j += 256) {
     io[j] = -1;
