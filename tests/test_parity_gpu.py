@@ -99,6 +99,36 @@ def test_rope(K, store, D, R, theta):
         assert_close(goth.float().cpu().numpy(), ref, "bf16", f"rope f16 out inv={inv}")
 
 
+@pytest.mark.parametrize("store,D,R,n,offset", [
+    ("f32", 6, 4, 70000, 0),      # a width that is not a multiple of 8, rows over two launches
+    ("bf16", 30, 16, 1000, 0),
+    ("bf16", 64, 64, 1000, 1),    # the input 2 bytes off 16-byte alignment
+])
+def test_rope_per_pair_path(K, store, D, R, n, offset):
+    """Rows the eight-channel kernel does not take (width not a multiple of 8,
+    or unaligned rows) go through the one-pair-per-thread kernel, whose launches
+    hold at most 65535 rows each."""
+    say("rope per-pair path", store, D, R, n, offset)
+    rng = np.random.default_rng(9)
+    theta = 1e4
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    if store == "bf16":
+        x = S.bf16_to_f32(S.bf16_bits(x))
+    pos = rng.integers(0, 2 ** 20, n).astype(np.int64)
+    xt = tensor_of(x, store)
+    if offset:
+        buf = torch.empty(n * D + offset, dtype=xt.dtype, device="cuda")
+        view = buf[offset:offset + n * D].view(n, D)
+        view.copy_(xt)
+        xt = view
+        assert xt.data_ptr() % 16 != 0
+    for inv in (False, True):
+        ref = O.rope(x, pos, R, theta, -1 if inv else +1)
+        got = K.dsv4_rope(xt, dev(pos), R, theta, inverse=inv)
+        torch.cuda.synchronize()
+        assert_close(got.float().cpu().numpy(), ref, "f32" if store == "f32" else "bf16", f"rope inv={inv}")
+
+
 # --------------------------------------------------------------------------- indexer + top-k
 def _prefill_indexer_case(store, B, Sx, Hi, Di, m, k, seed):
     rng = np.random.default_rng(seed)
