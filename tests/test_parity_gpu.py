@@ -63,13 +63,13 @@ def test_compress(K, store, B, Sx, D, m, overlap, R, theta):
                           pos0=dev(pos0), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert_close(got.cpu().numpy(), ref, store, "compress")
-    if store == "bf16":   # bf16 / fp16 output paths round once more
-        got16 = K.dsv4_compress(tensor_of(c, store), tensor_of(z, store), dev(bias), m, overlap, R, theta,
-                                pos0=dev(pos0))
-        assert_close(got16.float().cpu().numpy(), ref, store, "compress bf16 out")
-        goth = K.dsv4_compress(tensor_of(c, store), tensor_of(z, store), dev(bias), m, overlap, R, theta,
-                               pos0=dev(pos0), out_dtype=torch.float16)
-        assert_close(goth.float().cpu().numpy(), ref, store, "compress f16 out")
+    # bf16 / fp16 outputs (every input type) round once more
+    got16 = K.dsv4_compress(tensor_of(c, store), tensor_of(z, store), dev(bias), m, overlap, R, theta,
+                            pos0=dev(pos0), out_dtype=torch.bfloat16)
+    assert_close(got16.float().cpu().numpy(), ref, "bf16", "compress bf16 out")
+    goth = K.dsv4_compress(tensor_of(c, store), tensor_of(z, store), dev(bias), m, overlap, R, theta,
+                           pos0=dev(pos0), out_dtype=torch.float16)
+    assert_close(goth.float().cpu().numpy(), ref, "bf16", "compress f16 out")
 
 
 def test_compress_empty_and_short(K):
@@ -97,6 +97,9 @@ def test_rope(K, store, D, R, theta):
         assert_close(got.float().cpu().numpy(), ref, tol_store, f"rope inv={inv}")
         goth = K.dsv4_rope(tensor_of(x, store), dev(pos), R, theta, inverse=inv, out_dtype=torch.float16)
         assert_close(goth.float().cpu().numpy(), ref, "bf16", f"rope f16 out inv={inv}")
+        if store == "f32":
+            gotb = K.dsv4_rope(tensor_of(x, store), dev(pos), R, theta, inverse=inv, out_dtype=torch.bfloat16)
+            assert_close(gotb.float().cpu().numpy(), ref, "bf16", f"rope bf16 out inv={inv}")
 
 
 @pytest.mark.parametrize("store,D,R,n,offset", [
