@@ -176,19 +176,24 @@ def test_index_topk_prefill(K, store, B, Sx, Hi, Di, m, k):
         assert np.allclose(sc[r, :len(p)], ref[r, p], rtol=1e-4, atol=1e-5)
 
 
-@pytest.mark.parametrize("kind,B,L,k", [
-    ("bf16", 3, [1000, 40001, 20050], 512),
-    ("mxfp4", 2, [70000, 5003], 1024),
-    ("bf16", 2, [20000, 9], 2048),
-    ("mxfp4", 1, [4 * 16384 + 7], 1),
+@pytest.mark.parametrize("kind,B,L,k,Hi,Di", [
+    ("bf16", 3, [1000, 40001, 20050], 512, 64, 128),
+    ("mxfp4", 2, [70000, 5003], 1024, 64, 128),
+    ("bf16", 2, [20000, 9], 2048, 64, 128),
+    ("mxfp4", 1, [4 * 16384 + 7], 1, 64, 128),
     # rows longer than one workgroup's select: the radix-threshold passes over
     # 4096-entry chunks, next to rows that take every entry or have none
-    ("bf16", 3, [4 * 20000, 4 * 300, 3], 2048),
-    ("bf16", 1, [4 * 200000], 2048),
+    ("bf16", 3, [4 * 20000, 4 * 300, 3], 2048, 64, 128),
+    ("bf16", 1, [4 * 200000], 2048, 64, 128),
+    # the other indexer head counts and head dims of the scan
+    ("mxfp4", 2, [30000, 4001], 512, 16, 128),
+    ("mxfp4", 2, [30000, 4001], 512, 48, 128),
+    ("bf16", 2, [30000, 4001], 512, 32, 96),
+    ("bf16", 2, [30000, 4001], 512, 48, 32),
 ])
-def test_index_topk_decode(K, kind, B, L, k):
-    say("index_topk decode", kind, B, L, k)
-    layer = S.decode_layer(31 + B, "csa", B, L, topk=k, idx_kind=kind)
+def test_index_topk_decode(K, kind, B, L, k, Hi, Di):
+    say("index_topk decode", kind, B, L, k, Hi, Di)
+    layer = S.decode_layer(31 + B, "csa", B, L, topk=k, idx_kind=kind, Hi=Hi, Di=Di)
     kp = layer.kpool
     tok = layer.tok
     seq = np.arange(B, dtype=np.int32)
