@@ -330,6 +330,46 @@ def test_sparse_attn_prefill_rope_out(K, B, R, out):
     assert_close(got.float().cpu().numpy(), ref, "bf16", f"sparse_attn R={R} out={out}")
 
 
+@pytest.mark.parametrize("H,rows", [(16, "f16"), (32, "f16"), (48, "f16"), (16, "fp8r"), (32, "fp8r"), (48, "fp8r")])
+def test_attn_rope32_every_head_count(K, H, rows):
+    """Each head count's kernel instance with a rope width other than 64 (a
+    run-time width): fp16 prefill rows and FP8 decode rows (64 bf16 tail
+    channels, the last 32 of them rotated)."""
+    say("attention rope 32", H, rows)
+    D, R, theta = 512, 32, 1.6e5
+    if rows == "f16":
+        B, Sx, W, m, k = 1, 300, 128, 4, 64
+        q, win, pool, sinks, pos0 = _attn_prefill_inputs(B, Sx, H, D, R, W, m, theta, 80 + H, rows="f16")
+        rng = np.random.default_rng(81)
+        N = Sx // m
+        seq = np.zeros(Sx, np.int32)
+        tok = np.arange(Sx, dtype=np.int32)
+        nv = O.n_visible(tok, m, np.full(Sx, N))
+        idx = O.topk(np.where(np.arange(N)[None] < nv[:, None], rng.standard_normal((Sx, N)), -np.inf), nv, k)
+        qs = S.bf16_bits(q.reshape(Sx, H, D))
+        ref = O.attn(seq, tok, pos0, qs, "bf16", win, W, pool, "csa", idx=idx, sinks=sinks,
+                     sm_scale=1 / np.sqrt(D), rope_dim=R, theta=theta)
+        Q = K.QueryRows(dev(seq), dev(tok), dev(pos0), B)
+        out = K.dsv4_sparse_attn(Q, tensor_of(q.reshape(Sx, H, D), "bf16"), upload_rows(win), W, upload_rows(pool),
+                                 dev(idx), dev(sinks), 1 / np.sqrt(D), R, theta, out_dtype=torch.float32)
+    else:
+        B, L, k = 2, [5000, 2222], 256
+        layer = S.decode_layer(82 + H, "csa", B, L, H=H, R=R, topk=k, tail=64)
+        seq = np.arange(B, dtype=np.int32)
+        rng = np.random.default_rng(83)
+        nv = O.n_visible(layer.tok, layer.m, layer.pool.count)
+        sc = rng.standard_normal((B, layer.pool.rows_per_seq))
+        idx = O.topk(np.where(np.arange(sc.shape[1])[None] < nv[:, None], sc, -np.inf), nv, k)
+        ref = O.attn(seq, layer.tok, layer.pos0, S.bf16_bits(layer.q), "bf16", layer.win, layer.W, layer.pool, "csa",
+                     idx=idx, sinks=layer.sinks, sm_scale=layer.sm_scale, rope_dim=R, theta=layer.theta)
+        Q = K.QueryRows(dev(seq), dev(layer.tok), dev(layer.pos0), B)
+        out = K.dsv4_sparse_attn(Q, tensor_of(layer.q, "bf16"), upload_rows(layer.win), layer.W,
+                                 upload_rows(layer.pool), dev(idx), dev(layer.sinks), layer.sm_scale, R, layer.theta,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, "bf16", f"attention rope 32, {H} heads, {rows} rows")
+
+
 @pytest.mark.parametrize("B,Sx,H,W,m,sink,rows", [
     (1, 1100, 64, 128, 16, True, "bf16"),
     (2, 300, 64, 128, 128, True, "bf16"),
