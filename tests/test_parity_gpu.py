@@ -190,6 +190,8 @@ def test_index_topk_prefill(K, store, B, Sx, Hi, Di, m, k):
     ("mxfp4", 2, [30000, 4001], 512, 48, 128),
     ("bf16", 2, [30000, 4001], 512, 32, 96),
     ("bf16", 2, [30000, 4001], 512, 48, 32),
+    ("bf16", 2, [4 * 3000 + 1, 4 * 2100], 512, 64, 128),   # rows of 2049..4096 entries: 16 keys per thread
+    ("f32", 1, [4 * 20000], 512, 4, 32),   # fp32 scores of a long row: the level-0 histogram in its own pass
 ])
 def test_index_topk_decode(K, kind, B, L, k, Hi, Di):
     say("index_topk decode", kind, B, L, k, Hi, Di)
@@ -201,8 +203,8 @@ def test_index_topk_decode(K, kind, B, L, k, Hi, Di):
         qst, qsc = layer.q_idx_packed, layer.q_idx_scale
         qdev, qscd = dev(qst), dev(qsc)
     else:
-        qst, qsc = S.bf16_bits(layer.q_idx), None
-        qdev, qscd = tensor_of(layer.q_idx, "bf16"), None
+        qst, qsc = (S.bf16_bits(layer.q_idx) if kind == "bf16" else layer.q_idx), None
+        qdev, qscd = tensor_of(layer.q_idx, kind), None
     ref = O.index_scores(seq, tok, qst, kind, layer.w_idx, kp, layer.m, layer.score_scale, q_scale=qsc)
     nv = O.n_visible(tok, layer.m, kp.count)
     Q = K.QueryRows(dev(seq), dev(tok), None, B)
