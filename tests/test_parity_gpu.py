@@ -208,15 +208,17 @@ def test_index_topk_decode(K, kind, B, L, k, Hi, Di):
     ref = O.index_scores(seq, tok, qst, kind, layer.w_idx, kp, layer.m, layer.score_scale, q_scale=qsc)
     nv = O.n_visible(tok, layer.m, kp.count)
     Q = K.QueryRows(dev(seq), dev(tok), None, B)
-    idx = K.dsv4_index_topk(Q, qdev, dev(layer.w_idx), upload_rows(kp), layer.m, k, layer.score_scale,
-                            q_idx_scale=qscd)
+    idx, sc = K.dsv4_index_topk(Q, qdev, dev(layer.w_idx), upload_rows(kp), layer.m, k, layer.score_scale,
+                                q_idx_scale=qscd, want_scores=True)
     torch.cuda.synchronize()
-    idx = idx.cpu().numpy()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
     stats = check_topk(idx, ref, nv, k, "decode")
     say("topk stats", stats)
-    for r in range(B):   # picks in ascending entry order
+    for r in range(B):   # picks in ascending entry order, each with its score
         p = idx[r][idx[r] >= 0]
         assert np.all(np.diff(p) > 0), f"row {r}: picks not in ascending order"
+        assert np.allclose(sc[r, :len(p)], ref[r, p], rtol=1e-4, atol=1e-5), f"row {r}: pick scores"
+        assert np.all(np.isneginf(sc[r, len(p):])), f"row {r}: scores past the picks"
 
 
 @pytest.mark.parametrize("B,L,k,n_distinct", [
