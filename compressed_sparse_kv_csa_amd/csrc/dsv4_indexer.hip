@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void k_index_scores_mfma(IdxQ Q, IdxK K, float
 // query operand at 64 VGPRs, which leaves room for three waves per SIMD so the
 // ReLU / weighting VALU work of one wave overlaps the MFMAs of another.
 template <int NHB, int QPW>
-__global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float scale, int T,
+__global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float scale, int T, int skip_n,
                                                          float *__restrict__ scores, int64_t ld) {
   constexpr int KS = 4;          // head dim 128 = 4 k-steps of 32
   constexpr int DI = 128;
@@ -237,7 +237,10 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
   if (tid < QG) {
     const int r = r0 + tid;
     sh_b[tid] = r < T ? Q.seq[r] : -1;
-    sh_n[tid] = r < T ? n_visible(Q.tok[r], K.m, K.count[Q.seq[r]]) : 0;
+    // a row with at most skip_n visible entries takes all of them whatever
+    // their scores (skip_n = top-k when no pick scores are wanted): not scored
+    const int n = r < T ? n_visible(Q.tok[r], K.m, K.count[Q.seq[r]]) : 0;
+    sh_n[tid] = n <= skip_n ? 0 : n;
   }
   // this wave's two queries: operands and weights in registers
   bf16x8 qa[QPW][NHB][KS];
@@ -605,8 +608,12 @@ __global__ __launch_bounds__(256) void k_topk_chunk(const int32_t *__restrict__ 
     io[rank] = pos;
     if (so) so[rank] = keyf(key);
   };
-  if (kk == n) {   // everything visible is taken, in order
-    for (int j = threadIdx.x; j < n; j += 256) emit(j, j, fkey(scores[(int64_t)r * ld + j]));
+  if (kk == n) {   // everything visible is taken, in order (scores read only for score_out)
+    if (so) {
+      for (int j = threadIdx.x; j < n; j += 256) emit(j, j, fkey(scores[(int64_t)r * ld + j]));
+    } else {
+      for (int j = threadIdx.x; j < n; j += 256) io[j] = j;
+    }
   } else {
     uint32_t k[KPT];
     const float *src = scores + (int64_t)r * ld;
@@ -1240,11 +1247,15 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
   } else {
     constexpr int QPW = 1;   // queries per wave (4 per workgroup share each key tile)
     dim3 g8((T + 4 * QPW - 1) / (4 * QPW));
+    // rows whose picks are all their visible entries need no score unless the
+    // pick scores are returned (k_topk_chunk reads them only then; the long-row
+    // path reads every row's scores)
+    const int skip_n = (!p.radix && !score_out) ? topk : 0;
     switch (H / 16) {
-    case 1: hipLaunchKernelGGL((k_index_scores_q8<1, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    case 2: hipLaunchKernelGGL((k_index_scores_q8<2, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    case 3: hipLaunchKernelGGL((k_index_scores_q8<3, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
-    default: hipLaunchKernelGGL((k_index_scores_q8<4, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, scores, ld); break;
+    case 1: hipLaunchKernelGGL((k_index_scores_q8<1, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, skip_n, scores, ld); break;
+    case 2: hipLaunchKernelGGL((k_index_scores_q8<2, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, skip_n, scores, ld); break;
+    case 3: hipLaunchKernelGGL((k_index_scores_q8<3, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, skip_n, scores, ld); break;
+    default: hipLaunchKernelGGL((k_index_scores_q8<4, QPW>), g8, dim3(256), 0, st, Q, K, scale, T, skip_n, scores, ld); break;
     }
   }
   int rc = check_launch("k_index_scores");

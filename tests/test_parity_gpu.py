@@ -176,6 +176,37 @@ def test_index_topk_prefill(K, store, B, Sx, Hi, Di, m, k):
         assert np.allclose(sc[r, :len(p)], ref[r, p], rtol=1e-4, atol=1e-5)
 
 
+@pytest.mark.parametrize("B,Sx,k", [
+    (1, 2050, 512),   # every row takes all its visible entries
+    (3, 701, 64),     # 4-query groups straddle sequences; rows on both sides of n = k
+    (1, 6000, 512),   # the 2048-entry select next to rows that are not scored
+])
+def test_index_topk_prefill_without_scores(K, B, Sx, k):
+    """Without pick scores, rows with at most k visible entries are not scored:
+    their picks are all of them.  The picks equal those of the call that
+    returns scores, and the oracle's under the gap rule."""
+    say("index_topk prefill, no scores", B, Sx, k)
+    Hi, Di, m = 64, 128, 4
+    keys, q_idx, w, seq, tok = _prefill_indexer_case("bf16", B, Sx, Hi, Di, m, k, 11 + Sx)
+    kp = S.rowset_from_values(keys, "bf16")
+    scale = 1.0 / np.sqrt(Hi * Di)
+    ref = O.index_scores(seq, tok, S.bf16_bits(q_idx), "bf16", w, kp, m, scale)
+    nv = O.n_visible(tok, m, kp.count[seq])
+    Q = K.QueryRows(dev(seq), dev(tok), None, B)
+    kpd = upload_rows(kp)
+    qd = tensor_of(q_idx, "bf16")
+    idx_s, _ = K.dsv4_index_topk(Q, qd, dev(w), kpd, m, k, scale, want_scores=True)
+    idx_n = K.dsv4_index_topk(Q, qd, dev(w), kpd, m, k, scale)
+    torch.cuda.synchronize()
+    idx_s, idx_n = idx_s.cpu().numpy(), idx_n.cpu().numpy()
+    assert np.array_equal(idx_n, idx_s)
+    short = nv <= k
+    assert short.any()
+    for r in np.nonzero(short)[0]:
+        assert np.array_equal(idx_n[r, :nv[r]], np.arange(nv[r])) and (idx_n[r, nv[r]:] == -1).all()
+    check_topk(idx_n, ref, nv, k, "prefill, no scores")
+
+
 @pytest.mark.parametrize("kind,B,L,k,Hi,Di", [
     ("bf16", 3, [1000, 40001, 20050], 512, 64, 128),
     ("mxfp4", 2, [70000, 5003], 1024, 64, 128),
