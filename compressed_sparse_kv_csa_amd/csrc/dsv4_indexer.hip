@@ -242,12 +242,23 @@ __global__ __launch_bounds__(256) void k_index_scores_q8(IdxQ Q, IdxK K, float s
     const int n = r < T ? n_visible(Q.tok[r], K.m, K.count[Q.seq[r]]) : 0;
     sh_n[tid] = n <= skip_n ? 0 : n;
   }
-  // this wave's two queries: operands and weights in registers
+  // this wave's queries: operands and weights in registers (not loaded for a
+  // row that is not scored)
   bf16x8 qa[QPW][NHB][KS];
   float wt[QPW][NHB][4];
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     const int r = min(r0 + QPW * wv + qq, T - 1);
+    if (skip_n > 0 && n_visible(Q.tok[r], K.m, K.count[Q.seq[r]]) <= skip_n) {   // wave-uniform
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) qa[qq][hb][j] = bf16x8{};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wt[qq][hb][i] = 0.f;
+      }
+      continue;
+    }
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       const int h = 16 * hb + c;
