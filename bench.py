@@ -71,11 +71,13 @@ def csa_prefill_counts(S, m, W, k, H, D, Hi, Di):
     n = np.minimum(S // m, (t + 1) // m)
     win = np.minimum(W, t + 1)
     sel = np.minimum(k, n)
+    # a row with at most k visible entries picks all of them: it is not scored
+    scored = n[n > k]
     return {
         "attn_pairs": int((win + sel).sum()),
         "attn_flop": float((win + sel).sum()) * H * D * 4,
-        "index_pairs": int(n.sum()),
-        "index_flop": float(n.sum()) * Hi * Di * 2,
+        "index_pairs": int(scored.sum()),
+        "index_flop": float(scored.sum()) * Hi * Di * 2,
     }
 
 
