@@ -256,8 +256,8 @@ def test_index_topk_decode(K, kind, B, L, k, Hi, Di):
     (2, [4 * 30000, 4 * 3000 + 3], 512, 3),   # radix-threshold passes over several chunks
     (1, [4 * 20000], 1024, 1),                # every score equal
     (3, [4 * 5000, 4 * 700, 9], 256, 2),      # one workgroup per row
-    (3, [4 * 2000, 4 * 700 + 3, 9], 512, 3),  # one wave per row (pools of at most 2048)
-    (2, [4 * 2048, 4 * 1500], 1024, 1),       # one wave per row, every score equal
+    (3, [4 * 2000, 4 * 700 + 3, 9], 512, 3),  # 128-thread workgroups (pools of at most 2048)
+    (2, [4 * 2048, 4 * 1500], 1024, 1),       # 128-thread workgroups, every score equal
 ])
 def test_index_topk_ties(K, B, L, k, n_distinct):
     """Pool rows repeat a few distinct keys in runs of 7, so each row's scores
