@@ -823,7 +823,7 @@ __global__ __launch_bounds__(256) void k_rt_hist0(const int32_t *__restrict__ se
 // from the score row: three histogram levels to the exact kk-th largest key
 // t*, then every key above t* and the lowest-position keys equal to t*, in
 // ascending position order.
-__device__ void rt_row_select(const float *scores, int64_t ld, int r, int n, int kk, int32_t *io, float *so,
+__device__ __forceinline__ void rt_row_select(const float *scores, int64_t ld, int r, int n, int kk, int32_t *io, float *so,
                               uint32_t *lh, uint32_t *sh) {
   RtThr t{0u, 0u, (uint32_t)kk};
 #pragma unroll
@@ -912,7 +912,7 @@ __device__ __forceinline__ void rt_word_prefix(const uint32_t *bm, uint32_t *wpr
 // prefix popcounts: the picks', and (only when t* has more equal keys than
 // are wanted) the equal keys' to rank them.
 template <int P>
-__device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, int nch, int cc, int M, int kk, uint32_t b0,
+__device__ __forceinline__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, int nch, int cc, int M, int kk, uint32_t b0,
                                 uint32_t above0, RtFinalLds &F, int32_t *io, float *so) {
   const int tid = (int)threadIdx.x;
   uint32_t k[P];
@@ -990,7 +990,7 @@ __device__ void rt_cands_select(const uint32_t *rk, const int32_t *rp, int nch, 
 // The picks of long row r from its candidates (or from the whole row when a
 // chunk's candidates overflowed), and the -1 tail.  Block-wide.
 
-__device__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t ld, int topk, int nch, int cc,
+__device__ __forceinline__ void rt_final_row(int r, int n, int kk, const float *scores, int64_t ld, int topk, int nch, int cc,
                              const uint32_t *ckey, const int32_t *cpos, const uint32_t *cr, int32_t *idx_out,
                              float *score_out, RtFinalLds &F) {
   int32_t *io = idx_out + (int64_t)r * topk;
