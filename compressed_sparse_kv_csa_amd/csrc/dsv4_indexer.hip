@@ -1272,7 +1272,11 @@ int launch_index_topk(const dsv4_queries *q, const void *qv, const uint8_t *qsca
     // runs as one wave of workgroups with no partly filled second round
     const int64_t unit = 64LL * eb;   // entries per super-block
     const int64_t blocks = (kp->seq_stride + unit - 1) / unit;
-    int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, resident_wgs((const void *)sk, 256) / T),
+    // two thirds of what is resident at once: swept at 1/2, 2/3 and all of it,
+    // the CSA decode scan took 60.8, 51.7 and 54.3 us, the MXFP4 scan of the 1M
+    // mixed decode 33.0, 32.1 and 33.4 us (fewer concurrent streams per CU; both
+    // rows' super-blocks then also divide evenly over their workgroups)
+    int64_t per_row = std::min<int64_t>(std::max<int64_t>(1, 2 * resident_wgs((const void *)sk, 256) / 3 / T),
                                         std::max<int64_t>(1, blocks));
     // at most kScoreStage / unit - 1 super-blocks per workgroup (its LDS staging)
     const int64_t cap = kScoreStage / unit - 1;
